@@ -1,0 +1,207 @@
+/*
+ * lce.h -- C ABI of liblce.so: fused linear cross-entropy on AMD MI355X (gfx950).
+ *
+ * Computes, for hidden states H [n_tok][d_model] and an output projection
+ * W [vocab][d_model] (row-major, as the lossk function table of
+ * "Loss functions and resident-context kernels" specifies), the cross-entropy
+ * of softmax(H W^T) against integer targets WITHOUT materializing the
+ * [n_tok][vocab] logit tensor, its analytic gradients, a z-loss term
+ * (the square of each token's log-sum-exp), and logit distillation against a
+ * full teacher distribution ("Fuse distillation + z-loss in the triton
+ * monolithic path", Fast-LLM pull request 566, section "What it does").
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * Status: every function that can refuse returns an int32 status from the
+ *   lossk range 580-599 ("Status codes" section of the lossk page); 589 and
+ *   590 are this library's extensions inside that range.  Nothing throws or
+ *   aborts.  On any refusal no output is modified.
+ * Ownership: the caller owns every buffer, including the workspace.  The
+ *   library allocates no device memory, keeps no pointer after returning and
+ *   holds no global state, so calls are reentrant given distinct workspaces.
+ *   Calls that share one workspace must be ordered (same stream).
+ * Streams: device work is enqueued on the caller's stream (a hipStream_t
+ *   passed as void*; NULL = the null stream).  lce_forward, lce_backward and
+ *   lce_distill_fwd_bwd synchronize that stream once before returning,
+ *   because their status (and the forward's scalars) come from the device.
+ * Validation order: dimensions -> chunk -> scalars -> dtypes -> buffer
+ *   lengths and workspace size -> objective id -> device-side target guard
+ *   -> compute.  The target guard runs on the device; when it fails, every
+ *   compute kernel exits before writing and 586 is returned.
+ * Precision: bf16 inputs are multiplied on the matrix cores with fp32
+ *   accumulation; every softmax statistic is fp32 and every token sum fp64.
+ *   fp64 inputs run end to end in fp64.
+ */
+#ifndef LCE_H
+#define LCE_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* ---- status codes (lossk "Status codes" section) ---------------------- */
+#define LCE_OK 580                           /* checks passed / work ran            */
+#define LCE_EMPTY_DIMENSION 581              /* a required dimension < 1            */
+#define LCE_LENGTH_MISMATCH 582              /* a buffer shorter than its shape     */
+#define LCE_DIMENSION_TOO_LARGE 583          /* a dimension above its ceiling       */
+#define LCE_WORK_BUDGET_EXCEEDED 584         /* n_tok*d_model*vocab > 2^46          */
+#define LCE_NON_FINITE_SCALAR 585            /* NaN/Inf scalar, or temperature <= 0 */
+#define LCE_TARGET_OUT_OF_RANGE 586          /* a target id < 0 or >= vocab         */
+#define LCE_CHUNK_EXCEEDS_LOGIT_BUDGET 587   /* chunk*vocab > 2^27                  */
+#define LCE_UNKNOWN_OBJECTIVE 588            /* distillation objective id not 0..2  */
+#define LCE_DEVICE_ERROR 589                 /* extension: a HIP call failed        */
+#define LCE_DTYPE_MISMATCH 590               /* extension: unsupported dtype combo  */
+
+/* Budgets of the lossk table: total work 2^46 cells, peak logits 2^27 cells.
+ * Per-dimension ceilings (the page states only that each dimension has one):
+ * n_tok <= 2^24, d_model <= 2^16, vocab <= 2^24; equality passes. */
+#define LCE_MAX_WORK_CELLS (((int64_t)1) << 46)
+#define LCE_MAX_LOGIT_CELLS (((int64_t)1) << 27)
+#define LCE_MAX_N_TOK (((int64_t)1) << 24)
+#define LCE_MAX_D_MODEL (((int64_t)1) << 16)
+#define LCE_MAX_VOCAB (((int64_t)1) << 24)
+
+/* ---- dtypes ------------------------------------------------------------ */
+#define LCE_BF16 1
+#define LCE_F32 2
+#define LCE_F64 3
+#define LCE_I64 4
+#define LCE_U8 6
+
+/* A flat buffer: data points to numel contiguous elements of dtype.
+ * Device buffers hold device pointers (hipMalloc / torch CUDA tensors). */
+typedef struct lce_tensor {
+  void *data;
+  int64_t numel;
+  int32_t dtype;
+} lce_tensor;
+
+/* Result of lce_peak_cells (the lossk reporter of chunked against
+ * materialized logit cells). */
+typedef struct lce_peak {
+  double chunked_cells;       /* min(chunk, n_tok) * vocab                 */
+  double materialized_cells;  /* n_tok * vocab                             */
+  double ratio;               /* materialized / chunked                    */
+  int64_t n_chunks;           /* ceil(n_tok / chunk)                       */
+  int32_t status;             /* lce_chunk_check(chunk, vocab), or 581     */
+} lce_peak;
+
+/* Scalars of a forward or distillation call (host memory). */
+typedef struct lce_loss {
+  double loss_sum;   /* sum over counted tokens of the per-token loss        */
+  double loss_mean;  /* loss_sum / n_counted (0 when nothing is counted)     */
+  double z_sum;      /* sum over counted tokens of lse^2 (unscaled z-loss)   */
+  double z_mean;     /* z_sum / n_counted                                    */
+  int64_t n_counted; /* number of counted (unmasked) tokens                  */
+} lce_loss;
+
+/* ---- host-only contract (no device needed) ----------------------------- */
+
+/* Name of a status code; any code not listed above gives "unknown_status"
+ * (lossk table, loss_status_name).  Returns a static string. */
+const char *lce_status_name(int32_t code);
+
+/* Shape check (lossk table, loss_dims_check): 581 if any dimension < 1,
+ * 583 if any is above its ceiling, 584 if n_tok*d_model*vocab > 2^46
+ * (decided by dividing the budget down, never by an overflowing product),
+ * else 580. */
+int32_t lce_dims_check(int64_t n_tok, int64_t d_model, int64_t vocab);
+
+/* Peak-memory check (lossk table, loss_chunk_check): 581 if chunk or vocab
+ * < 1, 587 if chunk*vocab > 2^27 (refused, never clamped), else 580. */
+int32_t lce_chunk_check(int64_t chunk, int64_t vocab);
+
+/* chunk*vocab as a double; -1.0 when chunk or vocab < 1
+ * (lossk table, loss_logit_cells). */
+double lce_logit_cells(int64_t chunk, int64_t vocab);
+
+/* 1 when n*d*v <= ceiling, by successive division (lossk table,
+ * loss_work_fits); 0 otherwise or when any argument is < 1. */
+int32_t lce_work_fits(int64_t n, int64_t d, int64_t v, int64_t ceiling);
+
+/* Chunked against materialized logit cells (lossk table,
+ * ce_peak_logit_cells, and the page's opening example).  Fills *out and
+ * returns out->status: 581 (all numbers -1, n_chunks 0) when any argument
+ * is < 1, else lce_chunk_check(chunk, vocab) with the numbers filled in.
+ * A chunk larger than the batch holds only n_tok rows. */
+int32_t lce_peak_cells(int64_t n_tok, int64_t vocab, int64_t chunk, lce_peak *out);
+
+/* Bytes of device workspace lce_forward and lce_backward need for this
+ * shape and compute dtype (LCE_BF16 or LCE_F64).  Negative = -status when
+ * the shape, chunk or dtype is refused.  The logit-derived part of the
+ * workspace never exceeds chunk*vocab cells. */
+int64_t lce_workspace_bytes(int64_t n_tok, int64_t d_model, int64_t vocab, int64_t chunk,
+                            int32_t dtype);
+
+/* Bytes of device workspace lce_distill_fwd_bwd needs (-status if refused). */
+int64_t lce_distill_workspace_bytes(int64_t n_tok, int64_t vocab);
+
+/* ---- device entry points ------------------------------------------------ */
+
+/* Fused projection + chunked cross-entropy, forward (lossk table,
+ * fused_linear_ce_flat; "lossk: the loss is where the memory goes"), with
+ * z-loss and a loss mask (Fast-LLM 566, "What it does").
+ *   hidden    [n_tok*d_model] LCE_BF16 or LCE_F64, row-major [n_tok][d_model]
+ *   weight    [vocab*d_model] same dtype, row-major [vocab][d_model]
+ *   targets   [n_tok] LCE_I64, each must satisfy 0 <= y < vocab (586)
+ *   loss_mask [n_tok] LCE_U8 (1 = counted) or data == NULL (all counted)
+ *   chunk     tokens whose logits may exist at once: the call holds at most
+ *             chunk*vocab logit-derived cells (587 above 2^27)
+ *   z_coef    z-loss coefficient; only validated here (z_sum is unscaled)
+ *   lse_out   [n_tok] per-token log-sum-exp, LCE_F32 for bf16 inputs,
+ *             LCE_F64 for fp64 inputs; lce_backward takes it back
+ *   workspace LCE_U8, numel >= lce_workspace_bytes(...)
+ *   out       host pointer; receives the scalars
+ * Per-token losses are summed in token order with a fixed reduction tree,
+ * so the result is bit-identical for every chunk size (lossk page,
+ * "Chunk invariance is checked to the last bit"). */
+int32_t lce_forward(const lce_tensor *hidden, const lce_tensor *weight,
+                    const lce_tensor *targets, const lce_tensor *loss_mask, int64_t n_tok,
+                    int64_t d_model, int64_t vocab, int64_t chunk, double z_coef,
+                    lce_tensor *lse_out, lce_tensor *workspace, lce_loss *out, void *stream);
+
+/* Analytic backward of loss_mean + z_coef*z_mean scaled by grad_out
+ * (lossk table, fused_linear_ce_bwd_flat; Fast-LLM 566, "What it does"):
+ *   d[t][v] = (g + 2 g_z lse_t) softmax_t[v] - g [v == y_t],
+ *   g = grad_out/C, g_z = z_coef*grad_out/C, C = counted tokens, masked -> 0;
+ *   d_hidden = d W,  d_weight (+)= d^T H.
+ *   lse        [n_tok] from lce_forward on the same inputs (F32 / F64)
+ *   d_hidden   [n_tok*d_model] in hidden's dtype (overwritten)
+ *   d_weight   [vocab*d_model] LCE_F32 for bf16 inputs, LCE_F64 for fp64;
+ *              overwritten, or added to when accumulate_d_weight != 0
+ * Logits are recomputed from H and W; the logit-gradient buffer holds at
+ * most chunk*vocab cells at once. */
+int32_t lce_backward(const lce_tensor *hidden, const lce_tensor *weight,
+                     const lce_tensor *targets, const lce_tensor *loss_mask,
+                     const lce_tensor *lse, int64_t n_tok, int64_t d_model, int64_t vocab,
+                     int64_t chunk, double z_coef, double grad_out, lce_tensor *d_hidden,
+                     lce_tensor *d_weight, int32_t accumulate_d_weight,
+                     lce_tensor *workspace, void *stream);
+
+/* Distillation against a teacher distribution, fused forward + backward,
+ * with z-loss over the same student softmax (Fast-LLM 566, "What it does"
+ * and "Changes": returns loss, z-loss and the logit gradient).
+ *   student, teacher [n_tok*vocab] logits, LCE_BF16, LCE_F32 or LCE_F64
+ *                    (same dtype), row-major [n_tok][vocab]
+ *   loss_mask        [n_tok] LCE_U8 or data == NULL
+ *   objective        0 soft-target cross-entropy -sum q log p,
+ *                    1 forward KL(q||p), 2 reverse KL(p||q)   (else 588)
+ *   temperature      > 0 and finite (else 585); x = s/T, y = u/T
+ *   grad_logits      [n_tok*vocab] in the student's dtype:
+ *                    (grad_out/C) (dL/dx + 2 z_coef lse(x) p) / T, masked rows 0
+ *   workspace        LCE_U8, numel >= lce_distill_workspace_bytes(...)
+ *   out              host; loss_sum/loss_mean = distillation loss,
+ *                    z_sum/z_mean = unscaled z-loss, n_counted = C */
+int32_t lce_distill_fwd_bwd(const lce_tensor *student, const lce_tensor *teacher,
+                            const lce_tensor *loss_mask, int64_t n_tok, int64_t vocab,
+                            int32_t objective, double temperature, double z_coef,
+                            double grad_out, lce_tensor *grad_logits, lce_tensor *workspace,
+                            lce_loss *out, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LCE_H */

@@ -1,0 +1,7 @@
+"""Fused linear cross-entropy for AMD MI355X (gfx950): HIP kernels behind the
+C ABI of include/lce.h, with a thin ctypes binding (``lm_head_linear_amd.lce``)."""
+from . import lce  # noqa: F401
+from .lce import (LceError, backward, distill, forward, lce_backward, lce_chunk_check,  # noqa: F401
+                  lce_dims_check, lce_distill_fwd_bwd, lce_distill_workspace_bytes, lce_forward,
+                  lce_logit_cells, lce_peak_cells, lce_status_name, lce_work_fits,
+                  lce_workspace_bytes)

@@ -1,0 +1,670 @@
+// lce_ce.hip -- fused linear cross-entropy forward and backward on gfx950.
+//
+// Forward (lossk table, fused_linear_ce_flat, and "lossk: the loss is where
+// the memory goes", on "Loss functions and resident-context kernels"):
+//   one MFMA GEMM launch per token pass computes logit tiles Z^T = W H^T in
+//   registers and reduces each (token, 128-row vocabulary block) at once to an
+//   online (max, sum-of-exp) pair plus the target logit; no logit is stored.
+//   A merge kernel folds the pairs in a fixed order into lse_t, and one
+//   fixed-tree reduction sums the counted tokens' losses and lse_t^2 in fp64.
+// Backward (lossk table, fused_linear_ce_bwd_flat; the one-hot superposition
+// and the z-loss coefficient of "Fuse distillation + z-loss in the triton
+// monolithic path", section "What it does"):
+//   the vocabulary is cut into slabs whose logit gradient for every token fits
+//   the chunk*vocab cell budget.  Per slab: a GEMM recomputes the logits and
+//   turns them into d = (g + 2 g_z lse) p - g [v == y] in its epilogue
+//   (stored bf16 / fp64); a GEMM forms that slab's d_weight rows = d^T H in one
+//   pass over all tokens (written once); a split-K GEMM adds d W_slab into
+//   fp32 / fp64 d_hidden accumulators.  A last kernel folds the splits.
+#include <hip/hip_runtime.h>
+
+#include <cfloat>
+#include <climits>
+#include <cmath>
+
+#include "lce_gemm.hpp"
+#include "lce_internal.h"
+
+namespace lce {
+
+// ---------------------------------------------------------- small kernels --
+
+__global__ void ctl_init_kernel(Control *ctl) {
+  if (threadIdx.x == 0) {
+    ctl->bad = 0;
+    ctl->pad0 = 0;
+    ctl->first_bad = LLONG_MAX;
+    ctl->count = 0;
+    ctl->pad1 = 0;
+    ctl->loss_sum = 0.0;
+    ctl->z_sum = 0.0;
+  }
+}
+
+// Target-range guard (lossk table, loss_targets_in_range) and the count of
+// counted tokens.  Integer work only, so the atomics are order-free.
+__global__ void guard_kernel(const int64_t *y, const uint8_t *mask, int64_t n, int64_t V,
+                             Control *ctl) {
+  __shared__ unsigned long long s_first[4];
+  __shared__ unsigned long long s_count[4];
+  unsigned long long first = ULLONG_MAX, count = 0;
+  for (int64_t t = int64_t(blockIdx.x) * blockDim.x + threadIdx.x; t < n;
+       t += int64_t(gridDim.x) * blockDim.x) {
+    const int64_t v = y[t];
+    if (v < 0 || v >= V) first = first < (unsigned long long)t ? first : (unsigned long long)t;
+    count += mask ? (mask[t] != 0) : 1;
+  }
+  for (int o = 32; o > 0; o >>= 1) {
+    unsigned long long f2 = __shfl_xor(first, o);
+    first = f2 < first ? f2 : first;
+    count += __shfl_xor(count, o);
+  }
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  if (lane == 0) { s_first[wave] = first; s_count[wave] = count; }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    for (int w = 1; w < int(blockDim.x >> 6); ++w) {
+      first = s_first[w] < first ? s_first[w] : first;
+      count += s_count[w];
+    }
+    if (count) atomicAdd(reinterpret_cast<unsigned long long *>(&ctl->count), count);
+    if (first != ULLONG_MAX) {
+      atomicMin(reinterpret_cast<unsigned long long *>(&ctl->first_bad), first);
+      atomicExch(&ctl->bad, 1);
+    }
+  }
+}
+
+template <class T> __device__ inline T fexp(T x);
+template <> __device__ inline float fexp<float>(float x) {
+  return __builtin_amdgcn_exp2f(x * 1.4426950408889634f);
+}
+template <> __device__ inline double fexp<double>(double x) { return exp(x); }
+template <class T> __device__ inline T flog(T x);
+template <> __device__ inline float flog<float>(float x) { return logf(x); }
+template <> __device__ inline double flog<double>(double x) { return log(x); }
+
+template <class T> __device__ inline T neg_inf();
+template <> __device__ inline float neg_inf<float>() { return -INFINITY; }
+template <> __device__ inline double neg_inf<double>() { return -INFINITY; }
+
+// Reduce over the lanes that hold the same output column of an MFMA block.
+template <class TR, class T> __device__ inline T col_max(T x);
+template <class TR, class T> __device__ inline T col_sum(T x);
+template <> __device__ inline float col_max<TraitsBF16, float>(float x) {
+  return fmaxf(x, __shfl_xor(x, 32));
+}
+template <> __device__ inline float col_sum<TraitsBF16, float>(float x) {
+  return x + __shfl_xor(x, 32);
+}
+template <> __device__ inline double col_max<TraitsF64, double>(double x) {
+  x = fmax(x, __shfl_xor(x, 16));
+  return fmax(x, __shfl_xor(x, 32));
+}
+template <> __device__ inline double col_sum<TraitsF64, double>(double x) {
+  x = x + __shfl_xor(x, 16);
+  return x + __shfl_xor(x, 32);
+}
+
+template <class TR> __device__ inline typename TR::E to_elem(typename TR::Acc x);
+template <> __device__ inline uint16_t to_elem<TraitsBF16>(float x) { return f32_to_bf16_rne(x); }
+template <> __device__ inline double to_elem<TraitsF64>(double x) { return x; }
+
+// ------------------------------------------------------ forward epilogue --
+
+// exp(x - m) with the shift folded into one FMA for fp32 (exp2 of a base-2
+// exponent); plain exp for fp64.
+template <class T> __device__ inline T shift_exp(T x, T m);
+template <> __device__ inline float shift_exp<float>(float x, float m) {
+  const float L2E = 1.4426950408889634f;
+  return __builtin_amdgcn_exp2f(fmaf(x, L2E, -m * L2E));
+}
+template <> __device__ inline double shift_exp<double>(double x, double m) { return exp(x - m); }
+
+// (max, sum exp(v - max)) over the rows of one output column held by a wave;
+// with CHECK only rows below `lim` (relative to the wave's first row) count.
+template <class TR, bool CHECK>
+__device__ __forceinline__ void column_lse(const typename TR::AccBlock (&acc)[TR::FM][TR::FN],
+                                           const int fn, const int lane, const int lim,
+                                           typename TR::Acc &mx_out, typename TR::Acc &s_out) {
+  typedef typename TR::Acc Acc;
+  Acc mx = neg_inf<Acc>();
+#pragma unroll
+  for (int fm = 0; fm < TR::FM; ++fm)
+#pragma unroll
+    for (int r = 0; r < TR::R; ++r)
+      if (!CHECK || fm * TR::MF + TR::row_of(r, lane) < lim)
+        mx = acc[fm][fn][r] > mx ? acc[fm][fn][r] : mx;
+  mx = col_max<TR, Acc>(mx);
+  Acc s = 0;
+#pragma unroll
+  for (int fm = 0; fm < TR::FM; ++fm)
+#pragma unroll
+    for (int r = 0; r < TR::R; ++r)
+      if (!CHECK || fm * TR::MF + TR::row_of(r, lane) < lim) s += shift_exp<Acc>(acc[fm][fn][r], mx);
+  s_out = col_sum<TR, Acc>(s);
+  mx_out = mx;
+}
+
+// The accumulator of this lane whose row (relative to the wave) is `yl`, or 0
+// when the lane holds no such row.  A sum of selects keeps every accumulator
+// index static, so the accumulators stay in registers.
+template <class TR>
+__device__ __forceinline__ typename TR::Acc pick_row(
+    const typename TR::AccBlock (&acc)[TR::FM][TR::FN], const int fn, const int lane, const int yl) {
+  typename TR::Acc z = 0;
+#pragma unroll
+  for (int fm = 0; fm < TR::FM; ++fm)
+#pragma unroll
+    for (int r = 0; r < TR::R; ++r)
+      z += (fm * TR::MF + TR::row_of(r, lane) == yl) ? acc[fm][fn][r] : typename TR::Acc(0);
+  return z;
+}
+
+// Z^T tile: rows = vocabulary ids, columns = tokens of the pass.  For every
+// token column and every wave (WTM consecutive vocabulary rows) write
+// (max, sum exp(z - max)) and, where the target falls in those rows, z[y].
+template <class TR>
+struct FwdLseEpi {
+  typedef typename TR::Acc Acc;
+  const int64_t *targets;  // first token of the pass
+  int64_t n_cols;          // tokens in the pass
+  int64_t V;
+  int64_t n_vparts;
+  Acc *partials;           // [n_cols][n_vparts][2]
+  Acc *zy;                 // first token of the pass
+
+  __device__ __forceinline__ void emit(const typename TR::AccBlock (&acc)[TR::FM][TR::FN],
+                                       int fn, int64_t t, int64_t vrow0, int64_t vpart, int lane,
+                                       Acc mx, Acc s) const {
+    if (t >= n_cols) return;
+    if (lane < TR::MF) {
+      Acc *p = partials + (t * n_vparts + vpart) * 2;
+      p[0] = mx;
+      p[1] = s;
+    }
+    const int64_t yr = targets[t] - vrow0;
+    const int yl = (yr >= 0 && yr < TR::WTM) ? int(yr) : -1;
+    const Acc z = pick_row<TR>(acc, fn, lane, yl);
+    // exactly one lane of the column holds row yl
+    bool mine = false;
+#pragma unroll
+    for (int fm = 0; fm < TR::FM; ++fm)
+#pragma unroll
+      for (int r = 0; r < TR::R; ++r) mine |= (fm * TR::MF + TR::row_of(r, lane) == yl);
+    if (mine) zy[t] = z;
+  }
+
+  __device__ __forceinline__ void operator()(typename TR::AccBlock (&acc)[TR::FM][TR::FN], int64_t m0, int64_t n0,
+                             int wm, int wn, int lane, int) const {
+    const int64_t vrow0 = m0 + int64_t(wm) * TR::WTM;
+    if (vrow0 >= V) return;  // wave-uniform
+    const int64_t vpart = vrow0 / TR::WTM;
+    const int lim = V - vrow0 < TR::WTM ? int(V - vrow0) : TR::WTM;
+    const int64_t tcol = n0 + int64_t(wn) * TR::WTN + TR::col_of(lane);
+    if (lim == TR::WTM) {
+#pragma unroll
+      for (int fn = 0; fn < TR::FN; ++fn) {
+        Acc mx, s;
+        column_lse<TR, false>(acc, fn, lane, lim, mx, s);
+        emit(acc, fn, tcol + fn * TR::MF, vrow0, vpart, lane, mx, s);
+      }
+    } else {
+#pragma unroll
+      for (int fn = 0; fn < TR::FN; ++fn) {
+        Acc mx, s;
+        column_lse<TR, true>(acc, fn, lane, lim, mx, s);
+        emit(acc, fn, tcol + fn * TR::MF, vrow0, vpart, lane, mx, s);
+      }
+    }
+  }
+};
+
+// One wave per token: fold the token's (max, sum) pairs in a fixed order.
+template <class Acc>
+__global__ void fwd_merge_kernel(const Acc *partials, const Acc *zy, int64_t n_vparts,
+                                 int64_t ntok, Acc *lse_out, double *loss_tok,
+                                 const int32_t *bad) {
+  if (*bad) return;
+  const int lane = threadIdx.x & 63;
+  const int64_t t = int64_t(blockIdx.x) * (blockDim.x >> 6) + (threadIdx.x >> 6);
+  if (t >= ntok) return;
+  const Acc *p = partials + t * n_vparts * 2;
+  Acc m = neg_inf<Acc>();
+  for (int64_t i = lane; i < n_vparts; i += 64) m = p[2 * i] > m ? p[2 * i] : m;
+  for (int o = 32; o > 0; o >>= 1) {
+    Acc o2 = __shfl_xor(m, o);
+    m = o2 > m ? o2 : m;
+  }
+  Acc s = 0;
+  for (int64_t i = lane; i < n_vparts; i += 64) s += p[2 * i + 1] * fexp<Acc>(p[2 * i] - m);
+  // Fixed tree; lane 0 holds the result.
+  for (int o = 32; o > 0; o >>= 1) s += __shfl_down(s, o);
+  if (lane == 0) {
+    const Acc lse = m + flog<Acc>(s);
+    lse_out[t] = lse;
+    loss_tok[t] = double(lse) - double(zy[t]);
+  }
+}
+
+// Sums over counted tokens in fp64 with a fixed thread-to-token map and a
+// fixed reduction tree, so the result is independent of the chunk size.
+template <class Acc>
+__global__ void fwd_final_kernel(const double *loss_tok, const Acc *lse, const uint8_t *mask,
+                                 int64_t n, Control *ctl) {
+  if (ctl->bad) return;
+  __shared__ double s_l[1024], s_z[1024];
+  double ls = 0.0, zs = 0.0;
+  for (int64_t t = threadIdx.x; t < n; t += blockDim.x) {
+    if (mask && !mask[t]) continue;
+    const double l = double(lse[t]);
+    ls += loss_tok[t];
+    zs += l * l;
+  }
+  s_l[threadIdx.x] = ls;
+  s_z[threadIdx.x] = zs;
+  __syncthreads();
+  for (int w = blockDim.x / 2; w > 0; w >>= 1) {
+    if (int(threadIdx.x) < w) {
+      s_l[threadIdx.x] += s_l[threadIdx.x + w];
+      s_z[threadIdx.x] += s_z[threadIdx.x + w];
+    }
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) {
+    ctl->loss_sum = s_l[0];
+    ctl->z_sum = s_z[0];
+  }
+}
+
+// ----------------------------------------------------- backward epilogues --
+
+// Recomputed Z^T tile of a vocabulary slab -> logit gradient, stored
+// [slab row][token] in the input dtype.
+template <class TR>
+struct DlogitEpi {
+  typedef typename TR::Acc Acc;
+  const int64_t *targets;
+  const uint8_t *mask;
+  const Acc *lse;
+  int64_t n;
+  int64_t vs0;     // first vocabulary row of the slab
+  int64_t rows;    // rows in the slab
+  const Control *ctl;
+  double grad_out, z_coef;
+  typename TR::E *dbuf;
+  int64_t d_ld;
+
+  template <bool CHECK>
+  __device__ __forceinline__ void body(const typename TR::AccBlock (&acc)[TR::FM][TR::FN],
+                                       int64_t vw0, int64_t tw0, int lane, Acc g, Acc gz) const {
+#pragma unroll
+    for (int fn = 0; fn < TR::FN; ++fn) {
+      const int64_t t = tw0 + fn * TR::MF + TR::col_of(lane);
+      if (CHECK && t >= n) continue;
+      const Acc l = lse[t];
+      const bool counted = !mask || mask[t];
+      const Acc coef = counted ? g + Acc(2) * gz * l : Acc(0);
+      const Acc gy = counted ? g : Acc(0);
+      const int64_t yr = targets[t] - (vs0 + vw0);
+      const int yl = (yr >= 0 && yr < TR::WTM) ? int(yr) : -1;
+      typename TR::E *col = dbuf + t;
+#pragma unroll
+      for (int fm = 0; fm < TR::FM; ++fm)
+#pragma unroll
+        for (int r = 0; r < TR::R; ++r) {
+          const int vr = fm * TR::MF + TR::row_of(r, lane);
+          if (CHECK && vw0 + vr >= rows) continue;
+          Acc d = coef * shift_exp<Acc>(acc[fm][fn][r], l);
+          d -= (vr == yl) ? gy : Acc(0);
+          col[(vw0 + vr) * d_ld] = to_elem<TR>(d);
+        }
+    }
+  }
+
+  __device__ __forceinline__ void operator()(typename TR::AccBlock (&acc)[TR::FM][TR::FN], int64_t m0, int64_t n0,
+                             int wm, int wn, int lane, int) const {
+    const int64_t C = ctl->count;
+    const Acc g = C ? Acc(grad_out / double(C)) : Acc(0);
+    const Acc gz = C ? Acc(z_coef * grad_out / double(C)) : Acc(0);
+    const int64_t vw0 = m0 + int64_t(wm) * TR::WTM;
+    const int64_t tw0 = n0 + int64_t(wn) * TR::WTN;
+    if (vw0 >= rows || tw0 >= n) return;
+    if (vw0 + TR::WTM <= rows && tw0 + TR::WTN <= n) body<false>(acc, vw0, tw0, lane, g, gz);
+    else body<true>(acc, vw0, tw0, lane, g, gz);
+  }
+};
+
+// out[split][row_off + row][col] = C (ACCUM false) or += C (ACCUM true).
+template <class TR, bool ACCUM>
+struct StoreEpi {
+  typedef typename TR::Acc Acc;
+  Acc *out;
+  int64_t ldo;
+  int64_t row_off;
+  int64_t rows, cols;
+  int64_t split_stride;
+
+  template <bool CHECK>
+  __device__ __forceinline__ void body(const typename TR::AccBlock (&acc)[TR::FM][TR::FN], Acc *o,
+                                       int64_t rw0, int64_t cw0, int lane) const {
+#pragma unroll
+    for (int fn = 0; fn < TR::FN; ++fn) {
+      const int64_t c = cw0 + fn * TR::MF + TR::col_of(lane);
+      if (CHECK && c >= cols) continue;
+      Acc *colp = o + c;
+#pragma unroll
+      for (int fm = 0; fm < TR::FM; ++fm) {
+#pragma unroll
+        for (int r = 0; r < TR::R; ++r) {
+          const int64_t row = rw0 + fm * TR::MF + TR::row_of(r, lane);
+          if (CHECK && row >= rows) continue;
+          Acc *q = colp + (row_off + row) * ldo;
+          if (ACCUM) *q += acc[fm][fn][r];
+          else *q = acc[fm][fn][r];
+        }
+        // keep the read-modify-write of one block in flight at a time
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+  }
+
+  __device__ __forceinline__ void operator()(typename TR::AccBlock (&acc)[TR::FM][TR::FN], int64_t m0, int64_t n0,
+                             int wm, int wn, int lane, int split) const {
+    Acc *o = out + int64_t(split) * split_stride;
+    const int64_t rw0 = m0 + int64_t(wm) * TR::WTM;
+    const int64_t cw0 = n0 + int64_t(wn) * TR::WTN;
+    if (rw0 >= rows || cw0 >= cols) return;
+    if (rw0 + TR::WTM <= rows && cw0 + TR::WTN <= cols) body<false>(acc, o, rw0, cw0, lane);
+    else body<true>(acc, o, rw0, cw0, lane);
+  }
+};
+
+// d_hidden = sum over splits (ascending) of the split accumulators.
+template <class TR>
+__global__ void dh_final_kernel(const typename TR::Acc *P, int64_t splits, int64_t count,
+                                typename TR::E *out, const int32_t *bad) {
+  if (*bad) return;
+  for (int64_t i = int64_t(blockIdx.x) * blockDim.x + threadIdx.x; i < count;
+       i += int64_t(gridDim.x) * blockDim.x) {
+    typename TR::Acc s = 0;
+    for (int64_t j = 0; j < splits; ++j) s += P[j * count + i];
+    out[i] = to_elem<TR>(s);
+  }
+}
+
+// ------------------------------------------------------------- host side --
+
+static int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+static bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+static uint8_t *ws_base(const lce_tensor *ws) {
+  uintptr_t p = reinterpret_cast<uintptr_t>(ws->data);
+  return reinterpret_cast<uint8_t *>((p + 255) & ~uintptr_t(255));
+}
+
+template <class TR, bool AK, bool BKM, class Epi>
+static void launch_gemm(bool vec, const GemmParams &g, int64_t splits, const Epi &epi,
+                        hipStream_t st) {
+  const int64_t tiles = cdiv(g.M, TR::BM) * g.tiles_n;
+  const dim3 grid{unsigned(tiles), unsigned(splits), 1u};
+  if (vec)
+    hipLaunchKernelGGL((gemm_kernel<TR, AK, BKM, true, Epi>), grid, dim3(TR::NT), 0, st, g, epi);
+  else
+    hipLaunchKernelGGL((gemm_kernel<TR, AK, BKM, false, Epi>), grid, dim3(TR::NT), 0, st, g, epi);
+}
+
+static void launch_guard(const int64_t *y, const uint8_t *mask, int64_t n, int64_t V,
+                         Control *ctl, hipStream_t st) {
+  hipLaunchKernelGGL(ctl_init_kernel, dim3(1), dim3(64), 0, st, ctl);
+  int64_t blocks = cdiv(n, 256);
+  if (blocks > 1024) blocks = 1024;
+  hipLaunchKernelGGL(guard_kernel, dim3(unsigned(blocks)), dim3(256), 0, st, y, mask, n, V, ctl);
+}
+
+template <class TR>
+static void forward_impl(const CEPlan &p, const void *H, const void *W, const int64_t *y,
+                         const uint8_t *mask, typename TR::Acc *lse_out, uint8_t *ws, bool vec,
+                         hipStream_t st) {
+  typedef typename TR::Acc Acc;
+  Control *ctl = reinterpret_cast<Control *>(ws);
+  Acc *partials = reinterpret_cast<Acc *>(ws + p.off_partials);
+  Acc *zy = reinterpret_cast<Acc *>(ws + p.off_zy);
+  double *loss_tok = reinterpret_cast<double *>(ws + p.off_losstok);
+  const typename TR::E *Hp = static_cast<const typename TR::E *>(H);
+  launch_guard(y, mask, p.n, p.V, ctl, st);
+  for (int64_t tok0 = 0; tok0 < p.n; tok0 += p.tok_per_pass) {
+    const int64_t ntok = p.tok_per_pass < p.n - tok0 ? p.tok_per_pass : p.n - tok0;
+    GemmParams g;
+    g.A = W; g.lda = p.D;
+    g.B = Hp + tok0 * p.D; g.ldb = p.D;
+    g.M = p.V; g.N = ntok; g.K = p.D;
+    g.M_read = p.V; g.N_read = ntok;
+    g.k_per_split = cdiv(p.D, TR::BK) * TR::BK;
+    g.tiles_n = cdiv(ntok, TR::BN);
+    g.bad = &ctl->bad;
+    FwdLseEpi<TR> epi{y + tok0, ntok, p.V, p.n_vparts, partials, zy + tok0};
+    launch_gemm<TR, true, true>(vec, g, 1, epi, st);
+    hipLaunchKernelGGL(fwd_merge_kernel<Acc>, dim3(unsigned(cdiv(ntok, 4))), dim3(256), 0, st,
+                       (const Acc *)partials, (const Acc *)(zy + tok0), p.n_vparts, ntok,
+                       lse_out + tok0, loss_tok + tok0, (const int32_t *)&ctl->bad);
+  }
+  hipLaunchKernelGGL(fwd_final_kernel<Acc>, dim3(1), dim3(1024), 0, st, (const double *)loss_tok,
+                     (const Acc *)lse_out, mask, p.n, ctl);
+}
+
+template <class TR>
+static void backward_impl(const CEPlan &p, const void *H, const void *W, const int64_t *y,
+                          const uint8_t *mask, const typename TR::Acc *lse, double z_coef,
+                          double grad_out, typename TR::E *dH, typename TR::Acc *dW,
+                          int accumulate, uint8_t *ws, bool vec, hipStream_t st) {
+  typedef typename TR::Acc Acc;
+  typedef typename TR::E E;
+  Control *ctl = reinterpret_cast<Control *>(ws);
+  E *dbuf = reinterpret_cast<E *>(ws + p.off_dbuf);
+  Acc *dhacc = reinterpret_cast<Acc *>(ws + p.off_dhacc);
+  const E *Hp = static_cast<const E *>(H);
+  const E *Wp = static_cast<const E *>(W);
+  launch_guard(y, mask, p.n, p.V, ctl, st);
+  for (int64_t s = 0; s < p.n_slabs; ++s) {
+    const int64_t vs0 = s * p.slab;
+    const int64_t rows = p.slab < p.V - vs0 ? p.slab : p.V - vs0;
+    const E *Wslab = Wp + vs0 * p.D;
+    {  // logits of the slab -> logit gradient
+      GemmParams g;
+      g.A = Wslab; g.lda = p.D;
+      g.B = Hp; g.ldb = p.D;
+      g.M = rows; g.N = p.n; g.K = p.D;
+      g.M_read = rows; g.N_read = p.n;
+      g.k_per_split = cdiv(p.D, TR::BK) * TR::BK;
+      g.tiles_n = cdiv(p.n, TR::BN);
+      g.bad = &ctl->bad;
+      DlogitEpi<TR> epi{y, mask, lse, p.n, vs0, rows, ctl, grad_out, z_coef, dbuf, p.d_ld};
+      launch_gemm<TR, true, true>(vec, g, 1, epi, st);
+    }
+    {  // d_weight rows of the slab = d^T H over all tokens
+      GemmParams g;
+      g.A = dbuf; g.lda = p.d_ld;
+      g.B = Hp; g.ldb = p.D;
+      g.M = rows; g.N = p.D; g.K = p.n;
+      g.M_read = rows; g.N_read = p.D;   // H rows are D long
+      g.k_per_split = cdiv(p.n, TR::BK) * TR::BK;
+      g.tiles_n = cdiv(p.D, TR::BN);
+      g.bad = &ctl->bad;
+      if (accumulate)
+        launch_gemm<TR, true, false>(vec, g, 1, StoreEpi<TR, true>{dW, p.D, vs0, rows, p.D, 0}, st);
+      else
+        launch_gemm<TR, true, false>(vec, g, 1, StoreEpi<TR, false>{dW, p.D, vs0, rows, p.D, 0}, st);
+    }
+    {  // d_hidden split accumulators += d W_slab
+      const int64_t kps = cdiv(cdiv(rows, p.dh_splits), TR::BK) * TR::BK;
+      GemmParams g;
+      g.A = dbuf; g.lda = p.d_ld;
+      g.B = Wslab; g.ldb = p.D;
+      g.M = p.n; g.N = p.D; g.K = rows;
+      g.M_read = p.d_ld; g.N_read = p.D;  // slab rows are d_ld long; W rows D long
+      g.k_per_split = kps;
+      g.tiles_n = cdiv(p.D, TR::BN);
+      g.bad = &ctl->bad;
+      if (s > 0)
+        launch_gemm<TR, false, false>(vec, g, p.dh_splits,
+                                      StoreEpi<TR, true>{dhacc, p.D, 0, p.n, p.D, p.n * p.D}, st);
+      else
+        launch_gemm<TR, false, false>(vec, g, p.dh_splits,
+                                      StoreEpi<TR, false>{dhacc, p.D, 0, p.n, p.D, p.n * p.D}, st);
+    }
+  }
+  int64_t count = p.n * p.D;
+  int64_t blocks = cdiv(count, 256);
+  if (blocks > 4096) blocks = 4096;
+  hipLaunchKernelGGL(dh_final_kernel<TR>, dim3(unsigned(blocks)), dim3(256), 0, st,
+                     (const Acc *)dhacc, p.dh_splits, count, dH, (const int32_t *)&ctl->bad);
+}
+
+}  // namespace lce
+
+using namespace lce;
+
+namespace {
+
+bool has(const lce_tensor *t) { return t && t->data; }
+
+// Dtype and length checks shared by forward and backward.
+int32_t check_ce_tensors(const lce_tensor *hidden, const lce_tensor *weight,
+                         const lce_tensor *targets, const lce_tensor *loss_mask, int64_t n,
+                         int64_t D, int64_t V, int32_t *dtype) {
+  if (!hidden || !weight || !targets) return LCE_LENGTH_MISMATCH;
+  const int32_t dt = hidden->dtype;
+  if (dt != LCE_BF16 && dt != LCE_F64) return LCE_DTYPE_MISMATCH;
+  if (weight->dtype != dt || targets->dtype != LCE_I64) return LCE_DTYPE_MISMATCH;
+  if (has(loss_mask) && loss_mask->dtype != LCE_U8) return LCE_DTYPE_MISMATCH;
+  *dtype = dt;
+  return LCE_OK;
+}
+
+int32_t check_ce_lengths(const lce_tensor *hidden, const lce_tensor *weight,
+                         const lce_tensor *targets, const lce_tensor *loss_mask, int64_t n,
+                         int64_t D, int64_t V) {
+  if (!has(hidden) || hidden->numel < n * D) return LCE_LENGTH_MISMATCH;
+  if (!has(weight) || weight->numel < V * D) return LCE_LENGTH_MISMATCH;
+  if (!has(targets) || targets->numel < n) return LCE_LENGTH_MISMATCH;
+  if (has(loss_mask) && loss_mask->numel < n) return LCE_LENGTH_MISMATCH;
+  return LCE_OK;
+}
+
+int32_t finish(hipStream_t st, Control *dev_ctl, Control *host_ctl) {
+  if (hipGetLastError() != hipSuccess) return LCE_DEVICE_ERROR;
+  if (hipMemcpyAsync(host_ctl, dev_ctl, sizeof(Control), hipMemcpyDeviceToHost, st) != hipSuccess)
+    return LCE_DEVICE_ERROR;
+  if (hipStreamSynchronize(st) != hipSuccess) return LCE_DEVICE_ERROR;
+  return host_ctl->bad ? LCE_TARGET_OUT_OF_RANGE : LCE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t lce_forward(const lce_tensor *hidden, const lce_tensor *weight,
+                    const lce_tensor *targets, const lce_tensor *loss_mask, int64_t n_tok,
+                    int64_t d_model, int64_t vocab, int64_t chunk, double z_coef,
+                    lce_tensor *lse_out, lce_tensor *workspace, lce_loss *out, void *stream) {
+  int32_t st = lce_dims_check(n_tok, d_model, vocab);
+  if (st != LCE_OK) return st;
+  st = lce_chunk_check(chunk, vocab);
+  if (st != LCE_OK) return st;
+  if (!finite_scalar(z_coef)) return LCE_NON_FINITE_SCALAR;
+  int32_t dt = 0;
+  st = check_ce_tensors(hidden, weight, targets, loss_mask, n_tok, d_model, vocab, &dt);
+  if (st != LCE_OK) return st;
+  if (!lse_out || !workspace) return LCE_LENGTH_MISMATCH;
+  if (lse_out->dtype != (dt == LCE_BF16 ? LCE_F32 : LCE_F64)) return LCE_DTYPE_MISMATCH;
+  if (workspace->dtype != LCE_U8) return LCE_DTYPE_MISMATCH;
+  CEPlan p;
+  st = plan_ce(n_tok, d_model, vocab, chunk, dt, &p);
+  if (st != LCE_OK) return st;
+  st = check_ce_lengths(hidden, weight, targets, loss_mask, n_tok, d_model, vocab);
+  if (st != LCE_OK) return st;
+  if (!has(lse_out) || lse_out->numel < n_tok) return LCE_LENGTH_MISMATCH;
+  if (!has(workspace) || workspace->numel < int64_t(p.total) + 256) return LCE_LENGTH_MISMATCH;
+  if (!out) return LCE_LENGTH_MISMATCH;
+
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  uint8_t *ws = ws_base(workspace);
+  const uint8_t *mask = has(loss_mask) ? static_cast<const uint8_t *>(loss_mask->data) : nullptr;
+  const int64_t *y = static_cast<const int64_t *>(targets->data);
+  (void)hipGetLastError();
+  if (dt == LCE_BF16) {
+    const bool vec = d_model % 8 == 0 && aligned16(hidden->data) && aligned16(weight->data);
+    forward_impl<TraitsBF16>(p, hidden->data, weight->data, y, mask,
+                             static_cast<float *>(lse_out->data), ws, vec, s);
+  } else {
+    const bool vec = d_model % 2 == 0 && aligned16(hidden->data) && aligned16(weight->data);
+    forward_impl<TraitsF64>(p, hidden->data, weight->data, y, mask,
+                            static_cast<double *>(lse_out->data), ws, vec, s);
+  }
+  Control hc;
+  st = finish(s, reinterpret_cast<Control *>(ws), &hc);
+  if (st != LCE_OK) return st;
+  out->loss_sum = hc.loss_sum;
+  out->z_sum = hc.z_sum;
+  out->n_counted = hc.count;
+  out->loss_mean = hc.count ? hc.loss_sum / double(hc.count) : 0.0;
+  out->z_mean = hc.count ? hc.z_sum / double(hc.count) : 0.0;
+  return LCE_OK;
+}
+
+int32_t lce_backward(const lce_tensor *hidden, const lce_tensor *weight,
+                     const lce_tensor *targets, const lce_tensor *loss_mask,
+                     const lce_tensor *lse, int64_t n_tok, int64_t d_model, int64_t vocab,
+                     int64_t chunk, double z_coef, double grad_out, lce_tensor *d_hidden,
+                     lce_tensor *d_weight, int32_t accumulate_d_weight,
+                     lce_tensor *workspace, void *stream) {
+  int32_t st = lce_dims_check(n_tok, d_model, vocab);
+  if (st != LCE_OK) return st;
+  st = lce_chunk_check(chunk, vocab);
+  if (st != LCE_OK) return st;
+  if (!finite_scalar(z_coef) || !finite_scalar(grad_out)) return LCE_NON_FINITE_SCALAR;
+  int32_t dt = 0;
+  st = check_ce_tensors(hidden, weight, targets, loss_mask, n_tok, d_model, vocab, &dt);
+  if (st != LCE_OK) return st;
+  if (!lse || !d_hidden || !d_weight || !workspace) return LCE_LENGTH_MISMATCH;
+  const int32_t acc_dt = dt == LCE_BF16 ? LCE_F32 : LCE_F64;
+  if (lse->dtype != acc_dt || d_weight->dtype != acc_dt || d_hidden->dtype != dt)
+    return LCE_DTYPE_MISMATCH;
+  if (workspace->dtype != LCE_U8) return LCE_DTYPE_MISMATCH;
+  CEPlan p;
+  st = plan_ce(n_tok, d_model, vocab, chunk, dt, &p);
+  if (st != LCE_OK) return st;
+  st = check_ce_lengths(hidden, weight, targets, loss_mask, n_tok, d_model, vocab);
+  if (st != LCE_OK) return st;
+  if (!has(lse) || lse->numel < n_tok) return LCE_LENGTH_MISMATCH;
+  if (!has(d_hidden) || d_hidden->numel < n_tok * d_model) return LCE_LENGTH_MISMATCH;
+  if (!has(d_weight) || d_weight->numel < vocab * d_model) return LCE_LENGTH_MISMATCH;
+  if (!has(workspace) || workspace->numel < int64_t(p.total) + 256) return LCE_LENGTH_MISMATCH;
+
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  uint8_t *ws = ws_base(workspace);
+  const uint8_t *mask = has(loss_mask) ? static_cast<const uint8_t *>(loss_mask->data) : nullptr;
+  const int64_t *y = static_cast<const int64_t *>(targets->data);
+  (void)hipGetLastError();
+  if (dt == LCE_BF16) {
+    const bool vec = d_model % 8 == 0 && aligned16(hidden->data) && aligned16(weight->data);
+    backward_impl<TraitsBF16>(p, hidden->data, weight->data, y, mask,
+                              static_cast<const float *>(lse->data), z_coef, grad_out,
+                              static_cast<uint16_t *>(d_hidden->data),
+                              static_cast<float *>(d_weight->data), accumulate_d_weight != 0, ws,
+                              vec, s);
+  } else {
+    const bool vec = d_model % 2 == 0 && aligned16(hidden->data) && aligned16(weight->data);
+    backward_impl<TraitsF64>(p, hidden->data, weight->data, y, mask,
+                             static_cast<const double *>(lse->data), z_coef, grad_out,
+                             static_cast<double *>(d_hidden->data),
+                             static_cast<double *>(d_weight->data), accumulate_d_weight != 0, ws,
+                             vec, s);
+  }
+  Control hc;
+  return finish(s, reinterpret_cast<Control *>(ws), &hc);
+}
+
+}  // extern "C"

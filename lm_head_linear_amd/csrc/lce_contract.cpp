@@ -1,0 +1,187 @@
+// lce_contract.cpp -- host-only contract of liblce.so: status names, the two
+// budgets, the peak-cell reporter and workspace planning.  Integer arithmetic
+// only; nothing here touches a device.
+//
+// Source: "Loss functions and resident-context kernels" (algenta docs), the
+// lossk function table, "Status codes" and "The two budgets are genuinely
+// different questions".
+#include <cmath>
+
+#include "lce_internal.h"
+
+namespace lce {
+
+bool finite_scalar(double x) { return std::isfinite(x); }
+
+size_t dtype_size(int32_t dtype) {
+  switch (dtype) {
+    case LCE_BF16: return 2;
+    case LCE_F32: return 4;
+    case LCE_F64: return 8;
+    case LCE_I64: return 8;
+    case LCE_U8: return 1;
+    default: return 0;
+  }
+}
+
+static int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+static int64_t round_up(int64_t a, int64_t b) { return ceil_div(a, b) * b; }
+static size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+int32_t plan_ce(int64_t n, int64_t D, int64_t V, int64_t chunk, int32_t dtype, CEPlan *p) {
+  int32_t st = lce_dims_check(n, D, V);
+  if (st != LCE_OK) return st;
+  st = lce_chunk_check(chunk, V);
+  if (st != LCE_OK) return st;
+  if (dtype != LCE_BF16 && dtype != LCE_F64) return LCE_DTYPE_MISMATCH;
+
+  CEPlan q;
+  q.dtype = dtype;
+  q.n = n; q.D = D; q.V = V; q.chunk = chunk;
+  const bool bf = dtype == LCE_BF16;
+  q.elem = bf ? 2 : 8;
+  q.acc = bf ? 4 : 8;
+  const int64_t tile_m = bf ? kBf16TileM : kF64TileM;
+  const int64_t budget = chunk * V;  // logit-derived cells allowed at once (<= 2^27)
+
+  // Forward: each token keeps n_vparts (max, sum) pairs; as many tokens run
+  // per launch as fit the chunk*vocab cell budget.
+  q.wave_m = bf ? kBf16WaveM : kF64WaveM;
+  q.n_vparts = ceil_div(V, q.wave_m);
+  int64_t tpp = budget / (2 * q.n_vparts);
+  if (tpp < 1) tpp = 1;
+  q.tok_per_pass = tpp < n ? tpp : n;
+
+  // Backward: the logit-gradient buffer holds a slab of vocabulary rows for
+  // every token, at most chunk*vocab cells; slabs are balanced in size.
+  q.d_ld = round_up(n, 8);
+  int64_t slab_max = budget / q.d_ld;
+  if (slab_max >= tile_m) slab_max = slab_max / tile_m * tile_m;
+  else if (slab_max >= 32) slab_max = slab_max / 32 * 32;
+  if (slab_max < 1) slab_max = 1;
+  if (slab_max >= V) {
+    q.slab = V;
+    q.n_slabs = 1;
+  } else {
+    q.n_slabs = ceil_div(V, slab_max);
+    int64_t gran = slab_max >= tile_m ? tile_m : (slab_max >= 32 ? 32 : 1);
+    int64_t bal = round_up(ceil_div(V, q.n_slabs), gran);
+    q.slab = bal <= slab_max ? bal : slab_max;
+    q.n_slabs = ceil_div(V, q.slab);
+  }
+  // Split the vocabulary reduction of d_hidden so that the grid has about one
+  // workgroup per compute unit (256), keeping each split at least 512 deep.
+  const int64_t tile_n = bf ? 256 : 128;
+  int64_t out_tiles = ceil_div(n, tile_m) * ceil_div(D, tile_n);
+  int64_t splits = ceil_div(256, out_tiles);
+  int64_t max_by_depth = q.slab / 512;
+  if (splits > max_by_depth) splits = max_by_depth;
+  if (splits > 16) splits = 16;
+  if (splits < 1) splits = 1;
+  q.dh_splits = splits;
+
+  // Workspace: [control | forward partials | zy | per-token loss] and the
+  // backward's [slab buffer | d_hidden split accumulators] overlap the
+  // forward region (the two calls never run on one workspace at once).
+  size_t off = kControlBytes;
+  size_t fwd_begin = off;
+  q.off_partials = off;
+  off = align256(off + size_t(q.tok_per_pass) * size_t(q.n_vparts) * 2 * q.acc);
+  q.off_zy = off;
+  off = align256(off + size_t(n) * q.acc);
+  q.off_losstok = off;
+  off = align256(off + size_t(n) * 8);
+  size_t fwd_end = off;
+  off = fwd_begin;
+  q.off_dbuf = off;
+  off = align256(off + size_t(q.slab) * size_t(q.d_ld) * q.elem);
+  q.off_dhacc = off;
+  off = align256(off + size_t(q.dh_splits) * size_t(n) * size_t(D) * q.acc);
+  q.total = off > fwd_end ? off : fwd_end;
+  *p = q;
+  return LCE_OK;
+}
+
+int32_t plan_distill(int64_t n, int64_t V, DistillPlan *p) {
+  if (n < 1 || V < 1) return LCE_EMPTY_DIMENSION;
+  if (n > LCE_MAX_N_TOK || V > LCE_MAX_VOCAB) return LCE_DIMENSION_TOO_LARGE;
+  DistillPlan q;
+  q.n = n; q.V = V;
+  q.off_rows = kControlBytes;
+  q.total = align256(q.off_rows + size_t(n) * 2 * sizeof(double));
+  *p = q;
+  return LCE_OK;
+}
+
+}  // namespace lce
+
+using namespace lce;
+
+extern "C" {
+
+const char *lce_status_name(int32_t code) {
+  static const char *const names[] = {
+      "ok", "empty_dimension", "length_mismatch", "dimension_too_large",
+      "work_budget_exceeded", "non_finite_scalar", "target_id_out_of_range",
+      "chunk_exceeds_logit_budget", "unknown_objective", "device_error", "dtype_mismatch"};
+  if (code < LCE_OK || code > LCE_DTYPE_MISMATCH) return "unknown_status";
+  return names[code - LCE_OK];
+}
+
+int32_t lce_work_fits(int64_t n, int64_t d, int64_t v, int64_t ceiling) {
+  if (n < 1 || d < 1 || v < 1 || ceiling < 0) return 0;
+  // n*d*v <= ceiling  <=>  n <= floor(floor(ceiling / v) / d)
+  const int64_t per_row = ceiling / v;
+  return n <= per_row / d ? 1 : 0;
+}
+
+int32_t lce_dims_check(int64_t n_tok, int64_t d_model, int64_t vocab) {
+  if (n_tok < 1 || d_model < 1 || vocab < 1) return LCE_EMPTY_DIMENSION;
+  if (n_tok > LCE_MAX_N_TOK || d_model > LCE_MAX_D_MODEL || vocab > LCE_MAX_VOCAB)
+    return LCE_DIMENSION_TOO_LARGE;
+  return lce_work_fits(n_tok, d_model, vocab, LCE_MAX_WORK_CELLS) ? LCE_OK
+                                                                  : LCE_WORK_BUDGET_EXCEEDED;
+}
+
+int32_t lce_chunk_check(int64_t chunk, int64_t vocab) {
+  if (chunk < 1 || vocab < 1) return LCE_EMPTY_DIMENSION;
+  // chunk*vocab > 2^27  <=>  chunk > floor(2^27 / vocab)
+  return chunk > LCE_MAX_LOGIT_CELLS / vocab ? LCE_CHUNK_EXCEEDS_LOGIT_BUDGET : LCE_OK;
+}
+
+double lce_logit_cells(int64_t chunk, int64_t vocab) {
+  if (chunk < 1 || vocab < 1) return -1.0;
+  return double(chunk) * double(vocab);
+}
+
+int32_t lce_peak_cells(int64_t n_tok, int64_t vocab, int64_t chunk, lce_peak *out) {
+  if (!out) return LCE_LENGTH_MISMATCH;
+  if (n_tok < 1 || vocab < 1 || chunk < 1) {
+    *out = lce_peak{-1.0, -1.0, -1.0, 0, LCE_EMPTY_DIMENSION};
+    return LCE_EMPTY_DIMENSION;
+  }
+  const int64_t rows = chunk < n_tok ? chunk : n_tok;
+  out->chunked_cells = lce_logit_cells(rows, vocab);
+  out->materialized_cells = lce_logit_cells(n_tok, vocab);
+  out->ratio = out->materialized_cells / out->chunked_cells;
+  out->n_chunks = (n_tok + chunk - 1) / chunk;
+  out->status = lce_chunk_check(chunk, vocab);
+  return out->status;
+}
+
+int64_t lce_workspace_bytes(int64_t n_tok, int64_t d_model, int64_t vocab, int64_t chunk,
+                            int32_t dtype) {
+  CEPlan p;
+  int32_t st = plan_ce(n_tok, d_model, vocab, chunk, dtype, &p);
+  if (st != LCE_OK) return -int64_t(st);
+  return int64_t(p.total) + 256;  // slack: the library aligns the base to 256 bytes
+}
+
+int64_t lce_distill_workspace_bytes(int64_t n_tok, int64_t vocab) {
+  DistillPlan p;
+  int32_t st = plan_distill(n_tok, vocab, &p);
+  if (st != LCE_OK) return -int64_t(st);
+  return int64_t(p.total) + 256;
+}
+
+}  // extern "C"

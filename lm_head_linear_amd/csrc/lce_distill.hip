@@ -1,0 +1,395 @@
+// lce_distill.hip -- logit distillation against a full teacher distribution,
+// fused forward + backward, with z-loss over the same student softmax.
+//
+// Source: "Fuse distillation + z-loss in the triton monolithic path"
+// (Fast-LLM pull request 566), sections "What it does" and "Changes": the
+// from-distribution kernels return loss, z-loss and the logit gradient; the
+// z term adds lse^2 to the forward and 2*grad_z*lse*p to the gradient and
+// shares the distillation loss mask and divisor.
+//
+// One workgroup per token row, streaming the row twice (HBM-bound):
+//   pass 1 reads student s and teacher u once, keeping online (max, sum exp)
+//          for x = s/T and y = u/T plus one objective accumulator tied to one
+//          of the two running maxima:
+//            0 cross-entropy  A = sum e^(y-my) x      L = lse_x - A/sy
+//            1 forward KL     A = sum e^(y-my) (y-x)  L = A/sy + lse_x - lse_y
+//            2 reverse KL     A = sum e^(x-mx) (x-y)  L = A/sx + lse_y - lse_x
+//   pass 2 re-reads the row (from the 256 MB Infinity Cache for rows in
+//          flight) and writes grad = (grad_out/C)(dL/dx + 2 z lse_x p)/T with
+//          dL/dx = p - q (0, 1) or p (ls - lq - L) (2).
+// Masked rows only write zeros.  Per-row L and lse_x go to the workspace; a
+// fixed-order fp64 reduction forms the means.
+#include <hip/hip_runtime.h>
+
+#include <climits>
+#include <cmath>
+
+#include "lce_internal.h"
+
+namespace lce {
+
+namespace {
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+template <class T> struct IO;
+template <> struct IO<uint16_t> {  // bf16 bits
+  typedef float C;
+  __device__ static inline void load8(const uint16_t *p, float *o) {
+    const u32x4 v = *reinterpret_cast<const u32x4 *>(p);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      o[2 * i] = __uint_as_float(v[i] << 16);
+      o[2 * i + 1] = __uint_as_float(v[i] & 0xffff0000u);
+    }
+  }
+  __device__ static inline float load1(const uint16_t *p) { return __uint_as_float(uint32_t(*p) << 16); }
+  __device__ static inline uint16_t cvt(float f) {
+    uint32_t u = __float_as_uint(f);
+    if ((u & 0x7fffffffu) > 0x7f800000u) return uint16_t((u >> 16) | 0x40);
+    u += 0x7fffu + ((u >> 16) & 1u);
+    return uint16_t(u >> 16);
+  }
+  __device__ static inline void store8(uint16_t *p, const float *g) {
+    u32x4 v;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) v[i] = uint32_t(cvt(g[2 * i])) | (uint32_t(cvt(g[2 * i + 1])) << 16);
+    *reinterpret_cast<u32x4 *>(p) = v;
+  }
+  __device__ static inline void store1(uint16_t *p, float g) { *p = cvt(g); }
+};
+template <> struct IO<float> {
+  typedef float C;
+  __device__ static inline void load8(const float *p, float *o) {
+    const float4 a = reinterpret_cast<const float4 *>(p)[0];
+    const float4 b = reinterpret_cast<const float4 *>(p)[1];
+    o[0] = a.x; o[1] = a.y; o[2] = a.z; o[3] = a.w; o[4] = b.x; o[5] = b.y; o[6] = b.z; o[7] = b.w;
+  }
+  __device__ static inline float load1(const float *p) { return *p; }
+  __device__ static inline void store8(float *p, const float *g) {
+    reinterpret_cast<float4 *>(p)[0] = make_float4(g[0], g[1], g[2], g[3]);
+    reinterpret_cast<float4 *>(p)[1] = make_float4(g[4], g[5], g[6], g[7]);
+  }
+  __device__ static inline void store1(float *p, float g) { *p = g; }
+};
+template <> struct IO<double> {
+  typedef double C;
+  __device__ static inline void load8(const double *p, double *o) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const double2 a = reinterpret_cast<const double2 *>(p)[i];
+      o[2 * i] = a.x;
+      o[2 * i + 1] = a.y;
+    }
+  }
+  __device__ static inline double load1(const double *p) { return *p; }
+  __device__ static inline void store8(double *p, const double *g) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) reinterpret_cast<double2 *>(p)[i] = make_double2(g[2 * i], g[2 * i + 1]);
+  }
+  __device__ static inline void store1(double *p, double g) { *p = g; }
+};
+
+template <class C> __device__ inline C dexp(C x);
+template <> __device__ inline float dexp<float>(float x) {
+  return __builtin_amdgcn_exp2f(x * 1.4426950408889634f);
+}
+template <> __device__ inline double dexp<double>(double x) { return exp(x); }
+template <class C> __device__ inline C dlog(C x);
+template <> __device__ inline float dlog<float>(float x) { return logf(x); }
+template <> __device__ inline double dlog<double>(double x) { return log(x); }
+
+// Running (max, sum of exp(v - max)) with a weighted sum tied to the same max.
+template <class C>
+struct Online {
+  C m, s, a;
+  __device__ inline void init() { m = -INFINITY; s = 0; a = 0; }
+  __device__ inline void merge(const Online &o) {
+    const C M = m > o.m ? m : o.m;
+    if (M == -INFINITY) return;
+    const C f1 = dexp<C>(m - M), f2 = dexp<C>(o.m - M);
+    s = s * f1 + o.s * f2;
+    a = a * f1 + o.a * f2;
+    m = M;
+  }
+};
+
+template <class C>
+__device__ inline Online<C> shfl_xor_online(const Online<C> &v, int o) {
+  Online<C> r;
+  r.m = __shfl_xor(v.m, o);
+  r.s = __shfl_xor(v.s, o);
+  r.a = __shfl_xor(v.a, o);
+  return r;
+}
+
+constexpr int kBlock = 256;
+
+// Reduce within the block in a fixed order; thread 0 gets the result.
+template <class C>
+__device__ inline void block_merge(Online<C> &v, Online<C> *sh) {
+  for (int o = 1; o < 64; o <<= 1) {
+    Online<C> w = shfl_xor_online(v, o);
+    v.merge(w);
+  }
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  if (lane == 0) sh[wave] = v;
+  __syncthreads();
+  if (threadIdx.x == 0)
+    for (int w = 1; w < kBlock / 64; ++w) v.merge(sh[w]);
+}
+
+template <class T, int OBJ, bool VEC>
+__global__ void __launch_bounds__(kBlock)
+distill_row_kernel(const T *S, const T *U, const uint8_t *mask, int64_t V, double inv_T,
+                   double z_coef, double grad_out, const Control *ctl, T *grad, double *row_out) {
+  typedef typename IO<T>::C C;
+  const int64_t t = blockIdx.x;
+  const T *s_row = S + t * V;
+  const T *u_row = U + t * V;
+  T *g_row = grad + t * V;
+  const C iT = C(inv_T);
+  const int tid = threadIdx.x;
+  const int64_t nvec = VEC ? V / 8 : 0;
+  const int64_t tail0 = nvec * 8;
+
+  if (mask && !mask[t]) {
+    const C z[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+    for (int64_t i = tid; i < nvec; i += kBlock) IO<T>::store8(g_row + i * 8, z);
+    for (int64_t v = tail0 + tid; v < V; v += kBlock) IO<T>::store1(g_row + v, C(0));
+    if (tid == 0) { row_out[2 * t] = 0.0; row_out[2 * t + 1] = 0.0; }
+    return;
+  }
+
+  // Pass 1: online statistics.  fx tracks x; fy tracks y.  The objective
+  // accumulator rides on fy (objectives 0, 1) or fx (objective 2).
+  Online<C> fx, fy;
+  fx.init();
+  fy.init();
+  auto consume = [&](const C *xs, const C *ys, int cnt) {
+    C lmx = -INFINITY, lmy = -INFINITY;
+    for (int i = 0; i < cnt; ++i) {
+      lmx = xs[i] > lmx ? xs[i] : lmx;
+      lmy = ys[i] > lmy ? ys[i] : lmy;
+    }
+    const C nmx = fx.m > lmx ? fx.m : lmx;
+    const C nmy = fy.m > lmy ? fy.m : lmy;
+    const C rx = dexp<C>(fx.m - nmx), ry = dexp<C>(fy.m - nmy);
+    fx.s *= rx; fx.a *= rx; fx.m = nmx;
+    fy.s *= ry; fy.a *= ry; fy.m = nmy;
+    for (int i = 0; i < cnt; ++i) {
+      const C ex = dexp<C>(xs[i] - nmx), ey = dexp<C>(ys[i] - nmy);
+      fx.s += ex;
+      fy.s += ey;
+      if (OBJ == 0) fy.a += ey * xs[i];
+      else if (OBJ == 1) fy.a += ey * (ys[i] - xs[i]);
+      else fx.a += ex * (xs[i] - ys[i]);
+    }
+  };
+  for (int64_t i = tid; i < nvec; i += kBlock) {
+    C xs[8], ys[8];
+    IO<T>::load8(s_row + i * 8, xs);
+    IO<T>::load8(u_row + i * 8, ys);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) { xs[j] *= iT; ys[j] *= iT; }
+    consume(xs, ys, 8);
+  }
+  for (int64_t v = tail0 + tid; v < V; v += kBlock) {
+    C xs[1] = {IO<T>::load1(s_row + v) * iT}, ys[1] = {IO<T>::load1(u_row + v) * iT};
+    consume(xs, ys, 1);
+  }
+
+  __shared__ Online<C> sh_x[kBlock / 64], sh_y[kBlock / 64];
+  __shared__ C sh_stats[3];
+  block_merge(fx, sh_x);
+  block_merge(fy, sh_y);
+  if (tid == 0) {
+    const C lse_x = fx.m + dlog<C>(fx.s);
+    const C lse_y = fy.m + dlog<C>(fy.s);
+    C L;
+    if (OBJ == 0) L = lse_x - fy.a / fy.s;
+    else if (OBJ == 1) L = fy.a / fy.s + lse_x - lse_y;
+    else L = fx.a / fx.s + lse_y - lse_x;
+    sh_stats[0] = lse_x;
+    sh_stats[1] = lse_y;
+    sh_stats[2] = L;
+    row_out[2 * t] = double(L);
+    row_out[2 * t + 1] = double(lse_x);
+  }
+  __syncthreads();
+  const C lse_x = sh_stats[0], lse_y = sh_stats[1], L = sh_stats[2];
+  const int64_t cnt = ctl->count;
+  const C scale = cnt ? C(grad_out / double(cnt) * inv_T) : C(0);
+  const C zc = C(2.0 * z_coef) * lse_x;
+
+  // Pass 2: gradient.
+  auto grad_of = [&](C x, C y) -> C {
+    const C ls = x - lse_x;
+    const C p = dexp<C>(ls);
+    C d;
+    if (OBJ == 2) d = p * (ls - (y - lse_y) - L);
+    else d = p - dexp<C>(y - lse_y);
+    return scale * (d + zc * p);
+  };
+  for (int64_t i = tid; i < nvec; i += kBlock) {
+    C xs[8], ys[8], gs[8];
+    IO<T>::load8(s_row + i * 8, xs);
+    IO<T>::load8(u_row + i * 8, ys);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) gs[j] = grad_of(xs[j] * iT, ys[j] * iT);
+    IO<T>::store8(g_row + i * 8, gs);
+  }
+  for (int64_t v = tail0 + tid; v < V; v += kBlock)
+    IO<T>::store1(g_row + v, grad_of(IO<T>::load1(s_row + v) * iT, IO<T>::load1(u_row + v) * iT));
+}
+
+__global__ void distill_init_kernel(Control *ctl) {
+  if (threadIdx.x == 0) {
+    ctl->bad = 0;
+    ctl->first_bad = LLONG_MAX;
+    ctl->count = 0;
+    ctl->loss_sum = 0.0;
+    ctl->z_sum = 0.0;
+  }
+}
+
+__global__ void distill_count_kernel(const uint8_t *mask, int64_t n, Control *ctl) {
+  __shared__ unsigned long long sh[4];
+  unsigned long long c = 0;
+  for (int64_t t = int64_t(blockIdx.x) * blockDim.x + threadIdx.x; t < n;
+       t += int64_t(gridDim.x) * blockDim.x)
+    c += mask ? (mask[t] != 0) : 1;
+  for (int o = 32; o > 0; o >>= 1) c += __shfl_xor(c, o);
+  if ((threadIdx.x & 63) == 0) sh[threadIdx.x >> 6] = c;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    for (int w = 1; w < int(blockDim.x >> 6); ++w) c += sh[w];
+    if (c) atomicAdd(reinterpret_cast<unsigned long long *>(&ctl->count), c);
+  }
+}
+
+// Fixed-order fp64 sums of the per-row loss and lse^2 over counted rows.
+__global__ void distill_final_kernel(const double *row_out, const uint8_t *mask, int64_t n,
+                                     Control *ctl) {
+  __shared__ double s_l[1024], s_z[1024];
+  double l = 0.0, z = 0.0;
+  for (int64_t t = threadIdx.x; t < n; t += blockDim.x) {
+    if (mask && !mask[t]) continue;
+    l += row_out[2 * t];
+    z += row_out[2 * t + 1] * row_out[2 * t + 1];
+  }
+  s_l[threadIdx.x] = l;
+  s_z[threadIdx.x] = z;
+  __syncthreads();
+  for (int w = blockDim.x / 2; w > 0; w >>= 1) {
+    if (int(threadIdx.x) < w) {
+      s_l[threadIdx.x] += s_l[threadIdx.x + w];
+      s_z[threadIdx.x] += s_z[threadIdx.x + w];
+    }
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) {
+    ctl->loss_sum = s_l[0];
+    ctl->z_sum = s_z[0];
+  }
+}
+
+template <class T, int OBJ>
+void launch_rows(bool vec, const T *S, const T *U, const uint8_t *mask, int64_t n, int64_t V,
+                 double inv_T, double z, double go, const Control *ctl, T *grad, double *rows,
+                 hipStream_t st) {
+  if (vec)
+    hipLaunchKernelGGL((distill_row_kernel<T, OBJ, true>), dim3(unsigned(n)), dim3(kBlock), 0, st,
+                       S, U, mask, V, inv_T, z, go, ctl, grad, rows);
+  else
+    hipLaunchKernelGGL((distill_row_kernel<T, OBJ, false>), dim3(unsigned(n)), dim3(kBlock), 0, st,
+                       S, U, mask, V, inv_T, z, go, ctl, grad, rows);
+}
+
+template <class T>
+void distill_impl(int objective, bool vec, const T *S, const T *U, const uint8_t *mask,
+                  int64_t n, int64_t V, double T_, double z, double go, Control *ctl, T *grad,
+                  double *rows, hipStream_t st) {
+  hipLaunchKernelGGL(distill_init_kernel, dim3(1), dim3(64), 0, st, ctl);
+  int64_t blocks = (n + 255) / 256;
+  if (blocks > 1024) blocks = 1024;
+  hipLaunchKernelGGL(distill_count_kernel, dim3(unsigned(blocks)), dim3(256), 0, st, mask, n, ctl);
+  const double inv_T = 1.0 / T_;
+  if (objective == 0) launch_rows<T, 0>(vec, S, U, mask, n, V, inv_T, z, go, ctl, grad, rows, st);
+  else if (objective == 1) launch_rows<T, 1>(vec, S, U, mask, n, V, inv_T, z, go, ctl, grad, rows, st);
+  else launch_rows<T, 2>(vec, S, U, mask, n, V, inv_T, z, go, ctl, grad, rows, st);
+  hipLaunchKernelGGL(distill_final_kernel, dim3(1), dim3(1024), 0, st, (const double *)rows, mask,
+                     n, ctl);
+}
+
+bool has(const lce_tensor *t) { return t && t->data; }
+bool aligned(const void *p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+}  // namespace
+}  // namespace lce
+
+using namespace lce;
+
+extern "C" int32_t lce_distill_fwd_bwd(const lce_tensor *student, const lce_tensor *teacher,
+                                       const lce_tensor *loss_mask, int64_t n_tok, int64_t vocab,
+                                       int32_t objective, double temperature, double z_coef,
+                                       double grad_out, lce_tensor *grad_logits,
+                                       lce_tensor *workspace, lce_loss *out, void *stream) {
+  DistillPlan p;
+  int32_t st = plan_distill(n_tok, vocab, &p);
+  if (st != LCE_OK) return st;
+  if (!finite_scalar(z_coef) || !finite_scalar(grad_out) || !finite_scalar(temperature) ||
+      !(temperature > 0.0))
+    return LCE_NON_FINITE_SCALAR;
+  if (!student || !teacher || !grad_logits || !workspace) return LCE_LENGTH_MISMATCH;
+  const int32_t dt = student->dtype;
+  if (dt != LCE_BF16 && dt != LCE_F32 && dt != LCE_F64) return LCE_DTYPE_MISMATCH;
+  if (teacher->dtype != dt || grad_logits->dtype != dt) return LCE_DTYPE_MISMATCH;
+  if (has(loss_mask) && loss_mask->dtype != LCE_U8) return LCE_DTYPE_MISMATCH;
+  if (workspace->dtype != LCE_U8) return LCE_DTYPE_MISMATCH;
+  const int64_t cells = n_tok * vocab;
+  if (!has(student) || student->numel < cells || !has(teacher) || teacher->numel < cells ||
+      !has(grad_logits) || grad_logits->numel < cells)
+    return LCE_LENGTH_MISMATCH;
+  if (has(loss_mask) && loss_mask->numel < n_tok) return LCE_LENGTH_MISMATCH;
+  if (!has(workspace) || workspace->numel < int64_t(p.total) + 256) return LCE_LENGTH_MISMATCH;
+  if (objective < 0 || objective > 2) return LCE_UNKNOWN_OBJECTIVE;
+  if (!out) return LCE_LENGTH_MISMATCH;
+
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  uintptr_t base = (reinterpret_cast<uintptr_t>(workspace->data) + 255) & ~uintptr_t(255);
+  uint8_t *ws = reinterpret_cast<uint8_t *>(base);
+  Control *ctl = reinterpret_cast<Control *>(ws);
+  double *rows = reinterpret_cast<double *>(ws + p.off_rows);
+  const uint8_t *mask = has(loss_mask) ? static_cast<const uint8_t *>(loss_mask->data) : nullptr;
+  const size_t esz = dtype_size(dt);
+  const bool vec = (vocab % 8 == 0) && aligned(student->data, 16) && aligned(teacher->data, 16) &&
+                   aligned(grad_logits->data, 16) && (esz * 8) % 16 == 0;
+  (void)hipGetLastError();
+  if (dt == LCE_BF16)
+    distill_impl<uint16_t>(objective, vec, static_cast<const uint16_t *>(student->data),
+                           static_cast<const uint16_t *>(teacher->data), mask, n_tok, vocab,
+                           temperature, z_coef, grad_out, ctl,
+                           static_cast<uint16_t *>(grad_logits->data), rows, s);
+  else if (dt == LCE_F32)
+    distill_impl<float>(objective, vec, static_cast<const float *>(student->data),
+                        static_cast<const float *>(teacher->data), mask, n_tok, vocab,
+                        temperature, z_coef, grad_out, ctl, static_cast<float *>(grad_logits->data),
+                        rows, s);
+  else
+    distill_impl<double>(objective, vec, static_cast<const double *>(student->data),
+                         static_cast<const double *>(teacher->data), mask, n_tok, vocab,
+                         temperature, z_coef, grad_out, ctl,
+                         static_cast<double *>(grad_logits->data), rows, s);
+  if (hipGetLastError() != hipSuccess) return LCE_DEVICE_ERROR;
+  Control hc;
+  if (hipMemcpyAsync(&hc, ctl, sizeof(Control), hipMemcpyDeviceToHost, s) != hipSuccess)
+    return LCE_DEVICE_ERROR;
+  if (hipStreamSynchronize(s) != hipSuccess) return LCE_DEVICE_ERROR;
+  out->loss_sum = hc.loss_sum;
+  out->z_sum = hc.z_sum;
+  out->n_counted = hc.count;
+  out->loss_mean = hc.count ? hc.loss_sum / double(hc.count) : 0.0;
+  out->z_mean = hc.count ? hc.z_sum / double(hc.count) : 0.0;
+  return LCE_OK;
+}

@@ -1,0 +1,66 @@
+// lce_internal.h -- host-side pieces shared by the translation units of liblce.so.
+#pragma once
+
+#include <cstddef>
+#include <cstdint>
+
+#include "../../include/lce.h"
+
+namespace lce {
+
+// Device-side control block at offset 0 of every workspace.  The guard
+// kernel fills bad/first_bad/count; the reduction kernels fill the sums.
+struct Control {
+  int32_t bad;          // nonzero when a target id is out of range
+  int32_t pad0;
+  int64_t first_bad;    // smallest offending token index (diagnostic)
+  int64_t count;        // counted (unmasked) tokens
+  int64_t pad1;
+  double loss_sum;
+  double z_sum;
+  double pad2[10];
+};
+static_assert(sizeof(Control) <= 256, "control block must fit its slot");
+constexpr size_t kControlBytes = 256;
+
+// Tile geometry the host planner needs (kept equal to the device traits).
+constexpr int64_t kBf16TileM = 256;   // vocabulary rows per GEMM tile (bf16)
+constexpr int64_t kBf16WaveM = 128;   // rows per forward partial (bf16)
+constexpr int64_t kF64TileM = 128;
+constexpr int64_t kF64WaveM = 64;
+
+// How one lce_forward / lce_backward call is laid out for a shape.
+struct CEPlan {
+  int32_t dtype = 0;          // LCE_BF16 or LCE_F64
+  int64_t n = 0, D = 0, V = 0, chunk = 0;
+  size_t elem = 0;            // bytes per input element
+  size_t acc = 0;             // bytes per accumulator element
+  // forward
+  int64_t wave_m = 0;         // vocabulary rows reduced into one partial
+  int64_t n_vparts = 0;       // partials per token
+  int64_t tok_per_pass = 0;   // tokens per forward launch
+  // backward
+  int64_t slab = 0;           // vocabulary rows per logit-gradient slab
+  int64_t n_slabs = 0;
+  int64_t d_ld = 0;           // row stride (tokens) of the slab buffer
+  int64_t dh_splits = 0;      // split-K factor of the d_hidden product
+  // workspace layout (byte offsets)
+  size_t off_partials = 0, off_zy = 0, off_losstok = 0;
+  size_t off_dbuf = 0, off_dhacc = 0;
+  size_t total = 0;
+};
+
+// Fills *p; returns LCE_OK or a refusal status.
+int32_t plan_ce(int64_t n, int64_t D, int64_t V, int64_t chunk, int32_t dtype, CEPlan *p);
+
+struct DistillPlan {
+  int64_t n = 0, V = 0;
+  size_t off_rows = 0;        // per-row {loss, lse} doubles
+  size_t total = 0;
+};
+int32_t plan_distill(int64_t n, int64_t V, DistillPlan *p);
+
+bool finite_scalar(double x);
+size_t dtype_size(int32_t dtype);
+
+}  // namespace lce

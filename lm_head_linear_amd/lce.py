@@ -1,0 +1,251 @@
+"""Thin Python binding of liblce.so (include/lce.h).
+
+Argument marshalling only: every step of the computation runs in the HIP
+kernels of liblce.so.  Functions carry the C names; tensors are torch
+tensors (device tensors for the device entry points), the stream is torch's
+current stream on the tensors' device.  If the library has not been built the
+first call raises: there is no fallback path.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+from typing import Optional
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "liblce.so")
+
+OK = 580
+BF16, F32, F64, I64, U8 = 1, 2, 3, 4, 6
+STATUS = {580: "ok", 581: "empty_dimension", 582: "length_mismatch", 583: "dimension_too_large",
+          584: "work_budget_exceeded", 585: "non_finite_scalar", 586: "target_id_out_of_range",
+          587: "chunk_exceeds_logit_budget", 588: "unknown_objective", 589: "device_error",
+          590: "dtype_mismatch"}
+_DT = {torch.bfloat16: BF16, torch.float32: F32, torch.float64: F64, torch.int64: I64,
+       torch.uint8: U8, torch.bool: U8}
+
+
+class LceError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        super().__init__(f"{where}: status {status} ({STATUS.get(status, 'unknown_status')})")
+        self.status = status
+
+
+class Tensor(ctypes.Structure):
+    _fields_ = [("data", ctypes.c_void_p), ("numel", ctypes.c_int64), ("dtype", ctypes.c_int32)]
+
+
+class Peak(ctypes.Structure):
+    _fields_ = [("chunked_cells", ctypes.c_double), ("materialized_cells", ctypes.c_double),
+                ("ratio", ctypes.c_double), ("n_chunks", ctypes.c_int64),
+                ("status", ctypes.c_int32)]
+
+
+class Loss(ctypes.Structure):
+    _fields_ = [("loss_sum", ctypes.c_double), ("loss_mean", ctypes.c_double),
+                ("z_sum", ctypes.c_double), ("z_mean", ctypes.c_double),
+                ("n_counted", ctypes.c_int64)]
+
+    def as_dict(self) -> dict:
+        return {k: getattr(self, k) for k, _ in self._fields_}
+
+
+_lib = None
+
+
+def lib():
+    """The loaded liblce.so (raises if it is missing)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is not built; run __graft_entry__.build() first")
+        L = ctypes.CDLL(LIB_PATH)
+        i64, i32, dbl, vp = ctypes.c_int64, ctypes.c_int32, ctypes.c_double, ctypes.c_void_p
+        PT = ctypes.POINTER(Tensor)
+        L.lce_status_name.restype = ctypes.c_char_p
+        L.lce_status_name.argtypes = [i32]
+        L.lce_dims_check.restype = i32
+        L.lce_dims_check.argtypes = [i64, i64, i64]
+        L.lce_chunk_check.restype = i32
+        L.lce_chunk_check.argtypes = [i64, i64]
+        L.lce_logit_cells.restype = dbl
+        L.lce_logit_cells.argtypes = [i64, i64]
+        L.lce_work_fits.restype = i32
+        L.lce_work_fits.argtypes = [i64, i64, i64, i64]
+        L.lce_peak_cells.restype = i32
+        L.lce_peak_cells.argtypes = [i64, i64, i64, ctypes.POINTER(Peak)]
+        L.lce_workspace_bytes.restype = i64
+        L.lce_workspace_bytes.argtypes = [i64, i64, i64, i64, i32]
+        L.lce_distill_workspace_bytes.restype = i64
+        L.lce_distill_workspace_bytes.argtypes = [i64, i64]
+        L.lce_forward.restype = i32
+        L.lce_forward.argtypes = [PT, PT, PT, PT, i64, i64, i64, i64, dbl, PT, PT,
+                                  ctypes.POINTER(Loss), vp]
+        L.lce_backward.restype = i32
+        L.lce_backward.argtypes = [PT, PT, PT, PT, PT, i64, i64, i64, i64, dbl, dbl, PT, PT, i32,
+                                   PT, vp]
+        L.lce_distill_fwd_bwd.restype = i32
+        L.lce_distill_fwd_bwd.argtypes = [PT, PT, PT, i64, i64, i32, dbl, dbl, dbl, PT, PT,
+                                          ctypes.POINTER(Loss), vp]
+        _lib = L
+    return _lib
+
+
+def _t(x: Optional[torch.Tensor]) -> Tensor:
+    """Flat descriptor of a contiguous tensor (NULL descriptor for None)."""
+    if x is None:
+        return Tensor(None, 0, 0)
+    if not x.is_contiguous():
+        raise ValueError("tensors must be contiguous")
+    return Tensor(x.data_ptr(), x.numel(), _DT.get(x.dtype, 0))
+
+
+def _stream(dev: torch.device) -> int:
+    return torch.cuda.current_stream(dev).cuda_stream
+
+
+# ------------------------------------------------------------- host contract
+
+def lce_status_name(code: int) -> str:
+    return lib().lce_status_name(int(code)).decode()
+
+
+def lce_dims_check(n_tok: int, d_model: int, vocab: int) -> int:
+    return lib().lce_dims_check(n_tok, d_model, vocab)
+
+
+def lce_chunk_check(chunk: int, vocab: int) -> int:
+    return lib().lce_chunk_check(chunk, vocab)
+
+
+def lce_logit_cells(chunk: int, vocab: int) -> float:
+    return lib().lce_logit_cells(chunk, vocab)
+
+
+def lce_work_fits(n: int, d: int, v: int, ceiling: int) -> bool:
+    return bool(lib().lce_work_fits(n, d, v, ceiling))
+
+
+def lce_peak_cells(n_tok: int, vocab: int, chunk: int) -> dict:
+    p = Peak()
+    lib().lce_peak_cells(n_tok, vocab, chunk, ctypes.byref(p))
+    return {"chunked_cells": p.chunked_cells, "materialized_cells": p.materialized_cells,
+            "ratio": p.ratio, "n_chunks": p.n_chunks, "status": p.status}
+
+
+def lce_workspace_bytes(n_tok: int, d_model: int, vocab: int, chunk: int, dtype) -> int:
+    dt = _DT[dtype] if isinstance(dtype, torch.dtype) else int(dtype)
+    return lib().lce_workspace_bytes(n_tok, d_model, vocab, chunk, dt)
+
+
+def lce_distill_workspace_bytes(n_tok: int, vocab: int) -> int:
+    return lib().lce_distill_workspace_bytes(n_tok, vocab)
+
+
+# ------------------------------------------------------------ device calls
+
+def lce_forward(hidden, weight, targets, loss_mask, n_tok, d_model, vocab, chunk, z_coef,
+                lse_out, workspace, stream: Optional[int] = None):
+    """Direct call of the C entry point.  Returns (status, Loss)."""
+    out = Loss()
+    args = [_t(hidden), _t(weight), _t(targets), _t(loss_mask)]
+    lse_t, ws_t = _t(lse_out), _t(workspace)
+    st = lib().lce_forward(*[ctypes.byref(a) for a in args], n_tok, d_model, vocab, chunk,
+                           float(z_coef), ctypes.byref(lse_t), ctypes.byref(ws_t),
+                           ctypes.byref(out), stream if stream is not None else
+                           _stream(hidden.device))
+    return st, out
+
+
+def lce_backward(hidden, weight, targets, loss_mask, lse, n_tok, d_model, vocab, chunk, z_coef,
+                 grad_out, d_hidden, d_weight, accumulate_d_weight, workspace,
+                 stream: Optional[int] = None) -> int:
+    """Direct call of the C entry point.  Returns the status."""
+    ts = [_t(hidden), _t(weight), _t(targets), _t(loss_mask), _t(lse)]
+    dh, dw, ws = _t(d_hidden), _t(d_weight), _t(workspace)
+    return lib().lce_backward(*[ctypes.byref(a) for a in ts], n_tok, d_model, vocab, chunk,
+                              float(z_coef), float(grad_out), ctypes.byref(dh), ctypes.byref(dw),
+                              int(bool(accumulate_d_weight)), ctypes.byref(ws),
+                              stream if stream is not None else _stream(hidden.device))
+
+
+def lce_distill_fwd_bwd(student, teacher, loss_mask, n_tok, vocab, objective, temperature,
+                        z_coef, grad_out, grad_logits, workspace, stream: Optional[int] = None):
+    """Direct call of the C entry point.  Returns (status, Loss)."""
+    out = Loss()
+    ts = [_t(student), _t(teacher), _t(loss_mask)]
+    g, ws = _t(grad_logits), _t(workspace)
+    st = lib().lce_distill_fwd_bwd(*[ctypes.byref(a) for a in ts], n_tok, vocab, int(objective),
+                                   float(temperature), float(z_coef), float(grad_out),
+                                   ctypes.byref(g), ctypes.byref(ws), ctypes.byref(out),
+                                   stream if stream is not None else _stream(student.device))
+    return st, out
+
+
+# ------------------------------------------------- allocating conveniences
+
+def _acc_dtype(dt: torch.dtype) -> torch.dtype:
+    return torch.float64 if dt == torch.float64 else torch.float32
+
+
+def workspace_for(n_tok, d_model, vocab, chunk, dtype, device) -> torch.Tensor:
+    nbytes = lce_workspace_bytes(n_tok, d_model, vocab, chunk, dtype)
+    if nbytes < 0:
+        raise LceError(int(-nbytes), "lce_workspace_bytes")
+    return torch.empty(nbytes, dtype=torch.uint8, device=device)
+
+
+@dataclass
+class ForwardResult:
+    loss: dict
+    lse: torch.Tensor
+
+
+def forward(hidden, weight, targets, loss_mask=None, chunk=256, z_coef=0.0, workspace=None):
+    """Allocate lse and (if needed) the workspace, call lce_forward, raise on refusal."""
+    n, D = hidden.shape
+    V = weight.shape[0]
+    lse = torch.empty(n, dtype=_acc_dtype(hidden.dtype), device=hidden.device)
+    ws = workspace if workspace is not None else workspace_for(n, D, V, chunk, hidden.dtype,
+                                                               hidden.device)
+    st, out = lce_forward(hidden, weight, targets, loss_mask, n, D, V, chunk, z_coef, lse, ws)
+    if st != OK:
+        raise LceError(st, "lce_forward")
+    return ForwardResult(out.as_dict(), lse)
+
+
+def backward(hidden, weight, targets, lse, loss_mask=None, chunk=256, z_coef=0.0, grad_out=1.0,
+             d_weight=None, accumulate=False, workspace=None):
+    """Allocate d_hidden (and d_weight unless given), call lce_backward."""
+    n, D = hidden.shape
+    V = weight.shape[0]
+    dh = torch.empty_like(hidden)
+    dw = d_weight if d_weight is not None else torch.empty(
+        V, D, dtype=_acc_dtype(hidden.dtype), device=hidden.device)
+    ws = workspace if workspace is not None else workspace_for(n, D, V, chunk, hidden.dtype,
+                                                               hidden.device)
+    st = lce_backward(hidden, weight, targets, loss_mask, lse, n, D, V, chunk, z_coef, grad_out,
+                      dh, dw, accumulate, ws)
+    if st != OK:
+        raise LceError(st, "lce_backward")
+    return dh, dw
+
+
+def distill(student, teacher, loss_mask=None, objective=0, temperature=1.0, z_coef=0.0,
+            grad_out=1.0, workspace=None):
+    """Allocate grad_logits and the workspace, call lce_distill_fwd_bwd."""
+    n, V = student.shape
+    g = torch.empty_like(student)
+    nbytes = lce_distill_workspace_bytes(n, V)
+    if nbytes < 0:
+        raise LceError(int(-nbytes), "lce_distill_workspace_bytes")
+    ws = workspace if workspace is not None else torch.empty(nbytes, dtype=torch.uint8,
+                                                             device=student.device)
+    st, out = lce_distill_fwd_bwd(student, teacher, loss_mask, n, V, objective, temperature,
+                                  z_coef, grad_out, g, ws)
+    if st != OK:
+        raise LceError(st, "lce_distill_fwd_bwd")
+    return out.as_dict(), g

@@ -1,0 +1,83 @@
+"""Host-side contract of liblce.so (no GPU): the library loads, exports every
+function include/lce.h declares, and its integer contract equals the
+independent oracle's bit for bit."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import oracle
+from lm_head_linear_amd import lce
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared():
+    text = open(os.path.join(ROOT, "include", "lce.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(lce_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_symbol():
+    names = _declared()
+    assert {"lce_dims_check", "lce_chunk_check", "lce_peak_cells", "lce_forward",
+            "lce_backward", "lce_distill_fwd_bwd"} <= set(names)
+    L = ctypes.CDLL(lce.LIB_PATH)
+    for n in names:
+        assert hasattr(L, n), n
+
+
+def test_printed_values_through_the_library():
+    r = lce.lce_peak_cells(2048, 151936, 256)
+    assert r == {"chunked_cells": 38895616.0, "materialized_cells": 311164928.0, "ratio": 8.0,
+                 "n_chunks": 8, "status": 580}
+    assert lce.lce_dims_check(2048, 4096, 151936) == 580
+    assert lce.lce_chunk_check(2048, 151936) == 587
+    assert lce.lce_chunk_check(256, 151936) == 580
+    assert lce.lce_chunk_check(1024, 151936) == 587   # the swept chunk 1024 is refused
+
+
+def test_contract_matches_oracle_on_a_sweep():
+    rng = np.random.default_rng(3)
+    vals = [0, 1, 2, 3, 7, 255, 256, 883, 884, 1024, 2 ** 10, 2 ** 16, 2 ** 16 + 1, 2 ** 17,
+            2 ** 24, 2 ** 24 + 1, 2 ** 27, 2 ** 27 + 1, 2 ** 40, -1, -(2 ** 40)]
+    vals += [int(x) for x in rng.integers(1, 2 ** 31, 40)]
+    for a in vals:
+        for b in vals:
+            assert lce.lce_chunk_check(a, b) == oracle.chunk_check(a, b), (a, b)
+            assert lce.lce_logit_cells(a, b) == oracle.logit_cells(a, b), (a, b)
+    trip = [(int(a), int(b), int(c)) for a, b, c in rng.choice(vals, size=(2000, 3))]
+    trip += [(2 ** 24, 2 ** 16, 64), (2 ** 24, 2 ** 16, 65), (2048, 1024, 151936)]
+    for n, d, v in trip:
+        assert lce.lce_dims_check(n, d, v) == oracle.dims_check(n, d, v), (n, d, v)
+        assert lce.lce_work_fits(n, d, v, 2 ** 46) == oracle.work_fits(n, d, v, 2 ** 46)
+        assert lce.lce_peak_cells(n, v, d) == oracle.peak_cells(n, v, d), (n, v, d)
+
+
+def test_status_names_match_oracle():
+    for code in list(range(570, 600)) + [-1, 0, 600, 2 ** 31 - 1]:
+        assert lce.lce_status_name(code) == oracle.status_name(code), code
+
+
+def test_workspace_sizes():
+    for dt in (lce.BF16, lce.F64):
+        b = lce.lce_workspace_bytes(2048, 1024, 151936, 256, dt)
+        assert b > 0
+        # the logit-gradient slab never exceeds chunk*vocab cells
+        assert b < 256 * 151936 * (2 if dt == lce.BF16 else 8) + 2048 * 1024 * 16 * 8 + 2 ** 24
+    assert lce.lce_workspace_bytes(2048, 1024, 151936, 1024, lce.BF16) == -587
+    assert lce.lce_workspace_bytes(0, 1024, 151936, 256, lce.BF16) == -581
+    assert lce.lce_workspace_bytes(64, 64, 1000, 16, lce.F32) == -590
+    assert lce.lce_distill_workspace_bytes(4096, 151936) > 0
+    assert lce.lce_distill_workspace_bytes(0, 5) == -581
+
+
+@pytest.mark.parametrize("n,D,V,chunk", [(64, 64, 1000, 16), (2048, 1024, 151936, 256),
+                                         (8192, 4096, 128256, 512), (7, 3, 5, 1),
+                                         (2048, 1024, 151936, 1), (100000, 64, 5000, 3)])
+def test_workspace_monotone_and_bounded(n, D, V, chunk):
+    for dt in (lce.BF16, lce.F64):
+        b = lce.lce_workspace_bytes(n, D, V, chunk, dt)
+        assert b > 0

@@ -1,0 +1,260 @@
+"""GPU parity of the fused linear cross-entropy path (lce_forward / lce_backward)
+against the CPU fp64 oracle, through the C ABI.
+
+Tolerances: fp64 path, loss relative error <= 1e-10 and every gradient tensor
+max|diff| <= 1e-10 * max|ref|; bf16-input / fp32-accumulate path, mean loss
+relative error <= 2e-3 and gradients max|diff| <= 1e-2 * max|ref|.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from lm_head_linear_amd import lce
+from tests import synthetic as syn
+
+pytestmark = pytest.mark.gpu
+
+TOL = {"f64": (1e-10, 1e-10), "bf16": (2e-3, 1e-2)}
+
+
+def _dev():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    return torch.device("cuda:0")
+
+
+def _say(*a):
+    print(*a, flush=True)
+
+
+def normwise(a, ref):
+    return float(np.max(np.abs(a - ref)) / max(float(np.max(np.abs(ref))), 1e-300))
+
+
+class Case:
+    """Inputs on the device plus their fp64 copies for the oracle."""
+
+    def __init__(self, w, n=None, D=None, V=None, seed=None, mask_frac=None, z=None):
+        self.w = w
+        x = syn.ce_inputs(w, n_tok=n, d_model=D, vocab=V, seed=seed)
+        if mask_frac is not None:
+            rng = np.random.default_rng(1234 + (seed or 0))
+            x.mask = syn.exact_mask(rng, x.hidden.shape[0], mask_frac)
+        self.x = x
+        self.n, self.D = x.hidden.shape
+        self.V = x.weight.shape[0]
+        self.z = w.z_coef if z is None else z
+        dev = _dev()
+        self.H = x.hidden.to(dev)
+        self.W = x.weight.to(dev)
+        self.y = torch.from_numpy(x.targets).to(dev)
+        self.m = torch.from_numpy(x.mask).to(dev) if x.mask is not None else None
+        self.H64, self.W64 = x.hidden64(), x.weight64()
+
+    def gpu_forward(self, chunk):
+        return lce.forward(self.H, self.W, self.y, self.m, chunk=chunk, z_coef=self.z)
+
+    def gpu_backward(self, lse, chunk, grad_out=1.0, d_weight=None, accumulate=False):
+        return lce.backward(self.H, self.W, self.y, lse, self.m, chunk=chunk, z_coef=self.z,
+                            grad_out=grad_out, d_weight=d_weight, accumulate=accumulate)
+
+    def oracle_forward(self, chunk):
+        return oracle.fused_forward(self.H64, self.W64, self.x.targets, mask=self.x.mask,
+                                    chunk=chunk, z_coef=self.z)
+
+
+def check_forward(c, fwd, ref):
+    loss_tol, _ = TOL[c.w.dtype]
+    assert fwd.loss["n_counted"] == ref["n_counted"]
+    e = abs(fwd.loss["loss_mean"] - ref["loss_mean"]) / abs(ref["loss_mean"])
+    ez = abs(fwd.loss["z_mean"] - ref["z_mean"]) / abs(ref["z_mean"])
+    el = normwise(fwd.lse.double().cpu().numpy(), ref["lse"])
+    _say(f"  loss {fwd.loss['loss_mean']:.12g} vs {ref['loss_mean']:.12g} rel {e:.2e}; "
+         f"z rel {ez:.2e}; lse {el:.2e}")
+    assert e <= loss_tol and ez <= loss_tol and el <= loss_tol
+
+
+def check_grads(c, dH, dW, rdH, rdW, rows_h=None, rows_w=None):
+    _, gtol = TOL[c.w.dtype]
+    gh = dH.double().cpu().numpy()
+    gw = dW.double().cpu().numpy()
+    if rows_h is not None:
+        gh = gh[rows_h]
+    if rows_w is not None:
+        gw = gw[rows_w]
+    eh, ew = normwise(gh, rdH), normwise(gw, rdW)
+    _say(f"  dH {eh:.2e} dW {ew:.2e} (max|dH| {np.max(np.abs(rdH)):.3e}, "
+         f"max|dW| {np.max(np.abs(rdW)):.3e})")
+    assert eh <= gtol and ew <= gtol
+
+
+# ------------------------------------------------------------ small, full --
+
+SMALL = [
+    # workload, n, D, V, chunk, mask, z : multiple tiles and ragged tails
+    ("f64", 64, 64, 1000, 16, None, 0.0),
+    ("f64", 64, 64, 1000, 16, 0.25, 1e-4),
+    ("f64", 200, 70, 1300, 33, 0.1, 1e-3),
+    ("f64", 130, 37, 301, 7, None, 1e-2),        # odd d_model: element-wise loads
+    ("bf16", 300, 192, 3000, 64, 0.05, 1e-4),
+    ("bf16", 517, 256, 2100, 100, None, 1e-3),
+    ("bf16", 96, 100, 777, 16, 0.2, 0.0),         # d_model % 8 != 0: element-wise loads
+    ("bf16", 1, 64, 33, 1, None, 0.0),            # single token, tiny vocab
+]
+
+
+@pytest.mark.parametrize("dt,n,D,V,chunk,mask,z", SMALL)
+def test_small_forward_backward(dt, n, D, V, chunk, mask, z):
+    w = syn.TINY_F64 if dt == "f64" else syn.QWEN_BF16
+    _say(f"case {dt} n={n} D={D} V={V} chunk={chunk} mask={mask} z={z}")
+    c = Case(w, n, D, V, seed=n + D, mask_frac=mask, z=z)
+    fwd = c.gpu_forward(chunk)
+    ref = c.oracle_forward(chunk)
+    check_forward(c, fwd, ref)
+    dH, dW = c.gpu_backward(fwd.lse, chunk, grad_out=1.5)
+    rdH, rdW = oracle.backward(c.H64, c.W64, c.x.targets, ref["lse"], mask=c.x.mask,
+                               z_coef=c.z, grad_out=1.5)
+    check_grads(c, dH, dW, rdH, rdW)
+    if c.m is not None:
+        assert not dH[c.m == 0].any()
+
+
+def test_tiny_workload_chunk_invariance_and_accumulate():
+    c = Case(syn.TINY_F64)
+    base = c.gpu_forward(1)
+    for chunk in (2, 5, 16, 63, 64, 1000):
+        f = c.gpu_forward(chunk)
+        assert f.loss["loss_mean"] == base.loss["loss_mean"], chunk   # bit for bit
+        assert torch.equal(f.lse, base.lse)
+    ref = c.oracle_forward(16)
+    check_forward(c, base, ref)
+    dw0 = torch.randn(c.V, c.D, dtype=torch.float64, device=c.H.device)
+    dH, dW = c.gpu_backward(base.lse, 16, d_weight=dw0.clone(), accumulate=True)
+    rdH, rdW = oracle.backward(c.H64, c.W64, c.x.targets, ref["lse"], mask=None, z_coef=c.z,
+                               dw_in=dw0.cpu().numpy())
+    check_grads(c, dH, dW, rdH, rdW)
+    # sum over the vocabulary of d_weight cancels (z = 0)
+    _, dW1 = c.gpu_backward(base.lse, 16)
+    assert float(dW1.sum(0).abs().max()) <= 1e-9
+
+
+def test_bf16_chunk_invariance_bitwise():
+    c = Case(syn.QWEN_BF16, 300, 128, 2000, seed=5, mask_frac=0.05)
+    a = c.gpu_forward(1)
+    for chunk in (3, 64, 256, 300):
+        b = c.gpu_forward(chunk)
+        assert b.loss["loss_mean"] == a.loss["loss_mean"] and torch.equal(a.lse, b.lse), chunk
+    # backward: d_hidden must not depend on the slab schedule beyond rounding
+    dh1, dw1 = c.gpu_backward(a.lse, 1)
+    dh2, dw2 = c.gpu_backward(a.lse, 300)
+    assert normwise(dh1.double().cpu().numpy(), dh2.double().cpu().numpy()) <= 1e-2
+    assert torch.equal(dw1, dw2)     # each d_weight row is one K-pass over all tokens
+
+
+def test_all_masked_gives_zeros():
+    c = Case(syn.QWEN_BF16, 100, 64, 500, seed=2)
+    c.m = torch.zeros(c.n, dtype=torch.uint8, device=c.H.device)
+    f = c.gpu_forward(50)
+    assert f.loss["n_counted"] == 0 and f.loss["loss_mean"] == 0.0 and f.loss["z_mean"] == 0.0
+    dH, dW = c.gpu_backward(f.lse, 50)
+    assert not dH.any() and not dW.any()
+
+
+# ------------------------------------------------------------ refusals --
+
+def test_refusals_leave_outputs_untouched():
+    c = Case(syn.QWEN_BF16, 64, 64, 500, seed=3)
+    dev = c.H.device
+    lse = torch.full((c.n,), 7.0, dtype=torch.float32, device=dev)
+    ws = lce.workspace_for(c.n, c.D, c.V, 16, torch.bfloat16, dev)
+
+    def fwd(**kw):
+        a = dict(hidden=c.H, weight=c.W, targets=c.y, loss_mask=None, n_tok=c.n, d_model=c.D,
+                 vocab=c.V, chunk=16, z_coef=0.0, lse_out=lse, workspace=ws)
+        a.update(kw)
+        return lce.lce_forward(**a)[0]
+
+    assert fwd(n_tok=0) == 581
+    assert fwd(d_model=2 ** 16 + 1) == 583
+    assert fwd(chunk=2 ** 27) == 587
+    assert fwd(z_coef=float("nan")) == 585
+    assert fwd(lse_out=lse.double()) == 590
+    assert fwd(weight=c.W.float()) == 590
+    assert fwd(workspace=ws[:100]) == 582
+    assert fwd(hidden=c.H[:10]) == 582
+    bad = c.y.clone()
+    bad[17] = c.V
+    assert fwd(targets=bad) == 586
+    bad[17] = -1
+    assert fwd(targets=bad) == 586
+    torch.cuda.synchronize()
+    assert torch.all(lse == 7.0)        # no refused call wrote its output
+    dh = torch.full_like(c.H, 3.0)
+    dw = torch.full((c.V, c.D), 5.0, dtype=torch.float32, device=dev)
+    st = lce.lce_backward(c.H, c.W, bad, None, lse, c.n, c.D, c.V, 16, 0.0, 1.0, dh, dw, 0, ws)
+    assert st == 586
+    st = lce.lce_backward(c.H, c.W, c.y, None, lse, c.n, c.D, c.V, 16, 0.0, float("inf"), dh,
+                          dw, 0, ws)
+    assert st == 585
+    torch.cuda.synchronize()
+    assert torch.all(dh == 3.0) and torch.all(dw == 5.0)
+
+
+# ------------------------------------------------------------ full size --
+
+def _sample(rng, hi, k):
+    return np.unique(np.concatenate([[0, hi - 1], rng.choice(hi, size=k, replace=False)]))
+
+
+def test_qwen_head_bf16_full_size():
+    """2048 x 1024 x 151936 bf16, chunk 256, z 1e-4, 5% masked: the headline workload."""
+    w = syn.QWEN_BF16
+    _say(f"case {w.name}: generating inputs")
+    c = Case(w)
+    fwd = c.gpu_forward(w.chunk)
+    dH, dW = c.gpu_backward(fwd.lse, w.chunk)
+    torch.cuda.synchronize()
+    _say("  oracle forward (all tokens)")
+    ref = c.oracle_forward(w.chunk)
+    check_forward(c, fwd, ref)
+    rng = np.random.default_rng(99)
+    th = _sample(rng, c.n, 6)
+    vw = _sample(rng, c.V, 6)
+    vw = np.unique(np.concatenate([vw, c.x.targets[th]]))
+    _say(f"  oracle d_hidden rows {th.tolist()} and d_weight rows {vw.tolist()}")
+    rdH = oracle.backward_dh_rows(c.H64, c.W64, c.x.targets, ref["lse"], th, mask=c.x.mask,
+                                  z_coef=c.z)
+    rdW = oracle.backward_dw_rows(c.H64, c.W64, c.x.targets, ref["lse"], vw, mask=c.x.mask,
+                                  z_coef=c.z)
+    check_grads(c, dH, dW, rdH, rdW, rows_h=th, rows_w=vw)
+
+
+def test_qwen_head_f64_full_size():
+    """2048 x 1024 x 151936 fp64: loss and sampled gradients; chunk 1024 is refused."""
+    w = syn.QWEN_F64
+    _say(f"case {w.name}: generating inputs")
+    c = Case(w)
+    f128 = c.gpu_forward(128)
+    f512 = c.gpu_forward(512)
+    assert f128.loss["loss_mean"] == f512.loss["loss_mean"]
+    with pytest.raises(lce.LceError) as e:
+        c.gpu_forward(1024)
+    assert e.value.status == 587
+    fwd = c.gpu_forward(256)
+    assert fwd.loss["loss_mean"] == f128.loss["loss_mean"]
+    dH, dW = c.gpu_backward(fwd.lse, 256)
+    torch.cuda.synchronize()
+    _say("  oracle forward (all tokens)")
+    ref = c.oracle_forward(256)
+    check_forward(c, fwd, ref)
+    rng = np.random.default_rng(98)
+    th = _sample(rng, c.n, 4)
+    vw = np.unique(np.concatenate([_sample(rng, c.V, 4), c.x.targets[th]]))
+    rdH = oracle.backward_dh_rows(c.H64, c.W64, c.x.targets, ref["lse"], th, mask=c.x.mask,
+                                  z_coef=c.z)
+    rdW = oracle.backward_dw_rows(c.H64, c.W64, c.x.targets, ref["lse"], vw, mask=c.x.mask,
+                                  z_coef=c.z)
+    check_grads(c, dH, dW, rdH, rdW, rows_h=th, rows_w=vw)

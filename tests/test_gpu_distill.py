@@ -1,0 +1,107 @@
+"""GPU parity of lce_distill_fwd_bwd (distillation + z-loss) against the CPU
+fp64 oracle, through the C ABI.  bf16/fp32: loss relative error <= 2e-3,
+gradient max|diff| <= 1e-2 * max|ref|; fp64: 1e-10 for both."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from lm_head_linear_amd import lce
+from tests import synthetic as syn
+
+pytestmark = pytest.mark.gpu
+TOL = {"bf16": (2e-3, 1e-2), "f32": (2e-3, 1e-2), "f64": (1e-10, 1e-10)}
+
+
+def _dev():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    return torch.device("cuda:0")
+
+
+def normwise(a, ref):
+    return float(np.max(np.abs(a - ref)) / max(float(np.max(np.abs(ref))), 1e-300))
+
+
+@pytest.mark.parametrize("dt", ["bf16", "f32", "f64"])
+@pytest.mark.parametrize("obj", [0, 1, 2])
+@pytest.mark.parametrize("n,V", [(37, 1000), (20, 1003)])
+def test_small_distill(dt, obj, n, V):
+    print(f"case distill {dt} obj={obj} n={n} V={V}", flush=True)
+    dev = _dev()
+    d = syn.distill_inputs(syn.DISTILL_BF16, n_tok=n, vocab=V, seed=n + obj, dtype=dt)
+    S, U = d.student.to(dev), d.teacher.to(dev)
+    m = torch.from_numpy(d.mask).to(dev)
+    out, g = lce.distill(S, U, m, objective=obj, temperature=2.0, z_coef=1e-3, grad_out=1.3)
+    r = oracle.distill(d.student.double().numpy(), d.teacher.double().numpy(), mask=d.mask,
+                       objective=obj, temperature=2.0, z_coef=1e-3, grad_out=1.3)
+    lt, gt = TOL[dt]
+    assert out["n_counted"] == r["n_counted"]
+    el = abs(out["loss_mean"] - r["loss"]) / abs(r["loss"])
+    ez = abs(out["z_mean"] - r["z_loss"]) / abs(r["z_loss"])
+    eg = normwise(g.double().cpu().numpy(), r["grad"])
+    print(f"  loss rel {el:.2e} z rel {ez:.2e} grad {eg:.2e}", flush=True)
+    assert el <= lt and ez <= lt and eg <= gt
+    assert not g[m == 0].any()
+
+
+@pytest.mark.parametrize("obj", [1, 2])
+def test_kl_zero_for_identical_logits(obj):
+    dev = _dev()
+    d = syn.distill_inputs(syn.DISTILL_BF16, n_tok=16, vocab=512, seed=3)
+    S = d.student.to(dev)
+    out, g = lce.distill(S, S.clone(), None, objective=obj, temperature=2.0)
+    assert abs(out["loss_mean"]) <= 1e-6
+    assert float(g.float().abs().max()) <= 1e-6
+
+
+def test_distill_refusals():
+    dev = _dev()
+    d = syn.distill_inputs(syn.DISTILL_BF16, n_tok=8, vocab=64, seed=4)
+    S, U = d.student.to(dev), d.teacher.to(dev)
+    g = torch.full_like(S, 9.0)
+    ws = torch.empty(lce.lce_distill_workspace_bytes(8, 64), dtype=torch.uint8, device=dev)
+    call = lambda **kw: lce.lce_distill_fwd_bwd(**{**dict(
+        student=S, teacher=U, loss_mask=None, n_tok=8, vocab=64, objective=0, temperature=1.0,
+        z_coef=0.0, grad_out=1.0, grad_logits=g, workspace=ws), **kw})[0]
+    assert call(objective=3) == 588
+    assert call(temperature=0.0) == 585
+    assert call(temperature=float("nan")) == 585
+    assert call(teacher=U.float()) == 590
+    assert call(grad_logits=g[:4]) == 582
+    assert call(n_tok=0) == 581
+    torch.cuda.synchronize()
+    assert torch.all(g == 9.0)
+
+
+def test_distill_full_size_sampled_rows():
+    """4096 x 151936 bf16, T = 2, 10% masked, z 1e-4: every objective."""
+    w = syn.DISTILL_BF16
+    dev = _dev()
+    print(f"case {w.name}: generating inputs", flush=True)
+    d = syn.distill_inputs(w)
+    S, U = d.student.to(dev), d.teacher.to(dev)
+    m = torch.from_numpy(d.mask).to(dev)
+    C = int(d.mask.sum())
+    rng = np.random.default_rng(5)
+    rows = np.unique(np.concatenate([[0, w.n_tok - 1], rng.choice(w.n_tok, 10, replace=False),
+                                     np.flatnonzero(d.mask == 0)[:2]]))
+    S64, U64 = d.student.double().numpy(), d.teacher.double().numpy()
+    for obj in (0, 1, 2):
+        out, g = lce.distill(S, U, m, objective=obj, temperature=w.temperature, z_coef=w.z_coef)
+        torch.cuda.synchronize()
+        full = oracle.distill(S64, U64, mask=d.mask, objective=obj, temperature=w.temperature,
+                              z_coef=w.z_coef, want_grad=False)
+        el = abs(out["loss_mean"] - full["loss"]) / abs(full["loss"])
+        ez = abs(out["z_mean"] - full["z_loss"]) / abs(full["z_loss"])
+        print(f"  objective {obj}: loss rel {el:.2e} z rel {ez:.2e}", flush=True)
+        assert el <= 2e-3 and ez <= 2e-3
+        gr, rl, rz = oracle.distill_rows(d.student[rows].double().numpy(),
+                                         d.teacher[rows].double().numpy(), C,
+                                         row_mask=d.mask[rows], objective=obj,
+                                         temperature=w.temperature, z_coef=w.z_coef)
+        eg = normwise(g[torch.from_numpy(rows).to(dev)].double().cpu().numpy(), gr)
+        assert out["n_counted"] == C
+        print(f"  objective {obj}: loss {out['loss_mean']:.6g} z {out['z_mean']:.6g} "
+              f"sampled grad {eg:.2e}", flush=True)
+        assert eg <= 1e-2
