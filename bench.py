@@ -1,0 +1,197 @@
+"""Benchmark: fused linear cross-entropy forward + backward on one MI355X.
+
+Default workload: the Qwen3-0.6B-shaped LM head, 2048 tokens x d_model 1024 x
+vocab 151936, bf16 inputs with fp32 accumulation, chunk 256, z-loss 1e-4, 5%
+of tokens masked, synthetic seeded inputs already resident in HBM.  One step
+= lce_forward + lce_backward as a caller makes them (target guard and status
+syncs included).  Prints one JSON line.
+
+Kernel durations for the roofline come from HIP events that the library
+records around every launch of each GEMM kind inside the timed region
+(lce_forward_timed / lce_backward_timed on torch's current stream).
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
+PEAK_F64_TFLOPS = 78.6         # MI355X fp64 MFMA
+PEAK_HBM_GBS = 8000.0
+
+GEMM_KINDS = ["fwd_gemm", "dlogit_gemm", "dw_gemm", "dh_gemm"]
+ALL_KINDS = ["guard", "fwd_gemm", "fwd_merge", "reduce", "dlogit_gemm", "dw_gemm", "dh_gemm",
+             "dh_final"]
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def cpu_baseline(w, x, tokens: int):
+    """The oracle, as it stands, on the first `tokens` tokens of the workload:
+    forward (all tokens of the prefix) + backward (d_hidden of the prefix and
+    every d_weight row)."""
+    import numpy as np
+    import oracle
+
+    H = x.hidden[:tokens].to(dtype=__import__("torch").float64).numpy()
+    W = x.weight64()
+    y = x.targets[:tokens]
+    m = x.mask[:tokens] if x.mask is not None else None
+    threads = oracle.default_threads()
+    t0 = time.perf_counter()
+    r = oracle.fused_forward(H, W, y, mask=m, chunk=w.chunk, z_coef=w.z_coef, nthreads=threads)
+    oracle.backward(H, W, y, r["lse"], mask=m, z_coef=w.z_coef, nthreads=threads)
+    dt = time.perf_counter() - t0
+    return {"value": tokens / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": f"first {tokens} tokens of the {w.n_tok}-token batch, full vocab "
+                      f"{w.vocab} and d_model {w.d_model}: fp64 forward + backward "
+                      f"(d_hidden of the sample, all d_weight rows), {dt:.2f} s",
+            "seconds": dt}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="qwen_bf16",
+                    choices=["qwen_bf16", "large_bf16", "qwen_f64"])
+    ap.add_argument("--cpu-tokens", type=int, default=256)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-kernel-events", action="store_true")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(run with --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    from lm_head_linear_amd import lce
+    from tests import synthetic as syn
+
+    w = {"qwen_bf16": syn.QWEN_BF16, "large_bf16": syn.LARGE_BF16,
+         "qwen_f64": syn.QWEN_F64}[args.workload]
+    dev = torch.device("cuda:0")
+    log(f"bench: workload {w.name}: generating inputs")
+    x = syn.ce_inputs(w)
+    n, D, V, chunk, z = w.n_tok, w.d_model, w.vocab, w.chunk, w.z_coef
+    H, W = x.hidden.to(dev), x.weight.to(dev)
+    y = torch.from_numpy(x.targets).to(dev)
+    m = torch.from_numpy(x.mask).to(dev) if x.mask is not None else None
+    acc_dt = torch.float64 if H.dtype == torch.float64 else torch.float32
+    lse = torch.empty(n, dtype=acc_dt, device=dev)
+    dH = torch.empty_like(H)
+    dW = torch.empty(V, D, dtype=acc_dt, device=dev)
+    ws_bytes = lce.lce_workspace_bytes(n, D, V, chunk, H.dtype)
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+    torch.cuda.synchronize()
+    mem0 = torch.cuda.memory_allocated()
+    torch.cuda.reset_peak_memory_stats()
+
+    def step(timer=None):
+        st, out = lce.lce_forward(H, W, y, m, n, D, V, chunk, z, lse, ws, timer=timer)
+        if st != lce.OK:
+            raise lce.LceError(st, "lce_forward")
+        st = lce.lce_backward(H, W, y, m, lse, n, D, V, chunk, z, 1.0, dH, dW, 0, ws,
+                              timer=timer)
+        if st != lce.OK:
+            raise lce.LceError(st, "lce_backward")
+        return out
+
+    log(f"bench: warmup {args.warmup} steps")
+    for _ in range(args.warmup):
+        out = step()
+    torch.cuda.synchronize()
+
+    timer = None
+    if not args.no_kernel_events:
+        timer = lce.KernelTimer(ALL_KINDS, capacity=args.steps * 32)
+    log(f"bench: timing {args.steps} steps")
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    e0.record()
+    for _ in range(args.steps):
+        out = step(timer)
+    e1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    gpu_ms = e0.elapsed_time(e1)
+    ms_per_step = 1e3 * wall / args.steps
+    peak_extra = torch.cuda.max_memory_allocated() - mem0
+    log(f"bench: {ms_per_step:.3f} ms/step wall, {gpu_ms / args.steps:.3f} ms/step events, "
+        f"loss {out.loss_mean:.6f}")
+
+    flop_gemm = 2.0 * n * D * V                  # one GEMM pass over every (token, vocab) pair
+    f8 = 4 * flop_gemm                            # forward + recompute + dH + dW
+    f6 = 3 * flop_gemm
+    tokens_per_s = n / (ms_per_step / 1e3)
+    peak = PEAK_F64_TFLOPS if w.dtype == "f64" else PEAK_BF16_TFLOPS
+
+    kernels = {}
+    roof = None
+    if timer is not None:
+        for k in ALL_KINDS:
+            d = timer.durations_ms(k)
+            if d:
+                kernels[k] = {"launches_per_step": len(d) / args.steps,
+                              "avg_ms": float(np.mean(d)), "ms_per_step": float(np.sum(d)) / args.steps}
+        dom = max((k for k in GEMM_KINDS if k in kernels), key=lambda k: kernels[k]["ms_per_step"])
+        kd = kernels[dom]
+        per_launch_flops = flop_gemm / kd["launches_per_step"]
+        achieved = per_launch_flops / (kd["avg_ms"] / 1e3) / 1e12
+        for k in GEMM_KINDS:
+            if k in kernels:
+                kernels[k]["tflops"] = flop_gemm / (kernels[k]["ms_per_step"] / 1e3) / 1e12
+        roof = {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak, "unit": "TFLOP/s",
+                "frac": round(achieved / peak, 4), "traffic": None, "kernel": dom,
+                "flops_per_launch": per_launch_flops, "avg_launch_ms": kd["avg_ms"]}
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        log(f"bench: CPU oracle baseline on {args.cpu_tokens} tokens")
+        cpu = cpu_baseline(w, x, args.cpu_tokens)
+        cpu.pop("seconds", None)
+
+    res = {
+        "metric": "fused linear-CE fwd+bwd tokens/s and % MFMA peak at 2048x1024x151936 bf16",
+        "value": round(tokens_per_s, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if w.dtype == "bf16" else "f64",
+        "data": "synthetic",
+        "config": {"workload": w.name, "n_tok": n, "d_model": D, "vocab": V, "chunk": chunk,
+                   "z_coef": z, "mask_frac": w.mask_frac, "targets": w.targets},
+        "tflops_8ndv": round(f8 / (ms_per_step / 1e3) / 1e12, 2),
+        "mfma_frac_8ndv": round(f8 / (ms_per_step / 1e3) / 1e12 / peak, 4),
+        "tflops_6ndv": round(f6 / (ms_per_step / 1e3) / 1e12, 2),
+        "mfma_frac_6ndv": round(f6 / (ms_per_step / 1e3) / 1e12 / peak, 4),
+        "gpu_ms_per_step_events": round(gpu_ms / args.steps, 4),
+        "workspace_bytes": ws_bytes,
+        "peak_extra_bytes": int(peak_extra),
+        "kernels": kernels,
+        "roofline": roof,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

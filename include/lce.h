@@ -200,6 +200,56 @@ int32_t lce_distill_fwd_bwd(const lce_tensor *student, const lce_tensor *teacher
                             double grad_out, lce_tensor *grad_logits, lce_tensor *workspace,
                             lce_loss *out, void *stream);
 
+/* ---- optional kernel timing (for benchmarks and profilers) ------------- */
+
+/* Kernel kinds a timed call can bracket with events. */
+#define LCE_K_GUARD 0        /* target guard and counted-token count            */
+#define LCE_K_FWD_GEMM 1     /* forward logit GEMM with the online-LSE epilogue */
+#define LCE_K_FWD_MERGE 2    /* per-token merge of (max, sum) pairs             */
+#define LCE_K_REDUCE 3       /* fixed-order token sums                          */
+#define LCE_K_DLOGIT_GEMM 4  /* backward logit recompute -> logit gradient      */
+#define LCE_K_DW_GEMM 5      /* d_weight rows of a slab                         */
+#define LCE_K_DH_GEMM 6      /* split-K d_hidden accumulation                   */
+#define LCE_K_DH_FINAL 7     /* fold of the d_hidden splits                     */
+#define LCE_K_DISTILL 8      /* distillation row kernel                         */
+#define LCE_NUM_KERNELS 9
+
+/* One slot per kernel kind.  start/stop hold `capacity` caller-created
+ * hipEvent_t handles (as void*); a timed call records start[i]/stop[i] on
+ * its stream around the i-th launch of that kind (i counted from `used`,
+ * which the call advances; launches beyond capacity are not recorded).
+ * Slots with capacity 0 are ignored.  The caller owns the events. */
+typedef struct lce_timer_slot {
+  void **start;
+  void **stop;
+  int32_t capacity;
+  int32_t used;
+} lce_timer_slot;
+
+typedef struct lce_timers {
+  lce_timer_slot slot[LCE_NUM_KERNELS];
+} lce_timers;
+
+/* Same as lce_forward / lce_backward / lce_distill_fwd_bwd, recording
+ * events into *timers (NULL = no timing, identical to the plain call). */
+int32_t lce_forward_timed(const lce_tensor *hidden, const lce_tensor *weight,
+                          const lce_tensor *targets, const lce_tensor *loss_mask, int64_t n_tok,
+                          int64_t d_model, int64_t vocab, int64_t chunk, double z_coef,
+                          lce_tensor *lse_out, lce_tensor *workspace, lce_loss *out,
+                          void *stream, lce_timers *timers);
+int32_t lce_backward_timed(const lce_tensor *hidden, const lce_tensor *weight,
+                           const lce_tensor *targets, const lce_tensor *loss_mask,
+                           const lce_tensor *lse, int64_t n_tok, int64_t d_model, int64_t vocab,
+                           int64_t chunk, double z_coef, double grad_out, lce_tensor *d_hidden,
+                           lce_tensor *d_weight, int32_t accumulate_d_weight,
+                           lce_tensor *workspace, void *stream, lce_timers *timers);
+int32_t lce_distill_fwd_bwd_timed(const lce_tensor *student, const lce_tensor *teacher,
+                                  const lce_tensor *loss_mask, int64_t n_tok, int64_t vocab,
+                                  int32_t objective, double temperature, double z_coef,
+                                  double grad_out, lce_tensor *grad_logits,
+                                  lce_tensor *workspace, lce_loss *out, void *stream,
+                                  lce_timers *timers);
+
 #ifdef __cplusplus
 }
 #endif

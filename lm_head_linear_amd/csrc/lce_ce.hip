@@ -395,6 +395,20 @@ __global__ void dh_final_kernel(const typename TR::Acc *P, int64_t splits, int64
 
 // ------------------------------------------------------------- host side --
 
+TimedLaunch::TimedLaunch(lce_timers *t, int kind, void *st) : slot(nullptr), stream(st), idx(-1) {
+  if (t && t->slot[kind].capacity > t->slot[kind].used) {
+    slot = &t->slot[kind];
+    idx = slot->used;
+    (void)hipEventRecord(static_cast<hipEvent_t>(slot->start[idx]), static_cast<hipStream_t>(st));
+  }
+}
+TimedLaunch::~TimedLaunch() {
+  if (slot) {
+    (void)hipEventRecord(static_cast<hipEvent_t>(slot->stop[idx]), static_cast<hipStream_t>(stream));
+    slot->used = idx + 1;
+  }
+}
+
 static int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
 static bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
@@ -416,7 +430,8 @@ static void launch_gemm(bool vec, const GemmParams &g, int64_t splits, const Epi
 }
 
 static void launch_guard(const int64_t *y, const uint8_t *mask, int64_t n, int64_t V,
-                         Control *ctl, hipStream_t st) {
+                         Control *ctl, hipStream_t st, lce_timers *tm) {
+  TimedLaunch tl(tm, LCE_K_GUARD, st);
   hipLaunchKernelGGL(ctl_init_kernel, dim3(1), dim3(64), 0, st, ctl);
   int64_t blocks = cdiv(n, 256);
   if (blocks > 1024) blocks = 1024;
@@ -426,14 +441,14 @@ static void launch_guard(const int64_t *y, const uint8_t *mask, int64_t n, int64
 template <class TR>
 static void forward_impl(const CEPlan &p, const void *H, const void *W, const int64_t *y,
                          const uint8_t *mask, typename TR::Acc *lse_out, uint8_t *ws, bool vec,
-                         hipStream_t st) {
+                         hipStream_t st, lce_timers *tm) {
   typedef typename TR::Acc Acc;
   Control *ctl = reinterpret_cast<Control *>(ws);
   Acc *partials = reinterpret_cast<Acc *>(ws + p.off_partials);
   Acc *zy = reinterpret_cast<Acc *>(ws + p.off_zy);
   double *loss_tok = reinterpret_cast<double *>(ws + p.off_losstok);
   const typename TR::E *Hp = static_cast<const typename TR::E *>(H);
-  launch_guard(y, mask, p.n, p.V, ctl, st);
+  launch_guard(y, mask, p.n, p.V, ctl, st, tm);
   for (int64_t tok0 = 0; tok0 < p.n; tok0 += p.tok_per_pass) {
     const int64_t ntok = p.tok_per_pass < p.n - tok0 ? p.tok_per_pass : p.n - tok0;
     GemmParams g;
@@ -445,11 +460,16 @@ static void forward_impl(const CEPlan &p, const void *H, const void *W, const in
     g.tiles_n = cdiv(ntok, TR::BN);
     g.bad = &ctl->bad;
     FwdLseEpi<TR> epi{y + tok0, ntok, p.V, p.n_vparts, partials, zy + tok0};
-    launch_gemm<TR, true, true>(vec, g, 1, epi, st);
+    {
+      TimedLaunch tl(tm, LCE_K_FWD_GEMM, st);
+      launch_gemm<TR, true, true>(vec, g, 1, epi, st);
+    }
+    TimedLaunch tl(tm, LCE_K_FWD_MERGE, st);
     hipLaunchKernelGGL(fwd_merge_kernel<Acc>, dim3(unsigned(cdiv(ntok, 4))), dim3(256), 0, st,
                        (const Acc *)partials, (const Acc *)(zy + tok0), p.n_vparts, ntok,
                        lse_out + tok0, loss_tok + tok0, (const int32_t *)&ctl->bad);
   }
+  TimedLaunch tl(tm, LCE_K_REDUCE, st);
   hipLaunchKernelGGL(fwd_final_kernel<Acc>, dim3(1), dim3(1024), 0, st, (const double *)loss_tok,
                      (const Acc *)lse_out, mask, p.n, ctl);
 }
@@ -458,7 +478,8 @@ template <class TR>
 static void backward_impl(const CEPlan &p, const void *H, const void *W, const int64_t *y,
                           const uint8_t *mask, const typename TR::Acc *lse, double z_coef,
                           double grad_out, typename TR::E *dH, typename TR::Acc *dW,
-                          int accumulate, uint8_t *ws, bool vec, hipStream_t st) {
+                          int accumulate, uint8_t *ws, bool vec, hipStream_t st,
+                          lce_timers *tm) {
   typedef typename TR::Acc Acc;
   typedef typename TR::E E;
   Control *ctl = reinterpret_cast<Control *>(ws);
@@ -466,7 +487,7 @@ static void backward_impl(const CEPlan &p, const void *H, const void *W, const i
   Acc *dhacc = reinterpret_cast<Acc *>(ws + p.off_dhacc);
   const E *Hp = static_cast<const E *>(H);
   const E *Wp = static_cast<const E *>(W);
-  launch_guard(y, mask, p.n, p.V, ctl, st);
+  launch_guard(y, mask, p.n, p.V, ctl, st, tm);
   for (int64_t s = 0; s < p.n_slabs; ++s) {
     const int64_t vs0 = s * p.slab;
     const int64_t rows = p.slab < p.V - vs0 ? p.slab : p.V - vs0;
@@ -481,6 +502,7 @@ static void backward_impl(const CEPlan &p, const void *H, const void *W, const i
       g.tiles_n = cdiv(p.n, TR::BN);
       g.bad = &ctl->bad;
       DlogitEpi<TR> epi{y, mask, lse, p.n, vs0, rows, ctl, grad_out, z_coef, dbuf, p.d_ld};
+      TimedLaunch tl(tm, LCE_K_DLOGIT_GEMM, st);
       launch_gemm<TR, true, true>(vec, g, 1, epi, st);
     }
     {  // d_weight rows of the slab = d^T H over all tokens
@@ -492,6 +514,7 @@ static void backward_impl(const CEPlan &p, const void *H, const void *W, const i
       g.k_per_split = cdiv(p.n, TR::BK) * TR::BK;
       g.tiles_n = cdiv(p.D, TR::BN);
       g.bad = &ctl->bad;
+      TimedLaunch tl(tm, LCE_K_DW_GEMM, st);
       if (accumulate)
         launch_gemm<TR, true, false>(vec, g, 1, StoreEpi<TR, true>{dW, p.D, vs0, rows, p.D, 0}, st);
       else
@@ -507,6 +530,7 @@ static void backward_impl(const CEPlan &p, const void *H, const void *W, const i
       g.k_per_split = kps;
       g.tiles_n = cdiv(p.D, TR::BN);
       g.bad = &ctl->bad;
+      TimedLaunch tl(tm, LCE_K_DH_GEMM, st);
       if (s > 0)
         launch_gemm<TR, false, false>(vec, g, p.dh_splits,
                                       StoreEpi<TR, true>{dhacc, p.D, 0, p.n, p.D, p.n * p.D}, st);
@@ -518,6 +542,7 @@ static void backward_impl(const CEPlan &p, const void *H, const void *W, const i
   int64_t count = p.n * p.D;
   int64_t blocks = cdiv(count, 256);
   if (blocks > 4096) blocks = 4096;
+  TimedLaunch tl(tm, LCE_K_DH_FINAL, st);
   hipLaunchKernelGGL(dh_final_kernel<TR>, dim3(unsigned(blocks)), dim3(256), 0, st,
                      (const Acc *)dhacc, p.dh_splits, count, dH, (const int32_t *)&ctl->bad);
 }
@@ -569,6 +594,15 @@ int32_t lce_forward(const lce_tensor *hidden, const lce_tensor *weight,
                     const lce_tensor *targets, const lce_tensor *loss_mask, int64_t n_tok,
                     int64_t d_model, int64_t vocab, int64_t chunk, double z_coef,
                     lce_tensor *lse_out, lce_tensor *workspace, lce_loss *out, void *stream) {
+  return lce_forward_timed(hidden, weight, targets, loss_mask, n_tok, d_model, vocab, chunk,
+                           z_coef, lse_out, workspace, out, stream, nullptr);
+}
+
+int32_t lce_forward_timed(const lce_tensor *hidden, const lce_tensor *weight,
+                          const lce_tensor *targets, const lce_tensor *loss_mask, int64_t n_tok,
+                          int64_t d_model, int64_t vocab, int64_t chunk, double z_coef,
+                          lce_tensor *lse_out, lce_tensor *workspace, lce_loss *out,
+                          void *stream, lce_timers *timers) {
   int32_t st = lce_dims_check(n_tok, d_model, vocab);
   if (st != LCE_OK) return st;
   st = lce_chunk_check(chunk, vocab);
@@ -597,11 +631,11 @@ int32_t lce_forward(const lce_tensor *hidden, const lce_tensor *weight,
   if (dt == LCE_BF16) {
     const bool vec = d_model % 8 == 0 && aligned16(hidden->data) && aligned16(weight->data);
     forward_impl<TraitsBF16>(p, hidden->data, weight->data, y, mask,
-                             static_cast<float *>(lse_out->data), ws, vec, s);
+                             static_cast<float *>(lse_out->data), ws, vec, s, timers);
   } else {
     const bool vec = d_model % 2 == 0 && aligned16(hidden->data) && aligned16(weight->data);
     forward_impl<TraitsF64>(p, hidden->data, weight->data, y, mask,
-                            static_cast<double *>(lse_out->data), ws, vec, s);
+                            static_cast<double *>(lse_out->data), ws, vec, s, timers);
   }
   Control hc;
   st = finish(s, reinterpret_cast<Control *>(ws), &hc);
@@ -620,6 +654,17 @@ int32_t lce_backward(const lce_tensor *hidden, const lce_tensor *weight,
                      int64_t chunk, double z_coef, double grad_out, lce_tensor *d_hidden,
                      lce_tensor *d_weight, int32_t accumulate_d_weight,
                      lce_tensor *workspace, void *stream) {
+  return lce_backward_timed(hidden, weight, targets, loss_mask, lse, n_tok, d_model, vocab, chunk,
+                            z_coef, grad_out, d_hidden, d_weight, accumulate_d_weight, workspace,
+                            stream, nullptr);
+}
+
+int32_t lce_backward_timed(const lce_tensor *hidden, const lce_tensor *weight,
+                           const lce_tensor *targets, const lce_tensor *loss_mask,
+                           const lce_tensor *lse, int64_t n_tok, int64_t d_model, int64_t vocab,
+                           int64_t chunk, double z_coef, double grad_out, lce_tensor *d_hidden,
+                           lce_tensor *d_weight, int32_t accumulate_d_weight,
+                           lce_tensor *workspace, void *stream, lce_timers *timers) {
   int32_t st = lce_dims_check(n_tok, d_model, vocab);
   if (st != LCE_OK) return st;
   st = lce_chunk_check(chunk, vocab);
@@ -654,14 +699,14 @@ int32_t lce_backward(const lce_tensor *hidden, const lce_tensor *weight,
                               static_cast<const float *>(lse->data), z_coef, grad_out,
                               static_cast<uint16_t *>(d_hidden->data),
                               static_cast<float *>(d_weight->data), accumulate_d_weight != 0, ws,
-                              vec, s);
+                              vec, s, timers);
   } else {
     const bool vec = d_model % 2 == 0 && aligned16(hidden->data) && aligned16(weight->data);
     backward_impl<TraitsF64>(p, hidden->data, weight->data, y, mask,
                              static_cast<const double *>(lse->data), z_coef, grad_out,
                              static_cast<double *>(d_hidden->data),
                              static_cast<double *>(d_weight->data), accumulate_d_weight != 0, ws,
-                             vec, s);
+                             vec, s, timers);
   }
   Control hc;
   return finish(s, reinterpret_cast<Control *>(ws), &hc);

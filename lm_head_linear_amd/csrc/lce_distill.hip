@@ -309,15 +309,23 @@ void launch_rows(bool vec, const T *S, const T *U, const uint8_t *mask, int64_t 
 template <class T>
 void distill_impl(int objective, bool vec, const T *S, const T *U, const uint8_t *mask,
                   int64_t n, int64_t V, double T_, double z, double go, Control *ctl, T *grad,
-                  double *rows, hipStream_t st) {
-  hipLaunchKernelGGL(distill_init_kernel, dim3(1), dim3(64), 0, st, ctl);
-  int64_t blocks = (n + 255) / 256;
-  if (blocks > 1024) blocks = 1024;
-  hipLaunchKernelGGL(distill_count_kernel, dim3(unsigned(blocks)), dim3(256), 0, st, mask, n, ctl);
+                  double *rows, hipStream_t st, lce_timers *tm) {
+  {
+    TimedLaunch tl(tm, LCE_K_GUARD, st);
+    hipLaunchKernelGGL(distill_init_kernel, dim3(1), dim3(64), 0, st, ctl);
+    int64_t blocks = (n + 255) / 256;
+    if (blocks > 1024) blocks = 1024;
+    hipLaunchKernelGGL(distill_count_kernel, dim3(unsigned(blocks)), dim3(256), 0, st, mask, n,
+                       ctl);
+  }
   const double inv_T = 1.0 / T_;
-  if (objective == 0) launch_rows<T, 0>(vec, S, U, mask, n, V, inv_T, z, go, ctl, grad, rows, st);
-  else if (objective == 1) launch_rows<T, 1>(vec, S, U, mask, n, V, inv_T, z, go, ctl, grad, rows, st);
-  else launch_rows<T, 2>(vec, S, U, mask, n, V, inv_T, z, go, ctl, grad, rows, st);
+  {
+    TimedLaunch tl(tm, LCE_K_DISTILL, st);
+    if (objective == 0) launch_rows<T, 0>(vec, S, U, mask, n, V, inv_T, z, go, ctl, grad, rows, st);
+    else if (objective == 1) launch_rows<T, 1>(vec, S, U, mask, n, V, inv_T, z, go, ctl, grad, rows, st);
+    else launch_rows<T, 2>(vec, S, U, mask, n, V, inv_T, z, go, ctl, grad, rows, st);
+  }
+  TimedLaunch tl(tm, LCE_K_REDUCE, st);
   hipLaunchKernelGGL(distill_final_kernel, dim3(1), dim3(1024), 0, st, (const double *)rows, mask,
                      n, ctl);
 }
@@ -335,6 +343,17 @@ extern "C" int32_t lce_distill_fwd_bwd(const lce_tensor *student, const lce_tens
                                        int32_t objective, double temperature, double z_coef,
                                        double grad_out, lce_tensor *grad_logits,
                                        lce_tensor *workspace, lce_loss *out, void *stream) {
+  return lce_distill_fwd_bwd_timed(student, teacher, loss_mask, n_tok, vocab, objective,
+                                   temperature, z_coef, grad_out, grad_logits, workspace, out,
+                                   stream, nullptr);
+}
+
+extern "C" int32_t lce_distill_fwd_bwd_timed(const lce_tensor *student, const lce_tensor *teacher,
+                                             const lce_tensor *loss_mask, int64_t n_tok,
+                                             int64_t vocab, int32_t objective, double temperature,
+                                             double z_coef, double grad_out,
+                                             lce_tensor *grad_logits, lce_tensor *workspace,
+                                             lce_loss *out, void *stream, lce_timers *timers) {
   DistillPlan p;
   int32_t st = plan_distill(n_tok, vocab, &p);
   if (st != LCE_OK) return st;
@@ -370,17 +389,17 @@ extern "C" int32_t lce_distill_fwd_bwd(const lce_tensor *student, const lce_tens
     distill_impl<uint16_t>(objective, vec, static_cast<const uint16_t *>(student->data),
                            static_cast<const uint16_t *>(teacher->data), mask, n_tok, vocab,
                            temperature, z_coef, grad_out, ctl,
-                           static_cast<uint16_t *>(grad_logits->data), rows, s);
+                           static_cast<uint16_t *>(grad_logits->data), rows, s, timers);
   else if (dt == LCE_F32)
     distill_impl<float>(objective, vec, static_cast<const float *>(student->data),
                         static_cast<const float *>(teacher->data), mask, n_tok, vocab,
                         temperature, z_coef, grad_out, ctl, static_cast<float *>(grad_logits->data),
-                        rows, s);
+                        rows, s, timers);
   else
     distill_impl<double>(objective, vec, static_cast<const double *>(student->data),
                          static_cast<const double *>(teacher->data), mask, n_tok, vocab,
                          temperature, z_coef, grad_out, ctl,
-                         static_cast<double *>(grad_logits->data), rows, s);
+                         static_cast<double *>(grad_logits->data), rows, s, timers);
   if (hipGetLastError() != hipSuccess) return LCE_DEVICE_ERROR;
   Control hc;
   if (hipMemcpyAsync(&hc, ctl, sizeof(Control), hipMemcpyDeviceToHost, s) != hipSuccess)

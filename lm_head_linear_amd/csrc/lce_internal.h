@@ -63,4 +63,13 @@ int32_t plan_distill(int64_t n, int64_t V, DistillPlan *p);
 bool finite_scalar(double x);
 size_t dtype_size(int32_t dtype);
 
+// Brackets one launch of kernel kind `kind` with the caller's events.
+struct TimedLaunch {
+  lce_timer_slot *slot;
+  void *stream;
+  int32_t idx;
+  TimedLaunch(lce_timers *t, int kind, void *st);
+  ~TimedLaunch();
+};
+
 }  // namespace lce

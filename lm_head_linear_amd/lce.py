@@ -44,6 +44,60 @@ class Peak(ctypes.Structure):
                 ("status", ctypes.c_int32)]
 
 
+NUM_KERNELS = 9
+KERNEL_KINDS = {"guard": 0, "fwd_gemm": 1, "fwd_merge": 2, "reduce": 3, "dlogit_gemm": 4,
+                "dw_gemm": 5, "dh_gemm": 6, "dh_final": 7, "distill": 8}
+
+
+class TimerSlot(ctypes.Structure):
+    _fields_ = [("start", ctypes.POINTER(ctypes.c_void_p)), ("stop", ctypes.POINTER(ctypes.c_void_p)),
+                ("capacity", ctypes.c_int32), ("used", ctypes.c_int32)]
+
+
+class Timers(ctypes.Structure):
+    _fields_ = [("slot", TimerSlot * NUM_KERNELS)]
+
+
+class KernelTimer:
+    """Caller-owned HIP events that the timed entry points record around each
+    launch of the chosen kernel kinds; elapsed times are read back here."""
+
+    def __init__(self, kinds, capacity: int, device=None):
+        self.kinds = list(kinds)
+        self.capacity = capacity
+        self.struct = Timers()
+        self._keep = []
+        self.events = {}
+        for k in self.kinds:
+            ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                  for _ in range(capacity)]
+            for a, b in ev:          # torch creates the HIP event on first record
+                a.record()
+                b.record()
+            starts = (ctypes.c_void_p * capacity)(*[a.cuda_event for a, _ in ev])
+            stops = (ctypes.c_void_p * capacity)(*[b.cuda_event for _, b in ev])
+            self._keep += [starts, stops]
+            sl = self.struct.slot[KERNEL_KINDS[k]]
+            sl.start = ctypes.cast(starts, ctypes.POINTER(ctypes.c_void_p))
+            sl.stop = ctypes.cast(stops, ctypes.POINTER(ctypes.c_void_p))
+            sl.capacity = capacity
+            sl.used = 0
+            self.events[k] = ev
+        torch.cuda.synchronize()
+
+    def reset(self):
+        for k in self.kinds:
+            self.struct.slot[KERNEL_KINDS[k]].used = 0
+
+    def used(self, kind) -> int:
+        return self.struct.slot[KERNEL_KINDS[kind]].used
+
+    def durations_ms(self, kind):
+        """Elapsed time of every recorded launch of `kind` (call after a sync)."""
+        n = self.used(kind)
+        return [a.elapsed_time(b) for a, b in self.events[kind][:n]]
+
+
 class Loss(ctypes.Structure):
     _fields_ = [("loss_sum", ctypes.c_double), ("loss_mean", ctypes.c_double),
                 ("z_sum", ctypes.c_double), ("z_mean", ctypes.c_double),
@@ -90,6 +144,13 @@ def lib():
         L.lce_distill_fwd_bwd.restype = i32
         L.lce_distill_fwd_bwd.argtypes = [PT, PT, PT, i64, i64, i32, dbl, dbl, dbl, PT, PT,
                                           ctypes.POINTER(Loss), vp]
+        PTM = ctypes.POINTER(Timers)
+        L.lce_forward_timed.restype = i32
+        L.lce_forward_timed.argtypes = L.lce_forward.argtypes + [PTM]
+        L.lce_backward_timed.restype = i32
+        L.lce_backward_timed.argtypes = L.lce_backward.argtypes + [PTM]
+        L.lce_distill_fwd_bwd_timed.restype = i32
+        L.lce_distill_fwd_bwd_timed.argtypes = L.lce_distill_fwd_bwd.argtypes + [PTM]
         _lib = L
     return _lib
 
@@ -148,40 +209,53 @@ def lce_distill_workspace_bytes(n_tok: int, vocab: int) -> int:
 # ------------------------------------------------------------ device calls
 
 def lce_forward(hidden, weight, targets, loss_mask, n_tok, d_model, vocab, chunk, z_coef,
-                lse_out, workspace, stream: Optional[int] = None):
-    """Direct call of the C entry point.  Returns (status, Loss)."""
+                lse_out, workspace, stream: Optional[int] = None,
+                timer: Optional[KernelTimer] = None):
+    """Direct call of the C entry point (lce_forward_timed when a timer is
+    given).  Returns (status, Loss)."""
     out = Loss()
     args = [_t(hidden), _t(weight), _t(targets), _t(loss_mask)]
     lse_t, ws_t = _t(lse_out), _t(workspace)
-    st = lib().lce_forward(*[ctypes.byref(a) for a in args], n_tok, d_model, vocab, chunk,
-                           float(z_coef), ctypes.byref(lse_t), ctypes.byref(ws_t),
-                           ctypes.byref(out), stream if stream is not None else
-                           _stream(hidden.device))
+    call = [*[ctypes.byref(a) for a in args], n_tok, d_model, vocab, chunk, float(z_coef),
+            ctypes.byref(lse_t), ctypes.byref(ws_t), ctypes.byref(out),
+            stream if stream is not None else _stream(hidden.device)]
+    if timer is None:
+        st = lib().lce_forward(*call)
+    else:
+        st = lib().lce_forward_timed(*call, ctypes.byref(timer.struct))
     return st, out
 
 
 def lce_backward(hidden, weight, targets, loss_mask, lse, n_tok, d_model, vocab, chunk, z_coef,
                  grad_out, d_hidden, d_weight, accumulate_d_weight, workspace,
-                 stream: Optional[int] = None) -> int:
-    """Direct call of the C entry point.  Returns the status."""
+                 stream: Optional[int] = None, timer: Optional[KernelTimer] = None) -> int:
+    """Direct call of the C entry point (lce_backward_timed when a timer is
+    given).  Returns the status."""
     ts = [_t(hidden), _t(weight), _t(targets), _t(loss_mask), _t(lse)]
     dh, dw, ws = _t(d_hidden), _t(d_weight), _t(workspace)
-    return lib().lce_backward(*[ctypes.byref(a) for a in ts], n_tok, d_model, vocab, chunk,
-                              float(z_coef), float(grad_out), ctypes.byref(dh), ctypes.byref(dw),
-                              int(bool(accumulate_d_weight)), ctypes.byref(ws),
-                              stream if stream is not None else _stream(hidden.device))
+    call = [*[ctypes.byref(a) for a in ts], n_tok, d_model, vocab, chunk, float(z_coef),
+            float(grad_out), ctypes.byref(dh), ctypes.byref(dw), int(bool(accumulate_d_weight)),
+            ctypes.byref(ws), stream if stream is not None else _stream(hidden.device)]
+    if timer is None:
+        return lib().lce_backward(*call)
+    return lib().lce_backward_timed(*call, ctypes.byref(timer.struct))
 
 
 def lce_distill_fwd_bwd(student, teacher, loss_mask, n_tok, vocab, objective, temperature,
-                        z_coef, grad_out, grad_logits, workspace, stream: Optional[int] = None):
-    """Direct call of the C entry point.  Returns (status, Loss)."""
+                        z_coef, grad_out, grad_logits, workspace, stream: Optional[int] = None,
+                        timer: Optional[KernelTimer] = None):
+    """Direct call of the C entry point (the _timed variant when a timer is
+    given).  Returns (status, Loss)."""
     out = Loss()
     ts = [_t(student), _t(teacher), _t(loss_mask)]
     g, ws = _t(grad_logits), _t(workspace)
-    st = lib().lce_distill_fwd_bwd(*[ctypes.byref(a) for a in ts], n_tok, vocab, int(objective),
-                                   float(temperature), float(z_coef), float(grad_out),
-                                   ctypes.byref(g), ctypes.byref(ws), ctypes.byref(out),
-                                   stream if stream is not None else _stream(student.device))
+    call = [*[ctypes.byref(a) for a in ts], n_tok, vocab, int(objective), float(temperature),
+            float(z_coef), float(grad_out), ctypes.byref(g), ctypes.byref(ws), ctypes.byref(out),
+            stream if stream is not None else _stream(student.device)]
+    if timer is None:
+        st = lib().lce_distill_fwd_bwd(*call)
+    else:
+        st = lib().lce_distill_fwd_bwd_timed(*call, ctypes.byref(timer.struct))
     return st, out
 
 
