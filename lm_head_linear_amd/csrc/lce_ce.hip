@@ -21,8 +21,10 @@
 #include <cfloat>
 #include <climits>
 #include <cmath>
+#include <type_traits>
 
 #include "lce_gemm.hpp"
+#include "lce_gemm2.hpp"
 #include "lce_internal.h"
 
 namespace lce {
@@ -380,6 +382,16 @@ struct StoreEpi {
   }
 };
 
+// Zero the token columns [n, d_ld) of every slab-buffer row: the pipelined
+// d_weight GEMM reads K in steps of 32 and relies on them being zero.
+template <class E>
+__global__ void zero_pad_kernel(E *dbuf, int64_t rows, int64_t d_ld, int64_t n) {
+  const int64_t w = d_ld - n;
+  for (int64_t i = int64_t(blockIdx.x) * blockDim.x + threadIdx.x; i < rows * w;
+       i += int64_t(gridDim.x) * blockDim.x)
+    dbuf[(i / w) * d_ld + n + i % w] = E(0);
+}
+
 // d_hidden = sum over splits (ascending) of the split accumulators.
 template <class TR>
 __global__ void dh_final_kernel(const typename TR::Acc *P, int64_t splits, int64_t count,
@@ -429,6 +441,46 @@ static void launch_gemm(bool vec, const GemmParams &g, int64_t splits, const Epi
     hipLaunchKernelGGL((gemm_kernel<TR, AK, BKM, false, Epi>), grid, dim3(TR::NT), 0, st, g, epi);
 }
 
+template <bool AK, bool BKM, class Epi>
+static void launch_gemm2(const Gemm2Params &g, int64_t splits, const Epi &epi, hipStream_t st) {
+  const int64_t tiles = cdiv(g.M, Pipe::BM) * g.tiles_n;
+  const dim3 grid{unsigned(tiles), unsigned(splits), 1u};
+  hipLaunchKernelGGL((gemm2_kernel<Pipe, AK, BKM, Epi>), grid, dim3(Pipe::NT), 0, st, g, epi);
+}
+
+static Gemm2Params to2(const GemmParams &g) {
+  Gemm2Params r;
+  r.A = g.A; r.lda = g.lda; r.B = g.B; r.ldb = g.ldb;
+  r.M = g.M; r.N = g.N; r.K = g.K; r.M_read = g.M_read; r.N_read = g.N_read;
+  r.k_per_split = (g.k_per_split + Pipe::BK - 1) / Pipe::BK * Pipe::BK;
+  r.tiles_n = g.tiles_n; r.bad = g.bad;
+  return r;
+}
+
+// The pipelined bf16 core applies when every operand is 16-byte aligned with
+// leading dimensions that are multiples of 8 and d_model is a multiple of the
+// pipeline's k-step.
+template <class TR> struct UsePipe { static bool ok(bool, int64_t, int64_t) { return false; } };
+template <> struct UsePipe<TraitsBF16> {
+  static bool ok(bool vec, int64_t D, int64_t d_ld) {
+    return vec && D % Pipe::BK == 0 && 256 * D * 2 < (int64_t(1) << 31) &&
+           256 * d_ld * 2 < (int64_t(1) << 31);
+  }
+};
+
+// bf16 with `pipe`: the pipelined core; otherwise the generic one.
+template <class TR, bool AK, bool BKM, class Epi>
+static void launch_any(bool pipe, bool vec, const GemmParams &g, int64_t splits, const Epi &epi,
+                       hipStream_t st) {
+  if constexpr (std::is_same<TR, TraitsBF16>::value) {
+    if (pipe) {
+      launch_gemm2<AK, BKM>(to2(g), splits, epi, st);
+      return;
+    }
+  }
+  launch_gemm<TR, AK, BKM>(vec, g, splits, epi, st);
+}
+
 static void launch_guard(const int64_t *y, const uint8_t *mask, int64_t n, int64_t V,
                          Control *ctl, hipStream_t st, lce_timers *tm) {
   TimedLaunch tl(tm, LCE_K_GUARD, st);
@@ -462,7 +514,7 @@ static void forward_impl(const CEPlan &p, const void *H, const void *W, const in
     FwdLseEpi<TR> epi{y + tok0, ntok, p.V, p.n_vparts, partials, zy + tok0};
     {
       TimedLaunch tl(tm, LCE_K_FWD_GEMM, st);
-      launch_gemm<TR, true, true>(vec, g, 1, epi, st);
+      launch_any<TR, true, true>(UsePipe<TR>::ok(vec, p.D, p.d_ld), vec, g, 1, epi, st);
     }
     TimedLaunch tl(tm, LCE_K_FWD_MERGE, st);
     hipLaunchKernelGGL(fwd_merge_kernel<Acc>, dim3(unsigned(cdiv(ntok, 4))), dim3(256), 0, st,
@@ -488,6 +540,13 @@ static void backward_impl(const CEPlan &p, const void *H, const void *W, const i
   const E *Hp = static_cast<const E *>(H);
   const E *Wp = static_cast<const E *>(W);
   launch_guard(y, mask, p.n, p.V, ctl, st, tm);
+  const bool pipe = UsePipe<TR>::ok(vec, p.D, p.d_ld);
+  if (pipe && p.d_ld > p.n) {
+    int64_t blocks = cdiv(p.slab * (p.d_ld - p.n), 256);
+    if (blocks > 1024) blocks = 1024;
+    hipLaunchKernelGGL(zero_pad_kernel<E>, dim3(unsigned(blocks)), dim3(256), 0, st, dbuf, p.slab,
+                       p.d_ld, p.n);
+  }
   for (int64_t s = 0; s < p.n_slabs; ++s) {
     const int64_t vs0 = s * p.slab;
     const int64_t rows = p.slab < p.V - vs0 ? p.slab : p.V - vs0;
@@ -503,7 +562,7 @@ static void backward_impl(const CEPlan &p, const void *H, const void *W, const i
       g.bad = &ctl->bad;
       DlogitEpi<TR> epi{y, mask, lse, p.n, vs0, rows, ctl, grad_out, z_coef, dbuf, p.d_ld};
       TimedLaunch tl(tm, LCE_K_DLOGIT_GEMM, st);
-      launch_gemm<TR, true, true>(vec, g, 1, epi, st);
+      launch_any<TR, true, true>(pipe, vec, g, 1, epi, st);
     }
     {  // d_weight rows of the slab = d^T H over all tokens
       GemmParams g;
@@ -515,10 +574,10 @@ static void backward_impl(const CEPlan &p, const void *H, const void *W, const i
       g.tiles_n = cdiv(p.D, TR::BN);
       g.bad = &ctl->bad;
       TimedLaunch tl(tm, LCE_K_DW_GEMM, st);
-      if (accumulate)
-        launch_gemm<TR, true, false>(vec, g, 1, StoreEpi<TR, true>{dW, p.D, vs0, rows, p.D, 0}, st);
-      else
-        launch_gemm<TR, true, false>(vec, g, 1, StoreEpi<TR, false>{dW, p.D, vs0, rows, p.D, 0}, st);
+      const StoreEpi<TR, true> e_acc{dW, p.D, vs0, rows, p.D, 0};
+      const StoreEpi<TR, false> e_set{dW, p.D, vs0, rows, p.D, 0};
+      if (accumulate) launch_any<TR, true, false>(pipe, vec, g, 1, e_acc, st);
+      else launch_any<TR, true, false>(pipe, vec, g, 1, e_set, st);
     }
     {  // d_hidden split accumulators += d W_slab
       const int64_t kps = cdiv(cdiv(rows, p.dh_splits), TR::BK) * TR::BK;
@@ -531,12 +590,10 @@ static void backward_impl(const CEPlan &p, const void *H, const void *W, const i
       g.tiles_n = cdiv(p.D, TR::BN);
       g.bad = &ctl->bad;
       TimedLaunch tl(tm, LCE_K_DH_GEMM, st);
-      if (s > 0)
-        launch_gemm<TR, false, false>(vec, g, p.dh_splits,
-                                      StoreEpi<TR, true>{dhacc, p.D, 0, p.n, p.D, p.n * p.D}, st);
-      else
-        launch_gemm<TR, false, false>(vec, g, p.dh_splits,
-                                      StoreEpi<TR, false>{dhacc, p.D, 0, p.n, p.D, p.n * p.D}, st);
+      const StoreEpi<TR, true> e_acc{dhacc, p.D, 0, p.n, p.D, p.n * p.D};
+      const StoreEpi<TR, false> e_set{dhacc, p.D, 0, p.n, p.D, p.n * p.D};
+      if (s > 0) launch_any<TR, false, false>(pipe, vec, g, p.dh_splits, e_acc, st);
+      else launch_any<TR, false, false>(pipe, vec, g, p.dh_splits, e_set, st);
     }
   }
   int64_t count = p.n * p.D;

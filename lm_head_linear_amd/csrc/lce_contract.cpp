@@ -54,7 +54,7 @@ int32_t plan_ce(int64_t n, int64_t D, int64_t V, int64_t chunk, int32_t dtype, C
 
   // Backward: the logit-gradient buffer holds a slab of vocabulary rows for
   // every token, at most chunk*vocab cells; slabs are balanced in size.
-  q.d_ld = round_up(n, 8);
+  q.d_ld = round_up(n, 64);
   int64_t slab_max = budget / q.d_ld;
   if (slab_max >= tile_m) slab_max = slab_max / tile_m * tile_m;
   else if (slab_max >= 32) slab_max = slab_max / 32 * 32;

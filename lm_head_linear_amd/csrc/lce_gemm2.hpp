@@ -1,0 +1,308 @@
+// lce_gemm2.hpp -- pipelined bf16 GEMM core for gfx950 (CDNA4).
+//
+// Same contract as gemm_kernel in lce_gemm.hpp (C = A(m,k) B(n,k) per
+// 256x256 tile, accumulators handed to an epilogue in the 32x32x16 MFMA
+// layout), built for throughput:
+//   * operands go global -> LDS with buffer_load_dwordx4 ... lds (no staging
+//     registers); the buffer descriptor's record count zero-fills every
+//     element past the operand's valid extent, which handles the M/N edges and
+//     the K tail of MN-major operands without branches;
+//   * a ring of 4 LDS stages of BK = 32 (128 KB) keeps 3 k-steps of loads in
+//     flight; each stage ends with one s_barrier after a vmcnt wait that only
+//     covers the stage about to be read;
+//   * K-major tiles keep 64-byte rows and are read with ds_read_b128; MN-major
+//     tiles keep their global orientation (512-byte k-rows) and are read with
+//     ds_read_b64_tr_b16, which hands each lane four consecutive k of one row.
+//     XOR swizzles of the 16-byte chunks keep the DMA writes and both kinds of
+//     operand reads free of LDS bank conflicts;
+//   * operand fragments are double-buffered in registers: the MFMAs of one
+//     k-substep run while the next substep's fragments are read, and the
+//     stage barrier sits between the two substeps, so LDS latency and the DMA
+//     issue hide behind MFMA work.
+// Requirements (checked by the host): 16-byte aligned bases, leading
+// dimensions multiple of 8, K-major operands zero-padded (or exact) to a
+// multiple of 32 along K, 256 * ld * 2 bytes below 2^31.
+#pragma once
+
+#include <type_traits>
+
+#include "lce_gemm.hpp"
+
+namespace lce {
+
+typedef short shortx4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) void lds_void_t;
+typedef __attribute__((address_space(3))) shortx4 lds_shortx4_t;
+
+template <int BK_, int STAGES_>
+struct PipeCfg {
+  static constexpr int BM = 256, BN = 256, BK = BK_, STAGES = STAGES_;
+  static constexpr int NT = 256;
+  static constexpr int KSUB = BK / 16;                // MFMA k-substeps per stage
+  static constexpr int ROWB = BK * 2;                  // bytes per K-major tile row
+  static constexpr int OP_BYTES = 256 * BK * 2;       // per operand per stage
+  static constexpr int STAGE_BYTES = 2 * OP_BYTES;
+  static constexpr int INSTR = OP_BYTES / 1024 / 4;   // DMA instructions per wave per operand
+  static constexpr int LOADS_PER_STAGE = 2 * INSTR;   // per wave
+};
+typedef PipeCfg<32, 4> Pipe;   // the configuration the library launches
+
+// Chunk swizzles.  K-major rows of 64 bytes (BK 32) or 128 bytes (BK 64): the
+// rows read by 16 consecutive lanes land in 16 distinct 16-byte bank groups of
+// a 256-byte window, and any 8 consecutive rows in 8 distinct groups of a
+// 128-byte window.  MN-major (512-byte k-rows): the four k-rows x 32 bytes read
+// by a 16-lane group of ds_read_b64_tr_b16, and the two such groups reading
+// the same k-rows, never share a bank.
+template <int ROWB>
+__device__ inline int kswz(int r) {
+  if (ROWB == 64) return ((r >> 1) & 3) ^ ((r >> 3) & 1);
+  return ((r >> 1) & 7) ^ ((r & 1) << 2);
+}
+__device__ inline int mswz2(int q) { return (q & 3) << 2; }
+
+__device__ inline __amdgpu_buffer_rsrc_t make_rsrc(const void *base, int64_t bytes) {
+  if (bytes < 0) bytes = 0;
+  if (bytes > 0x7fffffff) bytes = 0x7fffffff;
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), 0, int(bytes), 0x00020000);
+}
+
+// One 16-byte-per-lane load from the buffer `rs` at byte offset `voff` into
+// LDS at `dst` + 16 * lane.
+__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t rs, char *dst, uint32_t voff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void_t *)dst, 16, voff, 0, 0, 0);
+}
+
+// One operand of one stage: OP_BYTES / 1 KB wave-instructions, INSTR per wave.
+template <class CFG, bool KMAJOR>
+struct PipeOperand {
+  const uint16_t *p;   // operand base (element 0 of row/k-row 0)
+  int64_t ld;          // leading dimension in elements
+  int64_t row0;        // first tile row (M or N index)
+  int64_t row_lim;     // valid rows (K-major) / readable row length (MN-major)
+  int64_t k_lim;       // valid k (MN-major zero-fill)
+  uint32_t voff[CFG::INSTR];  // per-lane byte offsets
+  __amdgpu_buffer_rsrc_t rs;
+
+  __device__ inline void init(const uint16_t *p_, int64_t ld_, int64_t row0_, int64_t row_lim_,
+                              int64_t k_lim_, int wave, int lane) {
+    p = p_; ld = ld_; row0 = row0_; row_lim = row_lim_; k_lim = k_lim_;
+    constexpr int CPR = CFG::ROWB / 16;   // 16-byte chunks per K-major row
+    if (KMAJOR) {
+      rs = make_rsrc(p + row0 * ld, (row_lim - row0) * ld * 2);
+#pragma unroll
+      for (int i = 0; i < CFG::INSTR; ++i) {
+        const int j = wave * CFG::INSTR + i;
+        const int r = (64 / CPR) * j + lane / CPR;
+        const int c = (lane % CPR) ^ kswz<CFG::ROWB>(r);
+        voff[i] = uint32_t(r) * uint32_t(ld * 2) + uint32_t(c * 16);
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < CFG::INSTR; ++i) {
+        const int j = wave * CFG::INSTR + i;
+        const int q = 2 * j + (lane >> 5);
+        const int c = (lane & 31) ^ mswz2(q);
+        voff[i] = uint32_t(q) * uint32_t(ld * 2) + uint32_t(c * 16);
+      }
+    }
+  }
+
+  // Issue this wave's 4 loads of k-step k0 into the operand region `dst`.
+  __device__ inline void issue(int64_t k0, char *dst, int wave) const {
+    if (KMAJOR) {
+#pragma unroll
+      for (int i = 0; i < CFG::INSTR; ++i) {
+        const int j = wave * CFG::INSTR + i;
+        dma16(rs, dst + j * 1024, voff[i] + uint32_t(k0 * 2));
+      }
+    } else {
+      // base at (k0, row0): bytes up to the end of row k_lim-1's readable part
+      const int64_t rows = k_lim - k0;
+      const int64_t bytes = rows > 0 ? ((rows - 1) * ld + (row_lim - row0)) * 2 : 0;
+      const __amdgpu_buffer_rsrc_t r = make_rsrc(p + k0 * ld + row0, bytes);
+#pragma unroll
+      for (int i = 0; i < CFG::INSTR; ++i) {
+        const int j = wave * CFG::INSTR + i;
+        dma16(r, dst + j * 1024, voff[i]);
+      }
+    }
+  }
+
+  // The 32x32x16 MFMA operand of tile rows base..base+31 for k-substep kk.
+  __device__ inline u32x4 frag(const char *src, int base, int kk, int lane) const {
+    if (KMAJOR) {
+      const int r = base + (lane & 31);
+      const int c = kk * 2 + (lane >> 5);
+      return *reinterpret_cast<const u32x4 *>(src + r * CFG::ROWB +
+                                              ((c ^ kswz<CFG::ROWB>(r)) << 4));
+    } else {
+      const int g = lane >> 4, i = lane & 15;
+      const int mn = base + 16 * (g & 1) + 4 * (i & 3);
+      const int kb = kk * 16 + 8 * (g >> 1) + (i >> 2);
+      u32x4 out;
+#pragma unroll
+      for (int q = 0; q < 2; ++q) {
+        const int krow = kb + 4 * q;
+        const char *a = src + krow * 512 + (((mn >> 3) ^ mswz2(krow)) << 4) + (mn & 7) * 2;
+        const shortx4 h = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_shortx4_t *)(a));
+        out[2 * q] = uint32_t(uint16_t(h[0])) | (uint32_t(uint16_t(h[1])) << 16);
+        out[2 * q + 1] = uint32_t(uint16_t(h[2])) | (uint32_t(uint16_t(h[3])) << 16);
+      }
+      return out;
+    }
+  }
+};
+
+struct Gemm2Params {
+  const void *A;
+  int64_t lda;
+  const void *B;
+  int64_t ldb;
+  int64_t M, N, K;          // K: valid depth (K-major operands are zero-padded past it)
+  int64_t M_read, N_read;   // readable row lengths of MN-major operands
+  int64_t k_per_split;      // multiple of 32
+  int64_t tiles_n;
+  const int32_t *bad;
+};
+
+// s_waitcnt lgkmcnt(0) vmcnt(N) followed by a bare s_barrier: unlike
+// __syncthreads this leaves the N most recent loads in flight.
+template <int N>
+__device__ inline void wait_vm_barrier() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  asm volatile("s_waitcnt lgkmcnt(0) vmcnt(%0)\n\ts_barrier" ::"n"(N) : "memory");
+}
+// The same with the count chosen at run time among 0, L, 2L, ... (L loads per
+// stage, up to S stages).
+template <int L, int S>
+__device__ inline void wait_vm_barrier_stages(int stages) {
+  if constexpr (S > 0) {
+    if (stages >= S) { wait_vm_barrier<L * S>(); return; }
+    wait_vm_barrier_stages<L, S - 1>(stages);
+  } else {
+    wait_vm_barrier<0>();
+  }
+}
+
+template <class CFG, bool AK, bool BKM, class Epi>
+__global__ void __launch_bounds__(CFG::NT) gemm2_kernel(Gemm2Params g, Epi epi) {
+  typedef TraitsBF16 TR;
+  constexpr int BK = CFG::BK, STAGES = CFG::STAGES, KSUB = CFG::KSUB;
+  constexpr int LPS = CFG::LOADS_PER_STAGE;
+  static_assert(KSUB % 2 == 0 && KSUB >= 2, "fragment double-buffer parity");
+  if (g.bad && *g.bad) return;
+  __shared__ __attribute__((aligned(1024))) char smem[STAGES * CFG::STAGE_BYTES];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+
+  const int64_t L = xcd_remap(blockIdx.x, gridDim.x);
+  const int64_t m0 = (L / g.tiles_n) * CFG::BM;
+  const int64_t n0 = (L % g.tiles_n) * CFG::BN;
+  const int split = blockIdx.y;
+  const int64_t k_begin = int64_t(split) * g.k_per_split;
+  int64_t k_end = k_begin + g.k_per_split;
+  if (k_end > g.K) k_end = g.K;
+  const int n_k = k_end > k_begin ? int((k_end - k_begin + BK - 1) / BK) : 0;
+
+  TR::AccBlock acc[TR::FM][TR::FN];
+#pragma unroll
+  for (int fm = 0; fm < TR::FM; ++fm)
+#pragma unroll
+    for (int fn = 0; fn < TR::FN; ++fn)
+#pragma unroll
+      for (int r = 0; r < TR::R; ++r) acc[fm][fn][r] = 0;
+
+  PipeOperand<CFG, AK> pa;
+  PipeOperand<CFG, BKM> pb;
+  pa.init(static_cast<const uint16_t *>(g.A), g.lda, m0, AK ? g.M : g.M_read, g.K, wave, lane);
+  pb.init(static_cast<const uint16_t *>(g.B), g.ldb, n0, BKM ? g.N : g.N_read, g.K, wave, lane);
+
+  // Prologue: every stage of the ring in flight; wait for stage 0 and read its
+  // first k-substep fragments.
+#pragma unroll
+  for (int s = 0; s < STAGES; ++s) {
+    if (s < n_k) {
+      char *st = smem + s * CFG::STAGE_BYTES;
+      pa.issue(k_begin + int64_t(s) * BK, st, wave);
+      pb.issue(k_begin + int64_t(s) * BK, st + CFG::OP_BYTES, wave);
+    }
+  }
+  wait_vm_barrier_stages<LPS, STAGES - 1>(n_k - 1);
+  u32x4 fa[2][TR::FM], fb[2][TR::FN];
+  if (n_k > 0) {
+#pragma unroll
+    for (int f = 0; f < 4; ++f) {
+      fa[0][f] = pa.frag(smem, wm * TR::WTM + f * 32, 0, lane);
+      fb[0][f] = pb.frag(smem + CFG::OP_BYTES, wn * TR::WTN + f * 32, 0, lane);
+    }
+  }
+
+  // One k-step of BK = KSUB MFMA k-substeps.  Substep kk computes on the
+  // fragments read during substep kk-1 while reading those of kk+1 (of the
+  // next stage for the last substep).  Between the last two substeps: stage
+  // it+1 has landed in every wave's view and stage it is in registers
+  // everywhere, so its buffer is refilled with stage it+STAGES.  STEADY: a
+  // refill is due and STAGES-2 later stages are in flight.
+  auto step = [&](const int it, auto steady_tag) {
+    constexpr bool STEADY = decltype(steady_tag)::value;
+    char *sa = smem + (it % CFG::STAGES) * CFG::STAGE_BYTES;
+    const char *sn = smem + ((it + 1) % CFG::STAGES) * CFG::STAGE_BYTES;
+#pragma unroll
+    for (int kk = 0; kk < CFG::KSUB; ++kk) {
+      const int cur = kk & 1, nxt = cur ^ 1;
+      const bool last = kk == CFG::KSUB - 1;
+      if (!last || STEADY || it + 1 < n_k) {
+        const char *src = last ? sn : sa;
+        const int ks = last ? 0 : kk + 1;
+#pragma unroll
+        for (int f = 0; f < 4; ++f) {
+          fa[nxt][f] = pa.frag(src, wm * TR::WTM + f * 32, ks, lane);
+          fb[nxt][f] = pb.frag(src + CFG::OP_BYTES, wn * TR::WTN + f * 32, ks, lane);
+        }
+      }
+#pragma unroll
+      for (int fm = 0; fm < TR::FM; ++fm)
+#pragma unroll
+        for (int fn = 0; fn < TR::FN; ++fn)
+          acc[fm][fn] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+              __builtin_bit_cast(bf16x8, fa[cur][fm]), __builtin_bit_cast(bf16x8, fb[cur][fn]),
+              acc[fm][fn], 0, 0, 0);
+      if (last && STEADY) {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                // one MFMA
+          if (i < CFG::LOADS_PER_STAGE) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);   // one refill load
+          if (i < 8) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);     // one LDS read
+        }
+      } else if (!last) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // one MFMA
+          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // one LDS read
+        }
+        __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
+      }
+      if (kk == CFG::KSUB - 2) {
+        if (STEADY) wait_vm_barrier<CFG::LOADS_PER_STAGE * (CFG::STAGES - 2)>();
+        else wait_vm_barrier_stages<CFG::LOADS_PER_STAGE, CFG::STAGES - 2>(n_k - 2 - it);
+        if (STEADY || it + CFG::STAGES < n_k) {
+          pa.issue(k_begin + int64_t(it + CFG::STAGES) * CFG::BK, sa, wave);
+          pb.issue(k_begin + int64_t(it + CFG::STAGES) * CFG::BK, sa + CFG::OP_BYTES, wave);
+        }
+      }
+    }
+  };
+  int it = 0;
+  for (; it + STAGES < n_k; ++it) step(it, std::true_type{});
+  for (; it < n_k; ++it) step(it, std::false_type{});
+
+  int lane_e = lane, wm_e = wm, wn_e = wn;
+  int64_t m0_e = m0, n0_e = n0;
+  asm volatile("" : "+v"(lane_e), "+v"(wm_e), "+v"(wn_e), "+v"(m0_e), "+v"(n0_e));
+  epi(acc, m0_e, n0_e, wm_e, wn_e, lane_e, split);
+}
+
+}  // namespace lce
