@@ -4,7 +4,8 @@
 // the memory goes", on "Loss functions and resident-context kernels"):
 //   one MFMA GEMM launch per token pass computes logit tiles Z^T = W H^T in
 //   registers and reduces each (token, 128-row vocabulary block) at once to an
-//   online (max, sum-of-exp) pair plus the target logit; no logit is stored.
+//   online (max, sum-of-exp) pair; no logit is stored.  The target logits
+//   <H_t, W_{y_t}> come from one small dot-product kernel.
 //   A merge kernel folds the pairs in a fixed order into lse_t, and one
 //   fixed-tree reduction sums the counted tokens' losses and lse_t^2 in fp64.
 // Backward (lossk table, fused_linear_ce_bwd_flat; the one-hot superposition
@@ -111,6 +112,9 @@ template <> __device__ inline double col_sum<TraitsF64, double>(double x) {
 template <class TR> __device__ inline typename TR::E to_elem(typename TR::Acc x);
 template <> __device__ inline uint16_t to_elem<TraitsBF16>(float x) { return f32_to_bf16_rne(x); }
 template <> __device__ inline double to_elem<TraitsF64>(double x) { return x; }
+template <class TR> __device__ inline typename TR::Acc to_acc(typename TR::E x);
+template <> __device__ inline float to_acc<TraitsBF16>(uint16_t x) { return bf16_to_f32(x); }
+template <> __device__ inline double to_acc<TraitsF64>(double x) { return x; }
 
 // ------------------------------------------------------ forward epilogue --
 
@@ -123,78 +127,47 @@ template <> __device__ inline float shift_exp<float>(float x, float m) {
 }
 template <> __device__ inline double shift_exp<double>(double x, double m) { return exp(x - m); }
 
-// (max, sum exp(v - max)) over the rows of one output column held by a wave;
-// with CHECK only rows below `lim` (relative to the wave's first row) count.
-template <class TR, bool CHECK>
-__device__ __forceinline__ void column_lse(const typename TR::AccBlock (&acc)[TR::FM][TR::FN],
-                                           const int fn, const int lane, const int lim,
-                                           typename TR::Acc &mx_out, typename TR::Acc &s_out) {
-  typedef typename TR::Acc Acc;
-  Acc mx = neg_inf<Acc>();
-#pragma unroll
-  for (int fm = 0; fm < TR::FM; ++fm)
-#pragma unroll
-    for (int r = 0; r < TR::R; ++r)
-      if (!CHECK || fm * TR::MF + TR::row_of(r, lane) < lim)
-        mx = acc[fm][fn][r] > mx ? acc[fm][fn][r] : mx;
-  mx = col_max<TR, Acc>(mx);
-  Acc s = 0;
-#pragma unroll
-  for (int fm = 0; fm < TR::FM; ++fm)
-#pragma unroll
-    for (int r = 0; r < TR::R; ++r)
-      if (!CHECK || fm * TR::MF + TR::row_of(r, lane) < lim) s += shift_exp<Acc>(acc[fm][fn][r], mx);
-  s_out = col_sum<TR, Acc>(s);
-  mx_out = mx;
-}
-
-// The accumulator of this lane whose row (relative to the wave) is `yl`, or 0
-// when the lane holds no such row.  A sum of selects keeps every accumulator
-// index static, so the accumulators stay in registers.
-template <class TR>
-__device__ __forceinline__ typename TR::Acc pick_row(
-    const typename TR::AccBlock (&acc)[TR::FM][TR::FN], const int fn, const int lane, const int yl) {
-  typename TR::Acc z = 0;
-#pragma unroll
-  for (int fm = 0; fm < TR::FM; ++fm)
-#pragma unroll
-    for (int r = 0; r < TR::R; ++r)
-      z += (fm * TR::MF + TR::row_of(r, lane) == yl) ? acc[fm][fn][r] : typename TR::Acc(0);
-  return z;
-}
-
 // Z^T tile: rows = vocabulary ids, columns = tokens of the pass.  For every
 // token column and every wave (WTM consecutive vocabulary rows) write
-// (max, sum exp(z - max)) and, where the target falls in those rows, z[y].
+// (max, sum exp(z - max)).  (The target logits come from target_logit_kernel.)
 template <class TR>
 struct FwdLseEpi {
   typedef typename TR::Acc Acc;
-  const int64_t *targets;  // first token of the pass
+  static constexpr bool kStaged = false;
   int64_t n_cols;          // tokens in the pass
   int64_t V;
   int64_t n_vparts;
   Acc *partials;           // [n_cols][n_vparts][2]
-  Acc *zy;                 // first token of the pass
 
-  __device__ __forceinline__ void emit(const typename TR::AccBlock (&acc)[TR::FM][TR::FN],
-                                       int fn, int64_t t, int64_t vrow0, int64_t vpart, int lane,
-                                       Acc mx, Acc s) const {
-    if (t >= n_cols) return;
-    if (lane < TR::MF) {
-      Acc *p = partials + (t * n_vparts + vpart) * 2;
-      p[0] = mx;
-      p[1] = s;
+  // With CHECK only rows below `lim` (relative to the wave's first row)
+  // count; row 0 always does, so every column max is finite.
+  template <bool CHECK>
+  __device__ __forceinline__ void body(const typename TR::AccBlock (&acc)[TR::FM][TR::FN],
+                                       int64_t tcol, int64_t vpart, int lane, int lim) const {
+#pragma unroll
+    for (int fn = 0; fn < TR::FN; ++fn) {
+      Acc x[TR::FM * TR::R];
+#pragma unroll
+      for (int fm = 0; fm < TR::FM; ++fm)
+#pragma unroll
+        for (int r = 0; r < TR::R; ++r)
+          x[fm * TR::R + r] = (!CHECK || fm * TR::MF + TR::row_of(r, lane) < lim)
+                                  ? acc[fm][fn][r] : neg_inf<Acc>();
+      Acc mx = x[0];
+#pragma unroll
+      for (int i = 1; i < TR::FM * TR::R; ++i) mx = fmax(mx, x[i]);
+      mx = col_max<TR, Acc>(mx);
+      Acc sm = 0;
+#pragma unroll
+      for (int i = 0; i < TR::FM * TR::R; ++i) sm += shift_exp<Acc>(x[i], mx);
+      sm = col_sum<TR, Acc>(sm);
+      const int64_t t = tcol + fn * TR::MF;
+      if (lane < TR::MF && t < n_cols) {
+        Acc *p = partials + (t * n_vparts + vpart) * 2;
+        p[0] = mx;
+        p[1] = sm;
+      }
     }
-    const int64_t yr = targets[t] - vrow0;
-    const int yl = (yr >= 0 && yr < TR::WTM) ? int(yr) : -1;
-    const Acc z = pick_row<TR>(acc, fn, lane, yl);
-    // exactly one lane of the column holds row yl
-    bool mine = false;
-#pragma unroll
-    for (int fm = 0; fm < TR::FM; ++fm)
-#pragma unroll
-      for (int r = 0; r < TR::R; ++r) mine |= (fm * TR::MF + TR::row_of(r, lane) == yl);
-    if (mine) zy[t] = z;
   }
 
   __device__ __forceinline__ void operator()(typename TR::AccBlock (&acc)[TR::FM][TR::FN], int64_t m0, int64_t n0,
@@ -204,23 +177,29 @@ struct FwdLseEpi {
     const int64_t vpart = vrow0 / TR::WTM;
     const int lim = V - vrow0 < TR::WTM ? int(V - vrow0) : TR::WTM;
     const int64_t tcol = n0 + int64_t(wn) * TR::WTN + TR::col_of(lane);
-    if (lim == TR::WTM) {
-#pragma unroll
-      for (int fn = 0; fn < TR::FN; ++fn) {
-        Acc mx, s;
-        column_lse<TR, false>(acc, fn, lane, lim, mx, s);
-        emit(acc, fn, tcol + fn * TR::MF, vrow0, vpart, lane, mx, s);
-      }
-    } else {
-#pragma unroll
-      for (int fn = 0; fn < TR::FN; ++fn) {
-        Acc mx, s;
-        column_lse<TR, true>(acc, fn, lane, lim, mx, s);
-        emit(acc, fn, tcol + fn * TR::MF, vrow0, vpart, lane, mx, s);
-      }
-    }
+    if (lim == TR::WTM) body<false>(acc, tcol, vpart, lane, lim);
+    else body<true>(acc, tcol, vpart, lane, lim);
   }
 };
+
+// zy[t] = <H[t], W[y_t]> for every token: one wave per token, lane-strided
+// partial sums in the accumulator type and a fixed shuffle tree.
+template <class TR>
+__global__ void target_logit_kernel(const typename TR::E *H, const typename TR::E *W,
+                                    const int64_t *y, int64_t n, int64_t D,
+                                    typename TR::Acc *zy, const int32_t *bad) {
+  typedef typename TR::Acc Acc;
+  if (*bad) return;
+  const int lane = threadIdx.x & 63;
+  const int64_t t = int64_t(blockIdx.x) * (blockDim.x >> 6) + (threadIdx.x >> 6);
+  if (t >= n) return;
+  const typename TR::E *h = H + t * D;
+  const typename TR::E *w = W + y[t] * D;
+  Acc s = 0;
+  for (int64_t d = lane; d < D; d += 64) s += to_acc<TR>(h[d]) * to_acc<TR>(w[d]);
+  for (int o = 32; o > 0; o >>= 1) s += __shfl_down(s, o);
+  if (lane == 0) zy[t] = s;
+}
 
 // One wave per token: fold the token's (max, sum) pairs in a fixed order.
 template <class Acc>
@@ -281,6 +260,77 @@ __global__ void fwd_final_kernel(const double *loss_tok, const Acc *lse, const u
 
 // ----------------------------------------------------- backward epilogues --
 
+// LDS-staged output of one wave's 128x128 fp32-accumulated tile (bf16 core).
+// Rows of the 32x32x16 accumulator layout are spread over lanes in steps of
+// four, so storing straight from registers costs one narrow access per value.
+// Instead each 32-row block goes to a private LDS region (value xf(fm, fn, r,
+// row) at [row][col]) and comes back as 16-byte row chunks, which are stored
+// (or added to memory) with one dwordx4 access each: 16 lanes cover 256
+// contiguous bytes of one output row.  Row pitches of 128 + 8 fp32 / 128 + 8
+// bf16 values keep the writes (lanes 32..63 hold rows four below lanes
+// 0..31) and the row-chunk reads free of bank conflicts.
+//   ptr(row, col): destination of the chunk at wave-tile (row, col), or
+//                  nullptr to skip it (outside the output);
+//   patch(fm, region): runs after block fm is written, before it is read
+//                  back (may overwrite single staged values).
+template <class T, bool ACCUM, class Xf, class Ptr, class Patch>
+__device__ __forceinline__ void staged_tile(const TraitsBF16::AccBlock (&acc)[4][4], char *region,
+                                            int lane, const Xf &xf, const Ptr &ptr,
+                                            const Patch &patch) {
+  constexpr int ES = int(sizeof(T));
+  constexpr int PITCH = (128 + 8) * ES;           // bytes per staged row
+  constexpr int CPR = 128 * ES / 16;              // 16-byte chunks per row
+  constexpr int NR = 32 * CPR / 64;               // chunk reads per lane per block
+  constexpr int EPC = 16 / ES;                    // values per chunk
+  static_assert(!ACCUM || ES == 4, "accumulation is fp32");
+#pragma unroll
+  for (int fm = 0; fm < 4; ++fm) {
+#pragma unroll
+    for (int fn = 0; fn < 4; ++fn)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int row = (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
+        const int col = fn * 32 + (lane & 31);
+        *reinterpret_cast<T *>(region + row * PITCH + col * ES) = xf(fm, fn, r, fm * 32 + row);
+      }
+    patch(fm, region);
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    u32x4 d[NR];
+    T *dst[NR];
+#pragma unroll
+    for (int i = 0; i < NR; ++i) {
+      const int q = i * 64 + lane;
+      const int row = q / CPR, c = q % CPR;
+      d[i] = *reinterpret_cast<const u32x4 *>(region + row * PITCH + c * 16);
+      dst[i] = ptr(fm * 32 + row, c * EPC);
+    }
+    if constexpr (ACCUM) {
+      u32x4 old[NR];
+#pragma unroll
+      for (int i = 0; i < NR; ++i)
+        old[i] = dst[i] ? *reinterpret_cast<const u32x4 *>(dst[i]) : u32x4{0, 0, 0, 0};
+#pragma unroll
+      for (int i = 0; i < NR; ++i) {
+        if (!dst[i]) continue;
+        u32x4 o;
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          o[j] = __float_as_uint(__uint_as_float(old[i][j]) + __uint_as_float(d[i][j]));
+        *reinterpret_cast<u32x4 *>(dst[i]) = o;
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < NR; ++i)
+        if (dst[i]) *reinterpret_cast<u32x4 *>(dst[i]) = d[i];
+    }
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    __builtin_amdgcn_sched_barrier(0);   // one block's registers at a time
+  }
+}
+
+// Bytes of LDS one wave's staging region takes.
+template <class T> constexpr int staged_region_bytes() { return 32 * (128 + 8) * int(sizeof(T)); }
+
 // Recomputed Z^T tile of a vocabulary slab -> logit gradient, stored
 // [slab row][token] in the input dtype.
 template <class TR>
@@ -296,6 +346,7 @@ struct DlogitEpi {
   double grad_out, z_coef;
   typename TR::E *dbuf;
   int64_t d_ld;
+  const Acc *zy;   // target logits (staged path)
 
   template <bool CHECK>
   __device__ __forceinline__ void body(const typename TR::AccBlock (&acc)[TR::FM][TR::FN],
@@ -303,7 +354,17 @@ struct DlogitEpi {
 #pragma unroll
     for (int fn = 0; fn < TR::FN; ++fn) {
       const int64_t t = tw0 + fn * TR::MF + TR::col_of(lane);
-      if (CHECK && t >= n) continue;
+      if (CHECK && t >= d_ld) continue;
+      if (CHECK && t >= n) {  // K padding of the d_weight product
+#pragma unroll
+        for (int fm = 0; fm < TR::FM; ++fm)
+#pragma unroll
+          for (int r = 0; r < TR::R; ++r) {
+            const int vr = fm * TR::MF + TR::row_of(r, lane);
+            if (vw0 + vr < rows) dbuf[(vw0 + vr) * d_ld + t] = to_elem<TR>(Acc(0));
+          }
+        continue;
+      }
       const Acc l = lse[t];
       const bool counted = !mask || mask[t];
       const Acc coef = counted ? g + Acc(2) * gz * l : Acc(0);
@@ -334,6 +395,63 @@ struct DlogitEpi {
     if (vw0 >= rows || tw0 >= n) return;
     if (vw0 + TR::WTM <= rows && tw0 + TR::WTN <= n) body<false>(acc, vw0, tw0, lane, g, gz);
     else body<true>(acc, vw0, tw0, lane, g, gz);
+  }
+
+  // bf16 core: the same values through LDS.  Token columns in [n, d_ld) get
+  // zeros (they are the K padding of the d_weight GEMM).
+  static constexpr bool kStaged = true;
+  __device__ __forceinline__ void staged(typename TR::AccBlock (&acc)[TR::FM][TR::FN], int64_t m0,
+                                         int64_t n0, int wm, int wn, int lane, int,
+                                         char *lds) const {
+    static_assert(std::is_same<TR, TraitsBF16>::value, "staged epilogue is bf16");
+    const int64_t C = ctl->count;
+    const Acc g = C ? Acc(grad_out / double(C)) : Acc(0);
+    const Acc gz = C ? Acc(z_coef * grad_out / double(C)) : Acc(0);
+    const int64_t vw0 = m0 + int64_t(wm) * TR::WTM;
+    const int64_t tw0 = n0 + int64_t(wn) * TR::WTN;
+    if (vw0 >= rows || tw0 >= d_ld) return;  // wave-uniform
+    // d = coef * exp(z - lse) - g [v == y] = s exp2(z log2(e) + c2) - g [v == y]
+    // with c2 = log2|coef| - lse log2(e) and s the sign of coef (coef 0 gives
+    // exp2(-inf) = 0; a negative coef needs grad_out < 0 or lse < -1/(2 z)).
+    const float L2E = 1.4426950408889634f;
+    float c2[TR::FN], gy[TR::FN];
+    uint32_t sb[TR::FN];
+    int yl[TR::FN];
+#pragma unroll
+    for (int fn = 0; fn < TR::FN; ++fn) {
+      const int64_t t = tw0 + fn * TR::MF + TR::col_of(lane);
+      const bool live = t < n;
+      const bool counted = live && (!mask || mask[t]);
+      const float l = live ? lse[t] : 0.f;
+      const float coef = counted ? g + 2.f * gz * l : 0.f;
+      c2[fn] = __builtin_amdgcn_logf(fabsf(coef)) - l * L2E;
+      sb[fn] = __float_as_uint(coef) & 0x80000000u;
+      // the target element, from the separately computed target logit
+      const int64_t yr = live ? targets[t] - (vs0 + vw0) : -1;
+      yl[fn] = (yr >= 0 && yr < TR::WTM && vw0 + yr < rows) ? int(yr) : -1;
+      const float ey = __uint_as_float(
+          __float_as_uint(__builtin_amdgcn_exp2f(fmaf(live ? zy[t] : 0.f, L2E, c2[fn]))) ^ sb[fn]);
+      gy[fn] = ey - (counted ? g : 0.f);
+    }
+    char *region = lds + (wm * 2 + wn) * staged_region_bytes<uint16_t>();
+    staged_tile<uint16_t, false>(
+        acc, region, lane,
+        [&](int fm, int fn, int r, int) -> uint16_t {
+          const float e = __builtin_amdgcn_exp2f(fmaf(acc[fm][fn][r], L2E, c2[fn]));
+          return to_elem<TR>(__uint_as_float(__float_as_uint(e) ^ sb[fn]));
+        },
+        [&](int vr, int tc) -> uint16_t * {
+          const int64_t v = vw0 + vr, t = tw0 + tc;
+          return (v < rows && t < d_ld) ? dbuf + v * d_ld + t : nullptr;
+        },
+        [&](int fm, char *blk) {
+          // overwrite the target element of each column that has it here
+#pragma unroll
+          for (int fn = 0; fn < TR::FN; ++fn)
+            if (lane < 32 && yl[fn] >= fm * 32 && yl[fn] < fm * 32 + 32)
+              *reinterpret_cast<uint16_t *>(blk + (yl[fn] - fm * 32) * ((128 + 8) * 2) +
+                                            (fn * 32 + lane) * 2) = to_elem<TR>(gy[fn]);
+        });
   }
 };
 
@@ -380,16 +498,47 @@ struct StoreEpi {
     if (rw0 + TR::WTM <= rows && cw0 + TR::WTN <= cols) body<false>(acc, o, rw0, cw0, lane);
     else body<true>(acc, o, rw0, cw0, lane);
   }
+
+  // bf16 core: through LDS, 16-byte accesses (cols and ldo multiples of 4,
+  // `out` 16-byte aligned; the host checks).
+  static constexpr bool kStaged = true;
+  __device__ __forceinline__ void staged(typename TR::AccBlock (&acc)[TR::FM][TR::FN], int64_t m0,
+                                         int64_t n0, int wm, int wn, int lane, int split,
+                                         char *lds) const {
+    static_assert(std::is_same<TR, TraitsBF16>::value, "staged epilogue is bf16");
+    Acc *o = out + int64_t(split) * split_stride;
+    const int64_t rw0 = m0 + int64_t(wm) * TR::WTM;
+    const int64_t cw0 = n0 + int64_t(wn) * TR::WTN;
+    if (rw0 >= rows || cw0 >= cols) return;  // wave-uniform
+    char *region = lds + (wm * 2 + wn) * staged_region_bytes<float>();
+    staged_tile<float, ACCUM>(
+        acc, region, lane, [&](int fm, int fn, int r, int) -> float { return acc[fm][fn][r]; },
+        [&](int rr, int cc) -> float * {
+          const int64_t row = rw0 + rr, c = cw0 + cc;
+          return (row < rows && c < cols) ? o + (row_off + row) * ldo + c : nullptr;
+        },
+        [](int, char *) {});
+  }
 };
 
-// Zero the token columns [n, d_ld) of every slab-buffer row: the pipelined
-// d_weight GEMM reads K in steps of 32 and relies on them being zero.
-template <class E>
-__global__ void zero_pad_kernel(E *dbuf, int64_t rows, int64_t d_ld, int64_t n) {
-  const int64_t w = d_ld - n;
-  for (int64_t i = int64_t(blockIdx.x) * blockDim.x + threadIdx.x; i < rows * w;
-       i += int64_t(gridDim.x) * blockDim.x)
-    dbuf[(i / w) * d_ld + n + i % w] = E(0);
+// Ht[d][t] = H[t][d] for t < n, 0 for n <= t < ld (bf16 bits).  64x64 tiles
+// through LDS; blockDim 256.
+__global__ void transpose_h_kernel(const uint16_t *H, int64_t n, int64_t D, uint16_t *Ht,
+                                   int64_t ld) {
+  __shared__ uint16_t tile[64][66];
+  const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;
+  const int64_t t0 = int64_t(blockIdx.x) * 64, d0 = int64_t(blockIdx.y) * 64;
+#pragma unroll
+  for (int j = 0; j < 16; ++j) {
+    const int64_t t = t0 + ty + 4 * j, d = d0 + tx;
+    tile[ty + 4 * j][tx] = (t < n && d < D) ? H[t * D + d] : uint16_t(0);
+  }
+  __syncthreads();
+#pragma unroll
+  for (int j = 0; j < 16; ++j) {
+    const int64_t d = d0 + ty + 4 * j, t = t0 + tx;
+    if (d < D && t < ld) Ht[d * ld + t] = tile[tx][ty + 4 * j];
+  }
 }
 
 // d_hidden = sum over splits (ascending) of the split accumulators.
@@ -441,40 +590,46 @@ static void launch_gemm(bool vec, const GemmParams &g, int64_t splits, const Epi
     hipLaunchKernelGGL((gemm_kernel<TR, AK, BKM, false, Epi>), grid, dim3(TR::NT), 0, st, g, epi);
 }
 
-template <bool AK, bool BKM, class Epi>
-static void launch_gemm2(const Gemm2Params &g, int64_t splits, const Epi &epi, hipStream_t st) {
-  const int64_t tiles = cdiv(g.M, Pipe::BM) * g.tiles_n;
-  const dim3 grid{unsigned(tiles), unsigned(splits), 1u};
-  hipLaunchKernelGGL((gemm2_kernel<Pipe, AK, BKM, Epi>), grid, dim3(Pipe::NT), 0, st, g, epi);
-}
+// Pipelined-core stage configurations: K-major x K-major products keep four
+// stages of k 32 (the deeper ring hides more load latency); products with
+// MN-major operands take two stages of k 64 (fewer transposed-read rounds and
+// barriers per k).
+typedef PipeCfg<32, 4> PipeKK;
+typedef PipeCfg<64, 2> PipeMN;
 
-static Gemm2Params to2(const GemmParams &g) {
-  Gemm2Params r;
-  r.A = g.A; r.lda = g.lda; r.B = g.B; r.ldb = g.ldb;
-  r.M = g.M; r.N = g.N; r.K = g.K; r.M_read = g.M_read; r.N_read = g.N_read;
-  r.k_per_split = (g.k_per_split + Pipe::BK - 1) / Pipe::BK * Pipe::BK;
-  r.tiles_n = g.tiles_n; r.bad = g.bad;
-  return r;
+template <class CFG, bool AK, bool BKM, class Epi>
+static void launch_gemm2(const GemmParams &g0, int64_t splits, const Epi &epi, hipStream_t st) {
+  Gemm2Params g;
+  g.A = g0.A; g.lda = g0.lda; g.B = g0.B; g.ldb = g0.ldb;
+  g.M = g0.M; g.N = g0.N; g.K = g0.K; g.M_read = g0.M_read; g.N_read = g0.N_read;
+  g.k_per_split = (g0.k_per_split + CFG::BK - 1) / CFG::BK * CFG::BK;
+  g.tiles_n = g0.tiles_n; g.bad = g0.bad;
+  const int64_t tiles = cdiv(g.M, CFG::BM) * g.tiles_n;
+  const dim3 grid{unsigned(tiles), unsigned(splits), 1u};
+  hipLaunchKernelGGL((gemm2_kernel<CFG, AK, BKM, Epi>), grid, dim3(CFG::NT), 0, st, g, epi);
 }
 
 // The pipelined bf16 core applies when every operand is 16-byte aligned with
-// leading dimensions that are multiples of 8 and d_model is a multiple of the
-// pipeline's k-step.
+// leading dimensions that are multiples of 8, d_model is a multiple of the
+// K-major configuration's k-step (K-major operands are read in whole steps)
+// and 256 rows of any operand span less than 2 GiB (buffer offsets are 32-bit).
 template <class TR> struct UsePipe { static bool ok(bool, int64_t, int64_t) { return false; } };
 template <> struct UsePipe<TraitsBF16> {
   static bool ok(bool vec, int64_t D, int64_t d_ld) {
-    return vec && D % Pipe::BK == 0 && 256 * D * 2 < (int64_t(1) << 31) &&
+    return vec && D % PipeKK::BK == 0 && 256 * D * 2 < (int64_t(1) << 31) &&
            256 * d_ld * 2 < (int64_t(1) << 31);
   }
 };
 
-// bf16 with `pipe`: the pipelined core; otherwise the generic one.
+// bf16 with `pipe`: the pipelined core (both operands K-major: PipeKK, else
+// PipeMN); otherwise the generic one.
 template <class TR, bool AK, bool BKM, class Epi>
 static void launch_any(bool pipe, bool vec, const GemmParams &g, int64_t splits, const Epi &epi,
                        hipStream_t st) {
   if constexpr (std::is_same<TR, TraitsBF16>::value) {
     if (pipe) {
-      launch_gemm2<AK, BKM>(to2(g), splits, epi, st);
+      if constexpr (AK && BKM) launch_gemm2<PipeKK, AK, BKM>(g, splits, epi, st);
+      else launch_gemm2<PipeMN, AK, BKM>(g, splits, epi, st);
       return;
     }
   }
@@ -501,6 +656,12 @@ static void forward_impl(const CEPlan &p, const void *H, const void *W, const in
   double *loss_tok = reinterpret_cast<double *>(ws + p.off_losstok);
   const typename TR::E *Hp = static_cast<const typename TR::E *>(H);
   launch_guard(y, mask, p.n, p.V, ctl, st, tm);
+  {
+    TimedLaunch tl(tm, LCE_K_FWD_MERGE, st);
+    hipLaunchKernelGGL(target_logit_kernel<TR>, dim3(unsigned(cdiv(p.n, 4))), dim3(256), 0, st,
+                       Hp, static_cast<const typename TR::E *>(W), y, p.n, p.D, zy,
+                       (const int32_t *)&ctl->bad);
+  }
   for (int64_t tok0 = 0; tok0 < p.n; tok0 += p.tok_per_pass) {
     const int64_t ntok = p.tok_per_pass < p.n - tok0 ? p.tok_per_pass : p.n - tok0;
     GemmParams g;
@@ -511,7 +672,7 @@ static void forward_impl(const CEPlan &p, const void *H, const void *W, const in
     g.k_per_split = cdiv(p.D, TR::BK) * TR::BK;
     g.tiles_n = cdiv(ntok, TR::BN);
     g.bad = &ctl->bad;
-    FwdLseEpi<TR> epi{y + tok0, ntok, p.V, p.n_vparts, partials, zy + tok0};
+    FwdLseEpi<TR> epi{ntok, p.V, p.n_vparts, partials};
     {
       TimedLaunch tl(tm, LCE_K_FWD_GEMM, st);
       launch_any<TR, true, true>(UsePipe<TR>::ok(vec, p.D, p.d_ld), vec, g, 1, epi, st);
@@ -541,11 +702,21 @@ static void backward_impl(const CEPlan &p, const void *H, const void *W, const i
   const E *Wp = static_cast<const E *>(W);
   launch_guard(y, mask, p.n, p.V, ctl, st, tm);
   const bool pipe = UsePipe<TR>::ok(vec, p.D, p.d_ld);
-  if (pipe && p.d_ld > p.n) {
-    int64_t blocks = cdiv(p.slab * (p.d_ld - p.n), 256);
-    if (blocks > 1024) blocks = 1024;
-    hipLaunchKernelGGL(zero_pad_kernel<E>, dim3(unsigned(blocks)), dim3(256), 0, st, dbuf, p.slab,
-                       p.d_ld, p.n);
+  E *Ht = nullptr;
+  Acc *zyb = nullptr;
+  if constexpr (std::is_same<TR, TraitsBF16>::value) {
+    if (pipe) {
+      // K-major operands of the d_weight product: H^T and the slab buffer,
+      // both zero in token columns [n, d_ld).
+      // (The staged logit-gradient epilogue writes the slab buffer's zeros.)
+      Ht = reinterpret_cast<E *>(ws + p.off_ht);
+      const dim3 tg{unsigned(cdiv(p.d_ld, 64)), unsigned(cdiv(p.D, 64)), 1u};
+      hipLaunchKernelGGL(transpose_h_kernel, tg, dim3(256), 0, st, Hp, p.n, p.D, Ht, p.d_ld);
+      // target logits for the staged logit-gradient epilogue
+      zyb = reinterpret_cast<Acc *>(ws + p.off_zyb);
+      hipLaunchKernelGGL(target_logit_kernel<TR>, dim3(unsigned(cdiv(p.n, 4))), dim3(256), 0, st,
+                         Hp, Wp, y, p.n, p.D, zyb, (const int32_t *)&ctl->bad);
+    }
   }
   for (int64_t s = 0; s < p.n_slabs; ++s) {
     const int64_t vs0 = s * p.slab;
@@ -560,24 +731,32 @@ static void backward_impl(const CEPlan &p, const void *H, const void *W, const i
       g.k_per_split = cdiv(p.D, TR::BK) * TR::BK;
       g.tiles_n = cdiv(p.n, TR::BN);
       g.bad = &ctl->bad;
-      DlogitEpi<TR> epi{y, mask, lse, p.n, vs0, rows, ctl, grad_out, z_coef, dbuf, p.d_ld};
+      DlogitEpi<TR> epi{y, mask, lse, p.n, vs0, rows, ctl, grad_out, z_coef, dbuf, p.d_ld, zyb};
       TimedLaunch tl(tm, LCE_K_DLOGIT_GEMM, st);
       launch_any<TR, true, true>(pipe, vec, g, 1, epi, st);
     }
     {  // d_weight rows of the slab = d^T H over all tokens
       GemmParams g;
       g.A = dbuf; g.lda = p.d_ld;
-      g.B = Hp; g.ldb = p.D;
       g.M = rows; g.N = p.D; g.K = p.n;
-      g.M_read = rows; g.N_read = p.D;   // H rows are D long
+      g.M_read = rows;
       g.k_per_split = cdiv(p.n, TR::BK) * TR::BK;
       g.tiles_n = cdiv(p.D, TR::BN);
       g.bad = &ctl->bad;
       TimedLaunch tl(tm, LCE_K_DW_GEMM, st);
       const StoreEpi<TR, true> e_acc{dW, p.D, vs0, rows, p.D, 0};
       const StoreEpi<TR, false> e_set{dW, p.D, vs0, rows, p.D, 0};
-      if (accumulate) launch_any<TR, true, false>(pipe, vec, g, 1, e_acc, st);
-      else launch_any<TR, true, false>(pipe, vec, g, 1, e_set, st);
+      if (pipe) {  // B = H^T, K-major like the slab buffer
+        g.B = Ht; g.ldb = p.d_ld;
+        g.N_read = p.D;
+        if (accumulate) launch_any<TR, true, true>(pipe, vec, g, 1, e_acc, st);
+        else launch_any<TR, true, true>(pipe, vec, g, 1, e_set, st);
+      } else {     // B = H read MN-major (rows D long)
+        g.B = Hp; g.ldb = p.D;
+        g.N_read = p.D;
+        if (accumulate) launch_gemm<TR, true, false>(vec, g, 1, e_acc, st);
+        else launch_gemm<TR, true, false>(vec, g, 1, e_set, st);
+      }
     }
     {  // d_hidden split accumulators += d W_slab
       const int64_t kps = cdiv(cdiv(rows, p.dh_splits), TR::BK) * TR::BK;
@@ -751,7 +930,9 @@ int32_t lce_backward_timed(const lce_tensor *hidden, const lce_tensor *weight,
   const int64_t *y = static_cast<const int64_t *>(targets->data);
   (void)hipGetLastError();
   if (dt == LCE_BF16) {
-    const bool vec = d_model % 8 == 0 && aligned16(hidden->data) && aligned16(weight->data);
+    // the staged d_weight epilogue writes 16-byte chunks
+    const bool vec = d_model % 8 == 0 && aligned16(hidden->data) && aligned16(weight->data) &&
+                     aligned16(d_weight->data);
     backward_impl<TraitsBF16>(p, hidden->data, weight->data, y, mask,
                               static_cast<const float *>(lse->data), z_coef, grad_out,
                               static_cast<uint16_t *>(d_hidden->data),

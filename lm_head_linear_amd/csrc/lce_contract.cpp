@@ -53,32 +53,59 @@ int32_t plan_ce(int64_t n, int64_t D, int64_t V, int64_t chunk, int32_t dtype, C
   q.tok_per_pass = tpp < n ? tpp : n;
 
   // Backward: the logit-gradient buffer holds a slab of vocabulary rows for
-  // every token, at most chunk*vocab cells; slabs are balanced in size.
+  // every token, at most chunk*vocab cells.
   q.d_ld = round_up(n, 64);
   int64_t slab_max = budget / q.d_ld;
-  if (slab_max >= tile_m) slab_max = slab_max / tile_m * tile_m;
-  else if (slab_max >= 32) slab_max = slab_max / 32 * 32;
-  if (slab_max < 1) slab_max = 1;
-  if (slab_max >= V) {
-    q.slab = V;
-    q.n_slabs = 1;
-  } else {
-    q.n_slabs = ceil_div(V, slab_max);
-    int64_t gran = slab_max >= tile_m ? tile_m : (slab_max >= 32 ? 32 : 1);
-    int64_t bal = round_up(ceil_div(V, q.n_slabs), gran);
-    q.slab = bal <= slab_max ? bal : slab_max;
-    q.n_slabs = ceil_div(V, q.slab);
-  }
-  // Split the vocabulary reduction of d_hidden so that the grid has about one
-  // workgroup per compute unit (256), keeping each split at least 512 deep.
   const int64_t tile_n = bf ? 256 : 128;
-  int64_t out_tiles = ceil_div(n, tile_m) * ceil_div(D, tile_n);
-  int64_t splits = ceil_div(256, out_tiles);
-  int64_t max_by_depth = q.slab / 512;
-  if (splits > max_by_depth) splits = max_by_depth;
-  if (splits > 16) splits = 16;
-  if (splits < 1) splits = 1;
-  q.dh_splits = splits;
+  const int64_t out_tiles = ceil_div(n, tile_m) * ceil_div(D, tile_n);
+  // Split the vocabulary reduction of d_hidden so that the grid has about one
+  // workgroup per compute unit, keeping each split at least 512 deep.
+  auto dh_splits_for = [&](int64_t slab) {
+    int64_t sp = ceil_div(kComputeUnits, out_tiles);
+    if (sp > slab / 512) sp = slab / 512;
+    if (sp > 16) sp = 16;
+    return sp < 1 ? int64_t(1) : sp;
+  };
+  if (bf && slab_max >= tile_m) {
+    // bf16: one 256x256 tile per compute unit per round, so a launch costs
+    // about (rounds of tiles) x (depth + epilogue).  Pick the slab (a multiple
+    // of 256 rows) with the lowest modelled total over the three backward
+    // GEMMs of every slab; ties go to the larger slab.
+    slab_max = slab_max / tile_m * tile_m;
+    if (slab_max > round_up(V, tile_m)) slab_max = round_up(V, tile_m);
+    const int64_t tn = ceil_div(n, tile_m), td = ceil_div(D, tile_n);
+    const int64_t kEpi = 256, kLaunch = 64;
+    auto rounds = [&](int64_t wgs) { return ceil_div(wgs, kComputeUnits); };
+    auto slab_cost = [&](int64_t rows, int64_t sp) {
+      const int64_t tm = ceil_div(rows, tile_m);
+      return rounds(tm * tn) * (D + kEpi) + rounds(tm * td) * (n + kEpi) +
+             rounds(out_tiles * sp) * (ceil_div(rows, sp) + kEpi) + 3 * kLaunch;
+    };
+    int64_t best = -1, best_cost = 0;
+    for (int64_t S = tile_m; S <= slab_max; S += tile_m) {
+      const int64_t ns = ceil_div(V, S);
+      const int64_t sp = dh_splits_for(S);
+      const int64_t c = (ns - 1) * slab_cost(S, sp) + slab_cost(V - (ns - 1) * S, sp);
+      if (best < 0 || c <= best_cost) { best = S; best_cost = c; }
+    }
+    q.slab = best < V ? best : V;
+    q.n_slabs = ceil_div(V, q.slab);
+  } else {
+    if (slab_max >= tile_m) slab_max = slab_max / tile_m * tile_m;
+    else if (slab_max >= 32) slab_max = slab_max / 32 * 32;
+    if (slab_max < 1) slab_max = 1;
+    if (slab_max >= V) {
+      q.slab = V;
+      q.n_slabs = 1;
+    } else {  // balanced slabs
+      q.n_slabs = ceil_div(V, slab_max);
+      int64_t gran = slab_max >= tile_m ? tile_m : (slab_max >= 32 ? 32 : 1);
+      int64_t bal = round_up(ceil_div(V, q.n_slabs), gran);
+      q.slab = bal <= slab_max ? bal : slab_max;
+      q.n_slabs = ceil_div(V, q.slab);
+    }
+  }
+  q.dh_splits = dh_splits_for(q.slab);
 
   // Workspace: [control | forward partials | zy | per-token loss] and the
   // backward's [slab buffer | d_hidden split accumulators] overlap the
@@ -97,6 +124,10 @@ int32_t plan_ce(int64_t n, int64_t D, int64_t V, int64_t chunk, int32_t dtype, C
   off = align256(off + size_t(q.slab) * size_t(q.d_ld) * q.elem);
   q.off_dhacc = off;
   off = align256(off + size_t(q.dh_splits) * size_t(n) * size_t(D) * q.acc);
+  q.off_ht = off;
+  if (bf) off = align256(off + size_t(D) * size_t(q.d_ld) * q.elem);
+  q.off_zyb = off;
+  if (bf) off = align256(off + size_t(n) * q.acc);
   q.total = off > fwd_end ? off : fwd_end;
   *p = q;
   return LCE_OK;

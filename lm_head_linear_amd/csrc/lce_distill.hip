@@ -44,16 +44,18 @@ template <> struct IO<uint16_t> {  // bf16 bits
     }
   }
   __device__ static inline float load1(const uint16_t *p) { return __uint_as_float(uint32_t(*p) << 16); }
+  // round to nearest even (v_cvt_pk_bf16_f32; NaN stays NaN)
   __device__ static inline uint16_t cvt(float f) {
-    uint32_t u = __float_as_uint(f);
-    if ((u & 0x7fffffffu) > 0x7f800000u) return uint16_t((u >> 16) | 0x40);
-    u += 0x7fffu + ((u >> 16) & 1u);
-    return uint16_t(u >> 16);
+    return __builtin_bit_cast(uint16_t, static_cast<__bf16>(f));
   }
   __device__ static inline void store8(uint16_t *p, const float *g) {
+    typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
     u32x4 v;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) v[i] = uint32_t(cvt(g[2 * i])) | (uint32_t(cvt(g[2 * i + 1])) << 16);
+    for (int i = 0; i < 4; ++i) {
+      const bf16x2_t h = {static_cast<__bf16>(g[2 * i]), static_cast<__bf16>(g[2 * i + 1])};
+      v[i] = __builtin_bit_cast(uint32_t, h);
+    }
     *reinterpret_cast<u32x4 *>(p) = v;
   }
   __device__ static inline void store1(uint16_t *p, float g) { *p = cvt(g); }

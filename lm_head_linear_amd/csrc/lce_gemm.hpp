@@ -82,11 +82,9 @@ __device__ inline int64_t xcd_remap(int64_t b, int64_t nb) {
 
 // ------------------------------------------------------------ bf16 / f64 --
 
+// Round to nearest even (v_cvt_pk_bf16_f32 on gfx950; NaN stays NaN).
 __device__ inline uint16_t f32_to_bf16_rne(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7fffffffu) > 0x7f800000u) return uint16_t((u >> 16) | 0x40);  // NaN stays NaN
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return uint16_t(u >> 16);
+  return __builtin_bit_cast(uint16_t, static_cast<__bf16>(f));
 }
 __device__ inline float bf16_to_f32(uint16_t h) { return __uint_as_float(uint32_t(h) << 16); }
 

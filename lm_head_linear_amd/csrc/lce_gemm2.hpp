@@ -17,8 +17,11 @@
 //     operand reads free of LDS bank conflicts;
 //   * operand fragments are double-buffered in registers: the MFMAs of one
 //     k-substep run while the next substep's fragments are read, and the
-//     stage barrier sits between the two substeps, so LDS latency and the DMA
-//     issue hide behind MFMA work.
+//     stage barrier sits between the last two substeps, so LDS latency and the
+//     DMA issue hide behind MFMA work;
+//   * an epilogue with kStaged set gets the LDS ring (after a barrier) as
+//     staging space for its output tile (staged()); otherwise operator() runs
+//     straight from the accumulators.
 // Requirements (checked by the host): 16-byte aligned bases, leading
 // dimensions multiple of 8, K-major operands zero-padded (or exact) to a
 // multiple of 32 along K, 256 * ld * 2 bytes below 2^31.
@@ -302,7 +305,14 @@ __global__ void __launch_bounds__(CFG::NT) gemm2_kernel(Gemm2Params g, Epi epi) 
   int lane_e = lane, wm_e = wm, wn_e = wn;
   int64_t m0_e = m0, n0_e = n0;
   asm volatile("" : "+v"(lane_e), "+v"(wm_e), "+v"(wn_e), "+v"(m0_e), "+v"(n0_e));
-  epi(acc, m0_e, n0_e, wm_e, wn_e, lane_e, split);
+  if constexpr (Epi::kStaged) {
+    // The epilogue reuses the stage ring as staging space: every wave must be
+    // done reading its operand fragments first.
+    __syncthreads();
+    epi.staged(acc, m0_e, n0_e, wm_e, wn_e, lane_e, split, smem);
+  } else {
+    epi(acc, m0_e, n0_e, wm_e, wn_e, lane_e, split);
+  }
 }
 
 }  // namespace lce

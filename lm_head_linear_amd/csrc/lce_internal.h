@@ -25,6 +25,7 @@ constexpr size_t kControlBytes = 256;
 
 // Tile geometry the host planner needs (kept equal to the device traits).
 constexpr int64_t kBf16TileM = 256;   // vocabulary rows per GEMM tile (bf16)
+constexpr int64_t kComputeUnits = 256; // compute units of an MI355X (gfx950): one tile each per round
 constexpr int64_t kBf16WaveM = 128;   // rows per forward partial (bf16)
 constexpr int64_t kF64TileM = 128;
 constexpr int64_t kF64WaveM = 64;
@@ -47,6 +48,8 @@ struct CEPlan {
   // workspace layout (byte offsets)
   size_t off_partials = 0, off_zy = 0, off_losstok = 0;
   size_t off_dbuf = 0, off_dhacc = 0;
+  size_t off_ht = 0;          // bf16: H^T [D][d_ld] (zero past n); 0 bytes for fp64
+  size_t off_zyb = 0;         // bf16: target logits for the backward; 0 bytes for fp64
   size_t total = 0;
 };
 
