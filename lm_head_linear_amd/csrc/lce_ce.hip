@@ -399,39 +399,73 @@ struct DlogitEpi {
 
   // bf16 core: the same values through LDS.  Token columns in [n, d_ld) get
   // zeros (they are the K padding of the d_weight GEMM).
+  //   d = coef * exp(z - lse) - g [v == y] = s exp2(z log2(e) + c2) - g [v == y]
+  // with c2 = log2|coef| - lse log2(e) and s the sign of coef (coef 0 gives
+  // exp2(-inf) = 0; a negative coef needs grad_out < 0 or lse < -1/(2 z)).
+  // The target element comes from the separately computed target logit.
+  // Per-token inputs are loaded before the main loop; after it, per-token
+  // constants {c2, sign bit, target row - tile row, d at the target} go
+  // through LDS to the lanes that hold each column.
   static constexpr bool kStaged = true;
+  static constexpr int kPrefetchBytes = 256 * 16;
+  struct Pre {
+    float l, z;
+    int32_t y;    // targets < 2^24
+    uint32_t mk;  // mask byte (any value when there is no mask)
+  };
+  __device__ __forceinline__ Pre pre_load(int64_t, int64_t n0, int tid) const {
+    // unconditional loads (index clamped; pre_store ignores columns >= n) so
+    // that nothing waits on them before the operand loads issue
+    const int64_t t = n0 + tid < n ? n0 + tid : n - 1;
+    // without a mask any readable byte will do (pre_store ignores it)
+    const uint8_t *mp = mask ? mask : reinterpret_cast<const uint8_t *>(lse);
+    Pre q;
+    q.l = lse[t];
+    q.z = zy[t];
+    q.y = int32_t(targets[t]);
+    q.mk = mp[t];
+    return q;
+  }
+  __device__ __forceinline__ void pre_store(const Pre &q, int64_t m0, int64_t n0, int tid,
+                                            char *pre) const {
+    const float L2E = 1.4426950408889634f;
+    const int64_t C = ctl->count;
+    const float g = C ? float(grad_out / double(C)) : 0.f;
+    const float gz = C ? float(z_coef * grad_out / double(C)) : 0.f;
+    const bool live = n0 + tid < n;
+    const bool counted = live && (!mask || q.mk != 0);
+    const float coef = counted ? g + 2.f * gz * q.l : 0.f;
+    const float c2 = __builtin_amdgcn_logf(fabsf(coef)) - q.l * L2E;
+    const uint32_t sb = __float_as_uint(coef) & 0x80000000u;
+    const int64_t yr = live ? int64_t(q.y) - (vs0 + m0) : -1;
+    const float ey = __uint_as_float(__float_as_uint(__builtin_amdgcn_exp2f(fmaf(q.z, L2E, c2))) ^ sb);
+    u32x4 v;
+    v[0] = __float_as_uint(c2);
+    v[1] = sb;
+    v[2] = uint32_t(int32_t(yr >= 0 && yr < 256 ? yr : -1));
+    v[3] = __float_as_uint(ey - (counted ? g : 0.f));
+    *reinterpret_cast<u32x4 *>(pre + tid * 16) = v;
+  }
   __device__ __forceinline__ void staged(typename TR::AccBlock (&acc)[TR::FM][TR::FN], int64_t m0,
                                          int64_t n0, int wm, int wn, int lane, int,
-                                         char *lds) const {
+                                         char *lds, const char *pre) const {
     static_assert(std::is_same<TR, TraitsBF16>::value, "staged epilogue is bf16");
-    const int64_t C = ctl->count;
-    const Acc g = C ? Acc(grad_out / double(C)) : Acc(0);
-    const Acc gz = C ? Acc(z_coef * grad_out / double(C)) : Acc(0);
+    const float L2E = 1.4426950408889634f;
     const int64_t vw0 = m0 + int64_t(wm) * TR::WTM;
     const int64_t tw0 = n0 + int64_t(wn) * TR::WTN;
     if (vw0 >= rows || tw0 >= d_ld) return;  // wave-uniform
-    // d = coef * exp(z - lse) - g [v == y] = s exp2(z log2(e) + c2) - g [v == y]
-    // with c2 = log2|coef| - lse log2(e) and s the sign of coef (coef 0 gives
-    // exp2(-inf) = 0; a negative coef needs grad_out < 0 or lse < -1/(2 z)).
-    const float L2E = 1.4426950408889634f;
     float c2[TR::FN], gy[TR::FN];
     uint32_t sb[TR::FN];
     int yl[TR::FN];
 #pragma unroll
     for (int fn = 0; fn < TR::FN; ++fn) {
-      const int64_t t = tw0 + fn * TR::MF + TR::col_of(lane);
-      const bool live = t < n;
-      const bool counted = live && (!mask || mask[t]);
-      const float l = live ? lse[t] : 0.f;
-      const float coef = counted ? g + 2.f * gz * l : 0.f;
-      c2[fn] = __builtin_amdgcn_logf(fabsf(coef)) - l * L2E;
-      sb[fn] = __float_as_uint(coef) & 0x80000000u;
-      // the target element, from the separately computed target logit
-      const int64_t yr = live ? targets[t] - (vs0 + vw0) : -1;
-      yl[fn] = (yr >= 0 && yr < TR::WTM && vw0 + yr < rows) ? int(yr) : -1;
-      const float ey = __uint_as_float(
-          __float_as_uint(__builtin_amdgcn_exp2f(fmaf(live ? zy[t] : 0.f, L2E, c2[fn]))) ^ sb[fn]);
-      gy[fn] = ey - (counted ? g : 0.f);
+      const u32x4 q = *reinterpret_cast<const u32x4 *>(
+          pre + (wn * TR::WTN + fn * TR::MF + TR::col_of(lane)) * 16);
+      c2[fn] = __uint_as_float(q[0]);
+      sb[fn] = q[1];
+      const int yr = int(q[2]) - wm * TR::WTM;   // row within this wave's 128
+      yl[fn] = (int(q[2]) >= 0 && yr >= 0 && yr < TR::WTM && vw0 + yr < rows) ? yr : -1;
+      gy[fn] = __uint_as_float(q[3]);
     }
     char *region = lds + (wm * 2 + wn) * staged_region_bytes<uint16_t>();
     staged_tile<uint16_t, false>(
@@ -504,7 +538,7 @@ struct StoreEpi {
   static constexpr bool kStaged = true;
   __device__ __forceinline__ void staged(typename TR::AccBlock (&acc)[TR::FM][TR::FN], int64_t m0,
                                          int64_t n0, int wm, int wn, int lane, int split,
-                                         char *lds) const {
+                                         char *lds, const char *) const {
     static_assert(std::is_same<TR, TraitsBF16>::value, "staged epilogue is bf16");
     Acc *o = out + int64_t(split) * split_stride;
     const int64_t rw0 = m0 + int64_t(wm) * TR::WTM;

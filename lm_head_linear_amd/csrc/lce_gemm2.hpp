@@ -21,7 +21,8 @@
 //     DMA issue hide behind MFMA work;
 //   * an epilogue with kStaged set gets the LDS ring (after a barrier) as
 //     staging space for its output tile (staged()); otherwise operator() runs
-//     straight from the accumulators.
+//     straight from the accumulators.  kPrefetchBytes lets it load per-tile
+//     constants into LDS while the first stages are in flight.
 // Requirements (checked by the host): 16-byte aligned bases, leading
 // dimensions multiple of 8, K-major operands zero-padded (or exact) to a
 // multiple of 32 along K, 256 * ld * 2 bytes below 2^31.
@@ -37,9 +38,10 @@ typedef short shortx4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) void lds_void_t;
 typedef __attribute__((address_space(3))) shortx4 lds_shortx4_t;
 
-template <int BK_, int STAGES_>
+template <int BK_, int STAGES_, int AUX_ = 0>
 struct PipeCfg {
   static constexpr int BM = 256, BN = 256, BK = BK_, STAGES = STAGES_;
+  static constexpr int AUX = AUX_;                    // cache-policy bits of the operand loads
   static constexpr int NT = 256;
   static constexpr int KSUB = BK / 16;                // MFMA k-substeps per stage
   static constexpr int ROWB = BK * 2;                  // bytes per K-major tile row
@@ -71,8 +73,9 @@ __device__ inline __amdgpu_buffer_rsrc_t make_rsrc(const void *base, int64_t byt
 
 // One 16-byte-per-lane load from the buffer `rs` at byte offset `voff` into
 // LDS at `dst` + 16 * lane.
+template <int AUX>
 __device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t rs, char *dst, uint32_t voff) {
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void_t *)dst, 16, voff, 0, 0, 0);
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void_t *)dst, 16, voff, 0, 0, AUX);
 }
 
 // One operand of one stage: OP_BYTES / 1 KB wave-instructions, INSTR per wave.
@@ -116,7 +119,7 @@ struct PipeOperand {
 #pragma unroll
       for (int i = 0; i < CFG::INSTR; ++i) {
         const int j = wave * CFG::INSTR + i;
-        dma16(rs, dst + j * 1024, voff[i] + uint32_t(k0 * 2));
+        dma16<CFG::AUX>(rs, dst + j * 1024, voff[i] + uint32_t(k0 * 2));
       }
     } else {
       // base at (k0, row0): bytes up to the end of row k_lim-1's readable part
@@ -126,7 +129,7 @@ struct PipeOperand {
 #pragma unroll
       for (int i = 0; i < CFG::INSTR; ++i) {
         const int j = wave * CFG::INSTR + i;
-        dma16(r, dst + j * 1024, voff[i]);
+        dma16<CFG::AUX>(r, dst + j * 1024, voff[i]);
       }
     }
   }
@@ -187,6 +190,20 @@ __device__ inline void wait_vm_barrier_stages(int stages) {
   }
 }
 
+// Optional epilogue hooks: kStaged (staged() gets the LDS ring after the main
+// loop) and kPrefetchBytes (pre_load() runs before the first operand load and
+// its values stay in registers through the main loop, so their latency hides
+// behind it; pre_store() then writes per-tile constants to an LDS area of that
+// size past the ring, which staged() reads).
+template <class E, class = void> struct EpiStaged { static constexpr bool value = false; };
+template <class E>
+struct EpiStaged<E, std::void_t<decltype(E::kStaged)>> { static constexpr bool value = E::kStaged; };
+template <class E, class = void> struct EpiPrefetch { static constexpr int bytes = 0; };
+template <class E>
+struct EpiPrefetch<E, std::void_t<decltype(E::kPrefetchBytes)>> {
+  static constexpr int bytes = E::kPrefetchBytes;
+};
+
 template <class CFG, bool AK, bool BKM, class Epi>
 __global__ void __launch_bounds__(CFG::NT) gemm2_kernel(Gemm2Params g, Epi epi) {
   typedef TraitsBF16 TR;
@@ -194,7 +211,9 @@ __global__ void __launch_bounds__(CFG::NT) gemm2_kernel(Gemm2Params g, Epi epi) 
   constexpr int LPS = CFG::LOADS_PER_STAGE;
   static_assert(KSUB % 2 == 0 && KSUB >= 2, "fragment double-buffer parity");
   if (g.bad && *g.bad) return;
-  __shared__ __attribute__((aligned(1024))) char smem[STAGES * CFG::STAGE_BYTES];
+  constexpr int PRE = EpiPrefetch<Epi>::bytes;
+  __shared__ __attribute__((aligned(1024))) char smem[STAGES * CFG::STAGE_BYTES + PRE];
+  char *const pre_lds = smem + STAGES * CFG::STAGE_BYTES;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -222,6 +241,13 @@ __global__ void __launch_bounds__(CFG::NT) gemm2_kernel(Gemm2Params g, Epi epi) 
   PipeOperand<CFG, BKM> pb;
   pa.init(static_cast<const uint16_t *>(g.A), g.lda, m0, AK ? g.M : g.M_read, g.K, wave, lane);
   pb.init(static_cast<const uint16_t *>(g.B), g.ldb, n0, BKM ? g.N : g.N_read, g.K, wave, lane);
+
+  // Epilogue constants: loaded before the operands, consumed after the main
+  // loop (the last stage wait covers them).
+  [[maybe_unused]] auto pre = [&] {
+    if constexpr (PRE > 0) return epi.pre_load(m0, n0, tid);
+    else return 0;
+  }();
 
   // Prologue: every stage of the ring in flight; wait for stage 0 and read its
   // first k-substep fragments.
@@ -305,11 +331,15 @@ __global__ void __launch_bounds__(CFG::NT) gemm2_kernel(Gemm2Params g, Epi epi) 
   int lane_e = lane, wm_e = wm, wn_e = wn;
   int64_t m0_e = m0, n0_e = n0;
   asm volatile("" : "+v"(lane_e), "+v"(wm_e), "+v"(wn_e), "+v"(m0_e), "+v"(n0_e));
-  if constexpr (Epi::kStaged) {
+  if constexpr (EpiStaged<Epi>::value) {
     // The epilogue reuses the stage ring as staging space: every wave must be
     // done reading its operand fragments first.
     __syncthreads();
-    epi.staged(acc, m0_e, n0_e, wm_e, wn_e, lane_e, split, smem);
+    if constexpr (PRE > 0) {
+      epi.pre_store(pre, m0_e, n0_e, tid, pre_lds);
+      __syncthreads();
+    }
+    epi.staged(acc, m0_e, n0_e, wm_e, wn_e, lane_e, split, smem, pre_lds);
   } else {
     epi(acc, m0_e, n0_e, wm_e, wn_e, lane_e, split);
   }
