@@ -153,7 +153,10 @@ int64_t lce_distill_workspace_bytes(int64_t n_tok, int64_t vocab);
  *   lse_out   [n_tok] per-token log-sum-exp, LCE_F32 for bf16 inputs,
  *             LCE_F64 for fp64 inputs; lce_backward takes it back
  *   workspace LCE_U8, numel >= lce_workspace_bytes(...)
- *   out       host pointer; receives the scalars
+ *   out       host pointer; receives the scalars after the call synchronizes
+ *             the stream.  NULL: asynchronous; nothing waits on the device,
+ *             the scalars stay in the workspace for lce_loss_fetch and a bad
+ *             target (586) shows there or in the next lce_backward.
  * Per-token losses are summed in token order with a fixed reduction tree,
  * so the result is bit-identical for every chunk size (lossk page,
  * "Chunk invariance is checked to the last bit"). */
@@ -161,6 +164,13 @@ int32_t lce_forward(const lce_tensor *hidden, const lce_tensor *weight,
                     const lce_tensor *targets, const lce_tensor *loss_mask, int64_t n_tok,
                     int64_t d_model, int64_t vocab, int64_t chunk, double z_coef,
                     lce_tensor *lse_out, lce_tensor *workspace, lce_loss *out, void *stream);
+
+/* The scalars of the last lce_forward on this workspace (lce_backward on the
+ * same workspace keeps them): synchronizes `stream`, fills *out.  Returns 586
+ * when that forward (or a later lce_backward) met a target out of range,
+ * 582 for a NULL out or a workspace shorter than its control block, 590 for
+ * a workspace that is not LCE_U8. */
+int32_t lce_loss_fetch(const lce_tensor *workspace, lce_loss *out, void *stream);
 
 /* Analytic backward of loss_mean + z_coef*z_mean scaled by grad_out
  * (lossk table, fused_linear_ce_bwd_flat; Fast-LLM 566, "What it does"):

@@ -32,15 +32,18 @@ namespace lce {
 
 // ---------------------------------------------------------- small kernels --
 
-__global__ void ctl_init_kernel(Control *ctl) {
+// keep_loss: leave the forward's loss scalars for lce_loss_fetch.
+__global__ void ctl_init_kernel(Control *ctl, int keep_loss) {
   if (threadIdx.x == 0) {
     ctl->bad = 0;
     ctl->pad0 = 0;
     ctl->first_bad = LLONG_MAX;
     ctl->count = 0;
     ctl->pad1 = 0;
-    ctl->loss_sum = 0.0;
-    ctl->z_sum = 0.0;
+    if (!keep_loss) {
+      ctl->loss_sum = 0.0;
+      ctl->z_sum = 0.0;
+    }
   }
 }
 
@@ -671,9 +674,9 @@ static void launch_any(bool pipe, bool vec, const GemmParams &g, int64_t splits,
 }
 
 static void launch_guard(const int64_t *y, const uint8_t *mask, int64_t n, int64_t V,
-                         Control *ctl, hipStream_t st, lce_timers *tm) {
+                         Control *ctl, hipStream_t st, lce_timers *tm, int keep_loss) {
   TimedLaunch tl(tm, LCE_K_GUARD, st);
-  hipLaunchKernelGGL(ctl_init_kernel, dim3(1), dim3(64), 0, st, ctl);
+  hipLaunchKernelGGL(ctl_init_kernel, dim3(1), dim3(64), 0, st, ctl, keep_loss);
   int64_t blocks = cdiv(n, 256);
   if (blocks > 1024) blocks = 1024;
   hipLaunchKernelGGL(guard_kernel, dim3(unsigned(blocks)), dim3(256), 0, st, y, mask, n, V, ctl);
@@ -689,7 +692,7 @@ static void forward_impl(const CEPlan &p, const void *H, const void *W, const in
   Acc *zy = reinterpret_cast<Acc *>(ws + p.off_zy);
   double *loss_tok = reinterpret_cast<double *>(ws + p.off_losstok);
   const typename TR::E *Hp = static_cast<const typename TR::E *>(H);
-  launch_guard(y, mask, p.n, p.V, ctl, st, tm);
+  launch_guard(y, mask, p.n, p.V, ctl, st, tm, 0);
   {
     TimedLaunch tl(tm, LCE_K_FWD_MERGE, st);
     hipLaunchKernelGGL(target_logit_kernel<TR>, dim3(unsigned(cdiv(p.n, 4))), dim3(256), 0, st,
@@ -734,7 +737,7 @@ static void backward_impl(const CEPlan &p, const void *H, const void *W, const i
   Acc *dhacc = reinterpret_cast<Acc *>(ws + p.off_dhacc);
   const E *Hp = static_cast<const E *>(H);
   const E *Wp = static_cast<const E *>(W);
-  launch_guard(y, mask, p.n, p.V, ctl, st, tm);
+  launch_guard(y, mask, p.n, p.V, ctl, st, tm, 1);
   const bool pipe = UsePipe<TR>::ok(vec, p.D, p.d_ld);
   E *Ht = nullptr;
   Acc *zyb = nullptr;
@@ -856,6 +859,14 @@ int32_t finish(hipStream_t st, Control *dev_ctl, Control *host_ctl) {
   return host_ctl->bad ? LCE_TARGET_OUT_OF_RANGE : LCE_OK;
 }
 
+void fill_loss(const Control &hc, lce_loss *out) {
+  out->loss_sum = hc.loss_sum;
+  out->z_sum = hc.z_sum;
+  out->n_counted = hc.count;
+  out->loss_mean = hc.count ? hc.loss_sum / double(hc.count) : 0.0;
+  out->z_mean = hc.count ? hc.z_sum / double(hc.count) : 0.0;
+}
+
 }  // namespace
 
 extern "C" {
@@ -891,7 +902,6 @@ int32_t lce_forward_timed(const lce_tensor *hidden, const lce_tensor *weight,
   if (st != LCE_OK) return st;
   if (!has(lse_out) || lse_out->numel < n_tok) return LCE_LENGTH_MISMATCH;
   if (!has(workspace) || workspace->numel < int64_t(p.total) + 256) return LCE_LENGTH_MISMATCH;
-  if (!out) return LCE_LENGTH_MISMATCH;
 
   hipStream_t s = static_cast<hipStream_t>(stream);
   uint8_t *ws = ws_base(workspace);
@@ -907,14 +917,24 @@ int32_t lce_forward_timed(const lce_tensor *hidden, const lce_tensor *weight,
     forward_impl<TraitsF64>(p, hidden->data, weight->data, y, mask,
                             static_cast<double *>(lse_out->data), ws, vec, s, timers);
   }
+  if (!out)  // asynchronous: the scalars stay in the workspace (lce_loss_fetch)
+    return hipGetLastError() == hipSuccess ? LCE_OK : LCE_DEVICE_ERROR;
   Control hc;
   st = finish(s, reinterpret_cast<Control *>(ws), &hc);
   if (st != LCE_OK) return st;
-  out->loss_sum = hc.loss_sum;
-  out->z_sum = hc.z_sum;
-  out->n_counted = hc.count;
-  out->loss_mean = hc.count ? hc.loss_sum / double(hc.count) : 0.0;
-  out->z_mean = hc.count ? hc.z_sum / double(hc.count) : 0.0;
+  fill_loss(hc, out);
+  return LCE_OK;
+}
+
+int32_t lce_loss_fetch(const lce_tensor *workspace, lce_loss *out, void *stream) {
+  if (!out || !has(workspace) || workspace->numel < int64_t(kControlBytes) + 256)
+    return LCE_LENGTH_MISMATCH;
+  if (workspace->dtype != LCE_U8) return LCE_DTYPE_MISMATCH;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  Control hc;
+  const int32_t st = finish(s, reinterpret_cast<Control *>(ws_base(workspace)), &hc);
+  if (st != LCE_OK) return st;
+  fill_loss(hc, out);
   return LCE_OK;
 }
 

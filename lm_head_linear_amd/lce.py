@@ -138,6 +138,8 @@ def lib():
         L.lce_forward.restype = i32
         L.lce_forward.argtypes = [PT, PT, PT, PT, i64, i64, i64, i64, dbl, PT, PT,
                                   ctypes.POINTER(Loss), vp]
+        L.lce_loss_fetch.restype = i32
+        L.lce_loss_fetch.argtypes = [PT, ctypes.POINTER(Loss), vp]
         L.lce_backward.restype = i32
         L.lce_backward.argtypes = [PT, PT, PT, PT, PT, i64, i64, i64, i64, dbl, dbl, PT, PT, i32,
                                    PT, vp]
@@ -210,19 +212,31 @@ def lce_distill_workspace_bytes(n_tok: int, vocab: int) -> int:
 
 def lce_forward(hidden, weight, targets, loss_mask, n_tok, d_model, vocab, chunk, z_coef,
                 lse_out, workspace, stream: Optional[int] = None,
-                timer: Optional[KernelTimer] = None):
+                timer: Optional[KernelTimer] = None, sync: bool = True):
     """Direct call of the C entry point (lce_forward_timed when a timer is
-    given).  Returns (status, Loss)."""
-    out = Loss()
+    given).  Returns (status, Loss); with sync=False the call passes a NULL
+    out (asynchronous) and returns (status, None): lce_loss_fetch reads the
+    scalars later."""
+    out = Loss() if sync else None
     args = [_t(hidden), _t(weight), _t(targets), _t(loss_mask)]
     lse_t, ws_t = _t(lse_out), _t(workspace)
     call = [*[ctypes.byref(a) for a in args], n_tok, d_model, vocab, chunk, float(z_coef),
-            ctypes.byref(lse_t), ctypes.byref(ws_t), ctypes.byref(out),
+            ctypes.byref(lse_t), ctypes.byref(ws_t), ctypes.byref(out) if sync else None,
             stream if stream is not None else _stream(hidden.device)]
     if timer is None:
         st = lib().lce_forward(*call)
     else:
         st = lib().lce_forward_timed(*call, ctypes.byref(timer.struct))
+    return st, out
+
+
+def lce_loss_fetch(workspace, stream: Optional[int] = None):
+    """Scalars of the last lce_forward on `workspace` (synchronizes the
+    stream).  Returns (status, Loss)."""
+    out = Loss()
+    ws_t = _t(workspace)
+    st = lib().lce_loss_fetch(ctypes.byref(ws_t), ctypes.byref(out),
+                              stream if stream is not None else _stream(workspace.device))
     return st, out
 
 

@@ -7,6 +7,7 @@ import re
 
 import numpy as np
 import pytest
+import torch
 
 import oracle
 from lm_head_linear_amd import lce
@@ -81,3 +82,9 @@ def test_workspace_monotone_and_bounded(n, D, V, chunk):
     for dt in (lce.BF16, lce.F64):
         b = lce.lce_workspace_bytes(n, D, V, chunk, dt)
         assert b > 0
+
+
+def test_loss_fetch_refuses_short_workspace_without_device():
+    ws = torch.zeros(100, dtype=torch.uint8)
+    assert lce.lce_loss_fetch(ws, stream=0)[0] == 582
+    assert lce.lce_loss_fetch(torch.zeros(1024, dtype=torch.int32), stream=0)[0] == 590

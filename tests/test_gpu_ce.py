@@ -163,6 +163,40 @@ def test_all_masked_gives_zeros():
     assert not dH.any() and not dW.any()
 
 
+def test_async_forward_then_fetch():
+    """A forward with a NULL out does not synchronize; lce_loss_fetch after the
+    backward on the same workspace returns the same scalars bit for bit, and a
+    bad target surfaces in the backward and the fetch."""
+    c = Case(syn.QWEN_BF16, 300, 192, 3000, seed=9, mask_frac=0.1)
+    dev = c.H.device
+    chunk = 40
+    ws = lce.workspace_for(c.n, c.D, c.V, chunk, torch.bfloat16, dev)
+    lse1 = torch.empty(c.n, dtype=torch.float32, device=dev)
+    st, ref = lce.lce_forward(c.H, c.W, c.y, c.m, c.n, c.D, c.V, chunk, c.z, lse1, ws)
+    assert st == 580
+    lse2 = torch.empty_like(lse1)
+    st, none = lce.lce_forward(c.H, c.W, c.y, c.m, c.n, c.D, c.V, chunk, c.z, lse2, ws, sync=False)
+    assert st == 580 and none is None
+    dh = torch.empty_like(c.H)
+    dw = torch.empty(c.V, c.D, dtype=torch.float32, device=dev)
+    st = lce.lce_backward(c.H, c.W, c.y, c.m, lse2, c.n, c.D, c.V, chunk, c.z, 1.0, dh, dw, 0, ws)
+    assert st == 580
+    st, got = lce.lce_loss_fetch(ws)
+    assert st == 580
+    assert torch.equal(lse1, lse2)
+    for k in ("loss_sum", "z_sum", "n_counted", "loss_mean", "z_mean"):
+        assert getattr(got, k) == getattr(ref, k), k
+    dh_ref, dw_ref = c.gpu_backward(lse1, chunk)
+    assert torch.equal(dh, dh_ref) and torch.equal(dw, dw_ref)
+    bad = c.y.clone()
+    bad[5] = c.V
+    st, _ = lce.lce_forward(c.H, c.W, bad, c.m, c.n, c.D, c.V, chunk, c.z, lse2, ws, sync=False)
+    assert st == 580
+    st = lce.lce_backward(c.H, c.W, bad, c.m, lse2, c.n, c.D, c.V, chunk, c.z, 1.0, dh, dw, 0, ws)
+    assert st == 586
+    assert lce.lce_loss_fetch(ws)[0] == 586
+
+
 # ------------------------------------------------------------ refusals --
 
 def test_refusals_leave_outputs_untouched():
