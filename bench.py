@@ -34,6 +34,37 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
+def kernel_sources_sha256() -> str:
+    """Digest of the HIP sources the GEMM kernels are built from."""
+    import hashlib
+    h = hashlib.sha256()
+    d = os.path.join(ROOT, "lm_head_linear_amd", "csrc")
+    for f in sorted(os.listdir(d)):
+        h.update(f.encode())
+        with open(os.path.join(d, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def traffic_from_profiles(workload: str, kind: str):
+    """HBM bytes per launch of `kind` from the committed counter summary
+    (FETCH_SIZE + WRITE_SIZE, each scaled by a known-size copy), or None when
+    there is none for this workload or the kernel sources changed since."""
+    import glob
+    for path in sorted(glob.glob(os.path.join(ROOT, "profiles", "*_hbm_traffic.md"))):
+        for line in open(path):
+            if not line.startswith("traffic: "):
+                continue
+            rec = json.loads(line[len("traffic: "):])
+            if rec.get("workload") != workload:
+                continue
+            if rec.get("sources_sha256") != kernel_sources_sha256():
+                return None
+            v = rec.get("per_launch_bytes", {}).get(kind)
+            return None if v is None else int(v)
+    return None
+
+
 def cpu_baseline(w, x, tokens: int):
     """The oracle, as it stands, on the first `tokens` tokens of the workload:
     forward (all tokens of the prefix) + backward (d_hidden of the prefix and
@@ -64,7 +95,10 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="qwen_bf16",
                     choices=["qwen_bf16", "large_bf16", "qwen_f64"])
-    ap.add_argument("--cpu-tokens", type=int, default=256)
+    ap.add_argument("--cpu-tokens", type=int, default=768)
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="only copy MIB MiB device-to-device twice and exit (the known-size "
+                         "reference for the FETCH_SIZE / WRITE_SIZE counters)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-kernel-events", action="store_true")
     args = ap.parse_args()
@@ -76,6 +110,16 @@ def main():
 
     import numpy as np
     import torch
+
+    if args.copy_calibration:
+        nbytes = args.copy_calibration << 20
+        src = torch.ones(nbytes, dtype=torch.uint8, device="cuda:0")
+        dst = torch.empty_like(src)
+        for _ in range(2):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes": nbytes, "copies": 2}), flush=True)
+        return
 
     from lm_head_linear_amd import lce
     from tests import synthetic as syn
@@ -160,8 +204,8 @@ def main():
             if k in kernels:
                 kernels[k]["tflops"] = flop_gemm / (kernels[k]["ms_per_step"] / 1e3) / 1e12
         roof = {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak, "unit": "TFLOP/s",
-                "frac": round(achieved / peak, 4), "traffic": None, "kernel": dom,
-                "flops_per_launch": per_launch_flops, "avg_launch_ms": kd["avg_ms"]}
+                "frac": round(achieved / peak, 4), "traffic": traffic_from_profiles(w.name, dom),
+                "kernel": dom, "flops_per_launch": per_launch_flops, "avg_launch_ms": kd["avg_ms"]}
 
     cpu = None
     if not args.no_cpu_baseline:
