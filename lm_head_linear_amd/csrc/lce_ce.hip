@@ -95,29 +95,34 @@ template <> __device__ inline float neg_inf<float>() { return -INFINITY; }
 template <> __device__ inline double neg_inf<double>() { return -INFINITY; }
 
 // Reduce over the lanes that hold the same output column of an MFMA block.
-template <class TR, class T> __device__ inline T col_max(T x);
-template <class TR, class T> __device__ inline T col_sum(T x);
-template <> __device__ inline float col_max<TraitsBF16, float>(float x) {
-  return fmaxf(x, __shfl_xor(x, 32));
+// Keyed on the accumulator type, which fixes the MFMA layout: fp32 = the
+// 32x32 bf16 block (a column's rows sit in lanes l and l ^ 32), fp64 = the
+// 16x16 fp64 block (lanes l, l ^ 16, l ^ 32, l ^ 48).
+template <class TR, class T> __device__ inline T col_max(T x) {
+  if constexpr (std::is_same<T, float>::value) {
+    return fmaxf(x, __shfl_xor(x, 32));
+  } else {
+    x = fmax(x, __shfl_xor(x, 16));
+    return fmax(x, __shfl_xor(x, 32));
+  }
 }
-template <> __device__ inline float col_sum<TraitsBF16, float>(float x) {
-  return x + __shfl_xor(x, 32);
-}
-template <> __device__ inline double col_max<TraitsF64, double>(double x) {
-  x = fmax(x, __shfl_xor(x, 16));
-  return fmax(x, __shfl_xor(x, 32));
-}
-template <> __device__ inline double col_sum<TraitsF64, double>(double x) {
-  x = x + __shfl_xor(x, 16);
-  return x + __shfl_xor(x, 32);
+template <class TR, class T> __device__ inline T col_sum(T x) {
+  if constexpr (std::is_same<T, float>::value) {
+    return x + __shfl_xor(x, 32);
+  } else {
+    x = x + __shfl_xor(x, 16);
+    return x + __shfl_xor(x, 32);
+  }
 }
 
-template <class TR> __device__ inline typename TR::E to_elem(typename TR::Acc x);
-template <> __device__ inline uint16_t to_elem<TraitsBF16>(float x) { return f32_to_bf16_rne(x); }
-template <> __device__ inline double to_elem<TraitsF64>(double x) { return x; }
-template <class TR> __device__ inline typename TR::Acc to_acc(typename TR::E x);
-template <> __device__ inline float to_acc<TraitsBF16>(uint16_t x) { return bf16_to_f32(x); }
-template <> __device__ inline double to_acc<TraitsF64>(double x) { return x; }
+template <class TR> __device__ inline typename TR::E to_elem(typename TR::Acc x) {
+  if constexpr (std::is_same<typename TR::Acc, float>::value) return f32_to_bf16_rne(x);
+  else return x;
+}
+template <class TR> __device__ inline typename TR::Acc to_acc(typename TR::E x) {
+  if constexpr (std::is_same<typename TR::Acc, float>::value) return bf16_to_f32(x);
+  else return x;
+}
 
 // ------------------------------------------------------ forward epilogue --
 
@@ -263,38 +268,54 @@ __global__ void fwd_final_kernel(const double *loss_tok, const Acc *lse, const u
 
 // ----------------------------------------------------- backward epilogues --
 
-// LDS-staged output of one wave's 128x128 fp32-accumulated tile (bf16 core).
-// Rows of the 32x32x16 accumulator layout are spread over lanes in steps of
-// four, so storing straight from registers costs one narrow access per value.
-// Instead each 32-row block goes to a private LDS region (value xf(fm, fn, r,
-// row) at [row][col]) and comes back as 16-byte row chunks, which are stored
-// (or added to memory) with one dwordx4 access each: 16 lanes cover 256
-// contiguous bytes of one output row.  Row pitches of 128 + 8 fp32 / 128 + 8
-// bf16 values keep the writes (lanes 32..63 hold rows four below lanes
-// 0..31) and the row-chunk reads free of bank conflicts.
+// LDS-staged output of one wave's fp32-accumulated tile (bf16 core; the wave
+// tile is TR::WTM x TR::WTN, 32x32 MFMA blocks).  Rows of the accumulator
+// layout are spread over lanes in steps of four, so storing straight from
+// registers costs one narrow access per value.  Instead each 32-row block goes
+// to a private LDS region (value xf(fm, fn, r, row) at [row][col]) and comes
+// back as 16-byte row chunks, which are stored (or added to memory) with one
+// dwordx4 access each: consecutive lanes cover contiguous bytes of one output
+// row.  Staged rows are unpadded; chunk c of row R sits at c ^ sw(R), which
+// moves rows R+4..R+7 (written by lanes 32..63 together with rows R..R+3 by
+// lanes 0..31) to the other half of the banks, so neither the writes nor the
+// row-chunk reads conflict.
 //   ptr(row, col): destination of the chunk at wave-tile (row, col), or
 //                  nullptr to skip it (outside the output);
 //   patch(fm, region): runs after block fm is written, before it is read
-//                  back (may overwrite single staged values).
-template <class T, bool ACCUM, class Xf, class Ptr, class Patch>
-__device__ __forceinline__ void staged_tile(const TraitsBF16::AccBlock (&acc)[4][4], char *region,
-                                            int lane, const Xf &xf, const Ptr &ptr,
+//                  back (may overwrite single staged values, staged_at()).
+template <class T, class TR> struct Staging {
+  static constexpr int ES = int(sizeof(T));
+  static constexpr int PITCH = TR::WTN * ES;           // bytes per staged row
+  static constexpr int CPR = PITCH / 16;                // 16-byte chunks per row
+  static constexpr int SW = CPR / 2 < 8 ? CPR / 2 : 8;  // swizzle span
+  static constexpr int BYTES = 32 * PITCH;              // one wave's region
+  __device__ static inline int chunk_at(int row, int c) {
+    return row * PITCH + ((c ^ (((row >> 2) & 1) * SW)) << 4);
+  }
+  // byte offset of value (row, col) of a staged block
+  __device__ static inline int at(int row, int col) {
+    return chunk_at(row, (col * ES) >> 4) + ((col * ES) & 15);
+  }
+};
+
+template <class T, class TR, bool ACCUM, class Xf, class Ptr, class Patch>
+__device__ __forceinline__ void staged_tile(const typename TR::AccBlock (&acc)[TR::FM][TR::FN],
+                                            char *region, int lane, const Xf &xf, const Ptr &ptr,
                                             const Patch &patch) {
-  constexpr int ES = int(sizeof(T));
-  constexpr int PITCH = (128 + 8) * ES;           // bytes per staged row
-  constexpr int CPR = 128 * ES / 16;              // 16-byte chunks per row
-  constexpr int NR = 32 * CPR / 64;               // chunk reads per lane per block
-  constexpr int EPC = 16 / ES;                    // values per chunk
-  static_assert(!ACCUM || ES == 4, "accumulation is fp32");
+  typedef Staging<T, TR> S;
+  constexpr int NR = 32 * S::CPR / 64;            // chunk reads per lane per block
+  constexpr int EPC = 16 / S::ES;                 // values per chunk
+  static_assert(!ACCUM || S::ES == 4, "accumulation is fp32");
+  static_assert(NR >= 1, "staged block");
 #pragma unroll
-  for (int fm = 0; fm < 4; ++fm) {
+  for (int fm = 0; fm < TR::FM; ++fm) {
 #pragma unroll
-    for (int fn = 0; fn < 4; ++fn)
+    for (int fn = 0; fn < TR::FN; ++fn)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int row = (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
-        const int col = fn * 32 + (lane & 31);
-        *reinterpret_cast<T *>(region + row * PITCH + col * ES) = xf(fm, fn, r, fm * 32 + row);
+      for (int r = 0; r < TR::R; ++r) {
+        const int row = TR::row_of(r, lane);
+        const int col = fn * TR::MF + TR::col_of(lane);
+        *reinterpret_cast<T *>(region + S::at(row, col)) = xf(fm, fn, r, fm * TR::MF + row);
       }
     patch(fm, region);
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
@@ -303,9 +324,9 @@ __device__ __forceinline__ void staged_tile(const TraitsBF16::AccBlock (&acc)[4]
 #pragma unroll
     for (int i = 0; i < NR; ++i) {
       const int q = i * 64 + lane;
-      const int row = q / CPR, c = q % CPR;
-      d[i] = *reinterpret_cast<const u32x4 *>(region + row * PITCH + c * 16);
-      dst[i] = ptr(fm * 32 + row, c * EPC);
+      const int row = q / S::CPR, c = q % S::CPR;
+      d[i] = *reinterpret_cast<const u32x4 *>(region + S::chunk_at(row, c));
+      dst[i] = ptr(fm * TR::MF + row, c * EPC);
     }
     if constexpr (ACCUM) {
       u32x4 old[NR];
@@ -330,9 +351,6 @@ __device__ __forceinline__ void staged_tile(const TraitsBF16::AccBlock (&acc)[4]
     __builtin_amdgcn_sched_barrier(0);   // one block's registers at a time
   }
 }
-
-// Bytes of LDS one wave's staging region takes.
-template <class T> constexpr int staged_region_bytes() { return 32 * (128 + 8) * int(sizeof(T)); }
 
 // Recomputed Z^T tile of a vocabulary slab -> logit gradient, stored
 // [slab row][token] in the input dtype.
@@ -452,7 +470,7 @@ struct DlogitEpi {
   __device__ __forceinline__ void staged(typename TR::AccBlock (&acc)[TR::FM][TR::FN], int64_t m0,
                                          int64_t n0, int wm, int wn, int lane, int,
                                          char *lds, const char *pre) const {
-    static_assert(std::is_same<TR, TraitsBF16>::value, "staged epilogue is bf16");
+    static_assert(std::is_same<typename TR::Acc, float>::value, "staged epilogue is bf16");
     const float L2E = 1.4426950408889634f;
     const int64_t vw0 = m0 + int64_t(wm) * TR::WTM;
     const int64_t tw0 = n0 + int64_t(wn) * TR::WTN;
@@ -470,8 +488,9 @@ struct DlogitEpi {
       yl[fn] = (int(q[2]) >= 0 && yr >= 0 && yr < TR::WTM && vw0 + yr < rows) ? yr : -1;
       gy[fn] = __uint_as_float(q[3]);
     }
-    char *region = lds + (wm * 2 + wn) * staged_region_bytes<uint16_t>();
-    staged_tile<uint16_t, false>(
+    typedef Staging<uint16_t, TR> S;
+    char *region = lds + (wm * TR::WAVES_N + wn) * S::BYTES;
+    staged_tile<uint16_t, TR, false>(
         acc, region, lane,
         [&](int fm, int fn, int r, int) -> uint16_t {
           const float e = __builtin_amdgcn_exp2f(fmaf(acc[fm][fn][r], L2E, c2[fn]));
@@ -485,9 +504,9 @@ struct DlogitEpi {
           // overwrite the target element of each column that has it here
 #pragma unroll
           for (int fn = 0; fn < TR::FN; ++fn)
-            if (lane < 32 && yl[fn] >= fm * 32 && yl[fn] < fm * 32 + 32)
-              *reinterpret_cast<uint16_t *>(blk + (yl[fn] - fm * 32) * ((128 + 8) * 2) +
-                                            (fn * 32 + lane) * 2) = to_elem<TR>(gy[fn]);
+            if (lane < TR::MF && yl[fn] >= fm * TR::MF && yl[fn] < fm * TR::MF + TR::MF)
+              *reinterpret_cast<uint16_t *>(blk + S::at(yl[fn] - fm * TR::MF, fn * TR::MF + lane)) =
+                  to_elem<TR>(gy[fn]);
         });
   }
 };
@@ -542,13 +561,13 @@ struct StoreEpi {
   __device__ __forceinline__ void staged(typename TR::AccBlock (&acc)[TR::FM][TR::FN], int64_t m0,
                                          int64_t n0, int wm, int wn, int lane, int split,
                                          char *lds, const char *) const {
-    static_assert(std::is_same<TR, TraitsBF16>::value, "staged epilogue is bf16");
+    static_assert(std::is_same<typename TR::Acc, float>::value, "staged epilogue is bf16");
     Acc *o = out + int64_t(split) * split_stride;
     const int64_t rw0 = m0 + int64_t(wm) * TR::WTM;
     const int64_t cw0 = n0 + int64_t(wn) * TR::WTN;
     if (rw0 >= rows || cw0 >= cols) return;  // wave-uniform
-    char *region = lds + (wm * 2 + wn) * staged_region_bytes<float>();
-    staged_tile<float, ACCUM>(
+    char *region = lds + (wm * TR::WAVES_N + wn) * Staging<float, TR>::BYTES;
+    staged_tile<float, TR, ACCUM>(
         acc, region, lane, [&](int fm, int fn, int r, int) -> float { return acc[fm][fn][r]; },
         [&](int rr, int cc) -> float * {
           const int64_t row = rw0 + rr, c = cw0 + cc;
@@ -634,6 +653,19 @@ static void launch_gemm(bool vec, const GemmParams &g, int64_t splits, const Epi
 typedef PipeCfg<32, 4> PipeKK;
 typedef PipeCfg<64, 2> PipeMN;
 
+// The pipelined core runs 8 waves per tile (TraitsBF16W8); its epilogues are
+// the same structs instantiated on those traits (same members, so the fields
+// carry over bit for bit).
+template <class TR2, class TR> FwdLseEpi<TR2> retrait(const FwdLseEpi<TR> &e) {
+  return __builtin_bit_cast(FwdLseEpi<TR2>, e);
+}
+template <class TR2, class TR> DlogitEpi<TR2> retrait(const DlogitEpi<TR> &e) {
+  return __builtin_bit_cast(DlogitEpi<TR2>, e);
+}
+template <class TR2, class TR, bool A> StoreEpi<TR2, A> retrait(const StoreEpi<TR, A> &e) {
+  return __builtin_bit_cast(StoreEpi<TR2, A>, e);
+}
+
 template <class CFG, bool AK, bool BKM, class Epi>
 static void launch_gemm2(const GemmParams &g0, int64_t splits, const Epi &epi, hipStream_t st) {
   Gemm2Params g;
@@ -642,8 +674,11 @@ static void launch_gemm2(const GemmParams &g0, int64_t splits, const Epi &epi, h
   g.k_per_split = (g0.k_per_split + CFG::BK - 1) / CFG::BK * CFG::BK;
   g.tiles_n = g0.tiles_n; g.bad = g0.bad;
   const int64_t tiles = cdiv(g.M, CFG::BM) * g.tiles_n;
-  const dim3 grid{unsigned(tiles), unsigned(splits), 1u};
-  hipLaunchKernelGGL((gemm2_kernel<CFG, AK, BKM, Epi>), grid, dim3(CFG::NT), 0, st, g, epi);
+  const dim3 grid{unsigned(tiles * splits), 1u, 1u};
+  typedef TraitsBF16W8 TRP;
+  const auto e = retrait<TRP>(epi);
+  hipLaunchKernelGGL((gemm2_kernel<CFG, TRP, AK, BKM, decltype(e)>), grid, dim3(TRP::NT), 0, st, g,
+                     e);
 }
 
 // The pipelined bf16 core applies when every operand is 16-byte aligned with

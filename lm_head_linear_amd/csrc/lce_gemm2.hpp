@@ -42,13 +42,19 @@ template <int BK_, int STAGES_, int AUX_ = 0>
 struct PipeCfg {
   static constexpr int BM = 256, BN = 256, BK = BK_, STAGES = STAGES_;
   static constexpr int AUX = AUX_;                    // cache-policy bits of the operand loads
-  static constexpr int NT = 256;
   static constexpr int KSUB = BK / 16;                // MFMA k-substeps per stage
   static constexpr int ROWB = BK * 2;                  // bytes per K-major tile row
   static constexpr int OP_BYTES = 256 * BK * 2;       // per operand per stage
   static constexpr int STAGE_BYTES = 2 * OP_BYTES;
-  static constexpr int INSTR = OP_BYTES / 1024 / 4;   // DMA instructions per wave per operand
-  static constexpr int LOADS_PER_STAGE = 2 * INSTR;   // per wave
+};
+
+// 256x256 tile on 8 waves (two per SIMD), each 128 x 64: while one wave of a
+// SIMD waits on LDS or the stage barrier the other keeps the matrix core busy.
+struct TraitsBF16W8 : TraitsBF16 {
+  static constexpr int WAVES_M = 2, WAVES_N = 4;
+  static constexpr int NT = WAVES_M * WAVES_N * 64;
+  static constexpr int WTM = BM / WAVES_M, WTN = BN / WAVES_N;
+  static constexpr int FM = WTM / MF, FN = WTN / MF;
 };
 typedef PipeCfg<32, 4> Pipe;   // the configuration the library launches
 
@@ -79,14 +85,15 @@ __device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t rs, char *dst, uint
 }
 
 // One operand of one stage: OP_BYTES / 1 KB wave-instructions, INSTR per wave.
-template <class CFG, bool KMAJOR>
+template <class CFG, int NWAVES, bool KMAJOR>
 struct PipeOperand {
+  static constexpr int INSTR = CFG::OP_BYTES / 1024 / NWAVES;
   const uint16_t *p;   // operand base (element 0 of row/k-row 0)
   int64_t ld;          // leading dimension in elements
   int64_t row0;        // first tile row (M or N index)
   int64_t row_lim;     // valid rows (K-major) / readable row length (MN-major)
   int64_t k_lim;       // valid k (MN-major zero-fill)
-  uint32_t voff[CFG::INSTR];  // per-lane byte offsets
+  uint32_t voff[INSTR];  // per-lane byte offsets
   __amdgpu_buffer_rsrc_t rs;
 
   __device__ inline void init(const uint16_t *p_, int64_t ld_, int64_t row0_, int64_t row_lim_,
@@ -96,16 +103,16 @@ struct PipeOperand {
     if (KMAJOR) {
       rs = make_rsrc(p + row0 * ld, (row_lim - row0) * ld * 2);
 #pragma unroll
-      for (int i = 0; i < CFG::INSTR; ++i) {
-        const int j = wave * CFG::INSTR + i;
+      for (int i = 0; i < INSTR; ++i) {
+        const int j = wave * INSTR + i;
         const int r = (64 / CPR) * j + lane / CPR;
         const int c = (lane % CPR) ^ kswz<CFG::ROWB>(r);
         voff[i] = uint32_t(r) * uint32_t(ld * 2) + uint32_t(c * 16);
       }
     } else {
 #pragma unroll
-      for (int i = 0; i < CFG::INSTR; ++i) {
-        const int j = wave * CFG::INSTR + i;
+      for (int i = 0; i < INSTR; ++i) {
+        const int j = wave * INSTR + i;
         const int q = 2 * j + (lane >> 5);
         const int c = (lane & 31) ^ mswz2(q);
         voff[i] = uint32_t(q) * uint32_t(ld * 2) + uint32_t(c * 16);
@@ -117,8 +124,8 @@ struct PipeOperand {
   __device__ inline void issue(int64_t k0, char *dst, int wave) const {
     if (KMAJOR) {
 #pragma unroll
-      for (int i = 0; i < CFG::INSTR; ++i) {
-        const int j = wave * CFG::INSTR + i;
+      for (int i = 0; i < INSTR; ++i) {
+        const int j = wave * INSTR + i;
         dma16<CFG::AUX>(rs, dst + j * 1024, voff[i] + uint32_t(k0 * 2));
       }
     } else {
@@ -127,8 +134,8 @@ struct PipeOperand {
       const int64_t bytes = rows > 0 ? ((rows - 1) * ld + (row_lim - row0)) * 2 : 0;
       const __amdgpu_buffer_rsrc_t r = make_rsrc(p + k0 * ld + row0, bytes);
 #pragma unroll
-      for (int i = 0; i < CFG::INSTR; ++i) {
-        const int j = wave * CFG::INSTR + i;
+      for (int i = 0; i < INSTR; ++i) {
+        const int j = wave * INSTR + i;
         dma16<CFG::AUX>(r, dst + j * 1024, voff[i]);
       }
     }
@@ -204,12 +211,17 @@ struct EpiPrefetch<E, std::void_t<decltype(E::kPrefetchBytes)>> {
   static constexpr int bytes = E::kPrefetchBytes;
 };
 
-template <class CFG, bool AK, bool BKM, class Epi>
-__global__ void __launch_bounds__(CFG::NT) gemm2_kernel(Gemm2Params g, Epi epi) {
-  typedef TraitsBF16 TR;
+template <class CFG, class TR, bool AK, bool BKM, class Epi>
+__global__ void __launch_bounds__(TR::NT) gemm2_kernel(Gemm2Params g, Epi epi) {
   constexpr int BK = CFG::BK, STAGES = CFG::STAGES, KSUB = CFG::KSUB;
-  constexpr int LPS = CFG::LOADS_PER_STAGE;
+  constexpr int NWAVES = TR::NT / 64;
+  typedef PipeOperand<CFG, NWAVES, AK> OpA;
+  typedef PipeOperand<CFG, NWAVES, BKM> OpB;
+  constexpr int LPS = OpA::INSTR + OpB::INSTR;          // loads per stage per wave
+  constexpr int NMF = TR::FM * TR::FN;                   // MFMAs per substep
+  constexpr int NDS = TR::FM * (AK ? 1 : 2) + TR::FN * (BKM ? 1 : 2);  // LDS reads per substep
   static_assert(KSUB % 2 == 0 && KSUB >= 2, "fragment double-buffer parity");
+  static_assert(TR::BM == CFG::BM && TR::BN == CFG::BN, "tile");
   if (g.bad && *g.bad) return;
   constexpr int PRE = EpiPrefetch<Epi>::bytes;
   __shared__ __attribute__((aligned(1024))) char smem[STAGES * CFG::STAGE_BYTES + PRE];
@@ -218,18 +230,23 @@ __global__ void __launch_bounds__(CFG::NT) gemm2_kernel(Gemm2Params g, Epi epi) 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
-  const int wm = wave >> 1, wn = wave & 1;
+  const int wm = wave / TR::WAVES_N, wn = wave % TR::WAVES_N;
 
-  const int64_t L = xcd_remap(blockIdx.x, gridDim.x);
+  // One flat grid over (split, tile), split-major, dealt to the XCDs in
+  // contiguous ranges: an XCD's workgroups share whole K-splits, so each
+  // split's operand rows are fetched into one L2 only.
+  const int64_t tiles = (g.M + CFG::BM - 1) / CFG::BM * g.tiles_n;
+  const int64_t LS = xcd_remap(blockIdx.x, gridDim.x);
+  const int split = int(LS / tiles);
+  const int64_t L = LS % tiles;
   const int64_t m0 = (L / g.tiles_n) * CFG::BM;
   const int64_t n0 = (L % g.tiles_n) * CFG::BN;
-  const int split = blockIdx.y;
   const int64_t k_begin = int64_t(split) * g.k_per_split;
   int64_t k_end = k_begin + g.k_per_split;
   if (k_end > g.K) k_end = g.K;
   const int n_k = k_end > k_begin ? int((k_end - k_begin + BK - 1) / BK) : 0;
 
-  TR::AccBlock acc[TR::FM][TR::FN];
+  typename TR::AccBlock acc[TR::FM][TR::FN];
 #pragma unroll
   for (int fm = 0; fm < TR::FM; ++fm)
 #pragma unroll
@@ -237,8 +254,8 @@ __global__ void __launch_bounds__(CFG::NT) gemm2_kernel(Gemm2Params g, Epi epi) 
 #pragma unroll
       for (int r = 0; r < TR::R; ++r) acc[fm][fn][r] = 0;
 
-  PipeOperand<CFG, AK> pa;
-  PipeOperand<CFG, BKM> pb;
+  OpA pa;
+  OpB pb;
   pa.init(static_cast<const uint16_t *>(g.A), g.lda, m0, AK ? g.M : g.M_read, g.K, wave, lane);
   pb.init(static_cast<const uint16_t *>(g.B), g.ldb, n0, BKM ? g.N : g.N_read, g.K, wave, lane);
 
@@ -263,10 +280,10 @@ __global__ void __launch_bounds__(CFG::NT) gemm2_kernel(Gemm2Params g, Epi epi) 
   u32x4 fa[2][TR::FM], fb[2][TR::FN];
   if (n_k > 0) {
 #pragma unroll
-    for (int f = 0; f < 4; ++f) {
-      fa[0][f] = pa.frag(smem, wm * TR::WTM + f * 32, 0, lane);
+    for (int f = 0; f < TR::FM; ++f) fa[0][f] = pa.frag(smem, wm * TR::WTM + f * 32, 0, lane);
+#pragma unroll
+    for (int f = 0; f < TR::FN; ++f)
       fb[0][f] = pb.frag(smem + CFG::OP_BYTES, wn * TR::WTN + f * 32, 0, lane);
-    }
   }
 
   // One k-step of BK = KSUB MFMA k-substeps.  Substep kk computes on the
@@ -287,10 +304,10 @@ __global__ void __launch_bounds__(CFG::NT) gemm2_kernel(Gemm2Params g, Epi epi) 
         const char *src = last ? sn : sa;
         const int ks = last ? 0 : kk + 1;
 #pragma unroll
-        for (int f = 0; f < 4; ++f) {
-          fa[nxt][f] = pa.frag(src, wm * TR::WTM + f * 32, ks, lane);
+        for (int f = 0; f < TR::FM; ++f) fa[nxt][f] = pa.frag(src, wm * TR::WTM + f * 32, ks, lane);
+#pragma unroll
+        for (int f = 0; f < TR::FN; ++f)
           fb[nxt][f] = pb.frag(src + CFG::OP_BYTES, wn * TR::WTN + f * 32, ks, lane);
-        }
       }
 #pragma unroll
       for (int fm = 0; fm < TR::FM; ++fm)
@@ -299,24 +316,26 @@ __global__ void __launch_bounds__(CFG::NT) gemm2_kernel(Gemm2Params g, Epi epi) 
           acc[fm][fn] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
               __builtin_bit_cast(bf16x8, fa[cur][fm]), __builtin_bit_cast(bf16x8, fb[cur][fn]),
               acc[fm][fn], 0, 0, 0);
+      // Interleave: one MFMA, then (while any remain) one refill load and one
+      // LDS read.
+      constexpr int NDS_I = NDS < NMF ? NDS : NMF;
       if (last && STEADY) {
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                // one MFMA
-          if (i < CFG::LOADS_PER_STAGE) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);   // one refill load
-          if (i < 8) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);     // one LDS read
+        for (int i = 0; i < NMF; ++i) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          if (i < LPS) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+          if (i < NDS_I) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
         }
       } else if (!last) {
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // one MFMA
-          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // one LDS read
+        for (int i = 0; i < NMF; ++i) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          if (i < NDS_I) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
         }
-        __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
       }
       if (kk == CFG::KSUB - 2) {
-        if (STEADY) wait_vm_barrier<CFG::LOADS_PER_STAGE * (CFG::STAGES - 2)>();
-        else wait_vm_barrier_stages<CFG::LOADS_PER_STAGE, CFG::STAGES - 2>(n_k - 2 - it);
+        if (STEADY) wait_vm_barrier<LPS * (CFG::STAGES - 2)>();
+        else wait_vm_barrier_stages<LPS, CFG::STAGES - 2>(n_k - 2 - it);
         if (STEADY || it + CFG::STAGES < n_k) {
           pa.issue(k_begin + int64_t(it + CFG::STAGES) * CFG::BK, sa, wave);
           pb.issue(k_begin + int64_t(it + CFG::STAGES) * CFG::BK, sa + CFG::OP_BYTES, wave);
@@ -336,7 +355,7 @@ __global__ void __launch_bounds__(CFG::NT) gemm2_kernel(Gemm2Params g, Epi epi) 
     // done reading its operand fragments first.
     __syncthreads();
     if constexpr (PRE > 0) {
-      epi.pre_store(pre, m0_e, n0_e, tid, pre_lds);
+      if (tid < CFG::BN) epi.pre_store(pre, m0_e, n0_e, tid, pre_lds);
       __syncthreads();
     }
     epi.staged(acc, m0_e, n0_e, wm_e, wn_e, lane_e, split, smem, pre_lds);
