@@ -3,12 +3,17 @@
 Default workload: the Qwen3-0.6B-shaped LM head, 2048 tokens x d_model 1024 x
 vocab 151936, bf16 inputs with fp32 accumulation, chunk 256, z-loss 1e-4, 5%
 of tokens masked, synthetic seeded inputs already resident in HBM.  One step
-= lce_forward + lce_backward as a caller makes them (target guard and status
-syncs included).  Prints one JSON line.
+= lce_forward (asynchronous: no host round trip) + lce_backward (target guard,
+its status synchronization included), as a training loop makes them; the loss
+scalars are read back once after the timed steps (lce_loss_fetch).  Prints
+one JSON line.
 
-Kernel durations for the roofline come from HIP events that the library
-records around every launch of each GEMM kind inside the timed region
-(lce_forward_timed / lce_backward_timed on torch's current stream).
+Timing: the K timed steps run with nothing recorded between kernels (value,
+ms_per_step).  A second pass repeats the K steps with HIP events that the
+library records around every kernel launch on the launch stream
+(lce_forward_timed / lce_backward_timed); those give the per-kind kernel
+durations and roofline.achieved.  Events add idle time between kernels, so
+that pass never feeds the step time.
 """
 from __future__ import annotations
 
@@ -25,9 +30,11 @@ PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
 PEAK_F64_TFLOPS = 78.6         # MI355X fp64 MFMA
 PEAK_HBM_GBS = 8000.0
 
-GEMM_KINDS = ["fwd_gemm", "dlogit_gemm", "dw_gemm", "dh_gemm"]
+GEMM_KINDS = ["fwd_gemm", "dlogit_gemm", "dw_gemm", "dh_gemm", "bwd_gemm"]
+# GEMM passes (2*n*D*V flops each) one step's launches of a kind perform
+GEMM_PASSES = {"fwd_gemm": 1, "dlogit_gemm": 1, "dw_gemm": 1, "dh_gemm": 1, "bwd_gemm": 3}
 ALL_KINDS = ["guard", "fwd_gemm", "fwd_merge", "reduce", "dlogit_gemm", "dw_gemm", "dh_gemm",
-             "dh_final"]
+             "dh_final", "bwd_gemm"]
 
 
 def log(*a):
@@ -144,8 +151,8 @@ def main():
     torch.cuda.reset_peak_memory_stats()
 
     def step(timer=None):
-        # forward without a host round trip, backward (synchronizes and
-        # reports its status), then the loss scalars from the workspace
+        # forward without a host round trip, then the backward (synchronizes
+        # and reports its status); the loss scalars stay in the workspace
         st, _ = lce.lce_forward(H, W, y, m, n, D, V, chunk, z, lse, ws, timer=timer, sync=False)
         if st != lce.OK:
             raise lce.LceError(st, "lce_forward")
@@ -153,6 +160,8 @@ def main():
                               timer=timer)
         if st != lce.OK:
             raise lce.LceError(st, "lce_backward")
+
+    def fetch():
         st, out = lce.lce_loss_fetch(ws)
         if st != lce.OK:
             raise lce.LceError(st, "lce_loss_fetch")
@@ -160,27 +169,38 @@ def main():
 
     log(f"bench: warmup {args.warmup} steps")
     for _ in range(args.warmup):
-        out = step()
+        step()
+    fetch()
     torch.cuda.synchronize()
 
-    timer = None
-    if not args.no_kernel_events:
-        timer = lce.KernelTimer(ALL_KINDS, capacity=args.steps * 32)
+    # Timed pass: K steps, nothing recorded between the kernels.
     log(f"bench: timing {args.steps} steps")
     torch.cuda.synchronize()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     t0 = time.perf_counter()
     e0.record()
     for _ in range(args.steps):
-        out = step(timer)
+        step()
     e1.record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     gpu_ms = e0.elapsed_time(e1)
+    out = fetch()
     ms_per_step = 1e3 * wall / args.steps
     peak_extra = torch.cuda.max_memory_allocated() - mem0
     log(f"bench: {ms_per_step:.3f} ms/step wall, {gpu_ms / args.steps:.3f} ms/step events, "
         f"loss {out.loss_mean:.6f}")
+
+    # Kernel pass: the same K steps again with HIP events around every kernel
+    # launch (on the launch stream); the events add idle time between kernels,
+    # so this pass gives kernel durations only, never the step time.
+    timer = None
+    if not args.no_kernel_events:
+        timer = lce.KernelTimer(ALL_KINDS, capacity=args.steps * 32)
+        log(f"bench: kernel pass, {args.steps} steps with per-kernel events")
+        for _ in range(args.steps):
+            step(timer)
+        torch.cuda.synchronize()
 
     flop_gemm = 2.0 * n * D * V                  # one GEMM pass over every (token, vocab) pair
     f8 = 4 * flop_gemm                            # forward + recompute + dH + dW
@@ -198,11 +218,12 @@ def main():
                               "avg_ms": float(np.mean(d)), "ms_per_step": float(np.sum(d)) / args.steps}
         dom = max((k for k in GEMM_KINDS if k in kernels), key=lambda k: kernels[k]["ms_per_step"])
         kd = kernels[dom]
-        per_launch_flops = flop_gemm / kd["launches_per_step"]
+        per_launch_flops = GEMM_PASSES[dom] * flop_gemm / kd["launches_per_step"]
         achieved = per_launch_flops / (kd["avg_ms"] / 1e3) / 1e12
         for k in GEMM_KINDS:
             if k in kernels:
-                kernels[k]["tflops"] = flop_gemm / (kernels[k]["ms_per_step"] / 1e3) / 1e12
+                kernels[k]["tflops"] = (GEMM_PASSES[k] * flop_gemm /
+                                        (kernels[k]["ms_per_step"] / 1e3) / 1e12)
         roof = {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak, "unit": "TFLOP/s",
                 "frac": round(achieved / peak, 4), "traffic": traffic_from_profiles(w.name, dom),
                 "kernel": dom, "flops_per_launch": per_launch_flops, "avg_launch_ms": kd["avg_ms"]}

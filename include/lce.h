@@ -222,7 +222,10 @@ int32_t lce_distill_fwd_bwd(const lce_tensor *student, const lce_tensor *teacher
 #define LCE_K_DH_GEMM 6      /* split-K d_hidden accumulation                   */
 #define LCE_K_DH_FINAL 7     /* fold of the d_hidden splits                     */
 #define LCE_K_DISTILL 8      /* distillation row kernel                         */
-#define LCE_NUM_KERNELS 9
+#define LCE_K_BWD_GEMM 9     /* one launch of the slab-pipelined bf16 backward: */
+                             /* d_hidden and d_weight of slab k with the logit  */
+                             /* gradient of slab k+1                            */
+#define LCE_NUM_KERNELS 10
 
 /* One slot per kernel kind.  start/stop hold `capacity` caller-created
  * hipEvent_t handles (as void*); a timed call records start[i]/stop[i] on

@@ -597,6 +597,12 @@ __global__ void transpose_h_kernel(const uint16_t *H, int64_t n, int64_t D, uint
   }
 }
 
+__global__ void zero_f32_kernel(float *p, int64_t count) {
+  for (int64_t i = int64_t(blockIdx.x) * blockDim.x + threadIdx.x; i < count;
+       i += int64_t(gridDim.x) * blockDim.x)
+    p[i] = 0.f;
+}
+
 // d_hidden = sum over splits (ascending) of the split accumulators.
 template <class TR>
 __global__ void dh_final_kernel(const typename TR::Acc *P, int64_t splits, int64_t count,
@@ -666,13 +672,18 @@ template <class TR2, class TR, bool A> StoreEpi<TR2, A> retrait(const StoreEpi<T
   return __builtin_bit_cast(StoreEpi<TR2, A>, e);
 }
 
-template <class CFG, bool AK, bool BKM, class Epi>
-static void launch_gemm2(const GemmParams &g0, int64_t splits, const Epi &epi, hipStream_t st) {
+template <class CFG> static Gemm2Params to_gemm2(const GemmParams &g0) {
   Gemm2Params g;
   g.A = g0.A; g.lda = g0.lda; g.B = g0.B; g.ldb = g0.ldb;
   g.M = g0.M; g.N = g0.N; g.K = g0.K; g.M_read = g0.M_read; g.N_read = g0.N_read;
   g.k_per_split = (g0.k_per_split + CFG::BK - 1) / CFG::BK * CFG::BK;
   g.tiles_n = g0.tiles_n; g.bad = g0.bad;
+  return g;
+}
+
+template <class CFG, bool AK, bool BKM, class Epi>
+static void launch_gemm2(const GemmParams &g0, int64_t splits, const Epi &epi, hipStream_t st) {
+  const Gemm2Params g = to_gemm2<CFG>(g0);
   const int64_t tiles = cdiv(g.M, CFG::BM) * g.tiles_n;
   const dim3 grid{unsigned(tiles * splits), 1u, 1u};
   typedef TraitsBF16W8 TRP;
@@ -759,6 +770,82 @@ static void forward_impl(const CEPlan &p, const void *H, const void *W, const in
                      (const Acc *)lse_out, mask, p.n, ctl);
 }
 
+// bf16 backward as a slab pipeline: launch k runs d_hidden and d_weight of
+// slab k-1 (from slab buffer (k-1) % 2) together with the logit gradient of
+// slab k (into buffer k % 2), longest products first.  The d_hidden split
+// accumulators start at zero and every launch adds to them.
+template <bool ACC_DW>
+static void backward_pipelined(const CEPlan &p, const uint16_t *Hp, const uint16_t *Wp,
+                               const int64_t *y, const uint8_t *mask, const float *lse,
+                               double z_coef, double grad_out, float *dW, uint16_t *dbuf,
+                               float *dhacc, const uint16_t *Ht, const float *zyb, Control *ctl,
+                               hipStream_t st, lce_timers *tm) {
+  typedef TraitsBF16W8 TRP;
+  typedef Gemm2Job<PipeMN, false, false, StoreEpi<TRP, true>> JH;
+  typedef Gemm2Job<PipeKK, true, true, StoreEpi<TRP, ACC_DW>> JW;
+  typedef Gemm2Job<PipeKK, true, true, DlogitEpi<TRP>> JL;
+  const int64_t n = p.n, D = p.D, V = p.V, S = p.pslab, sp = p.pdh_splits;
+  {
+    const int64_t count = sp * n * D;
+    int64_t blocks = cdiv(count, 256);
+    if (blocks > 4096) blocks = 4096;
+    hipLaunchKernelGGL(zero_f32_kernel, dim3(unsigned(blocks)), dim3(256), 0, st, dhacc, count);
+  }
+  const int64_t tiles_d = cdiv(D, 256), tiles_t = cdiv(n, 256);
+  for (int64_t k = 0; k <= p.pn_slabs; ++k) {
+    JH jh{};
+    JW jw{};
+    JL jl{};
+    if (k >= 1) {  // slab k-1: d_hidden += d W_slab, d_weight rows = d H
+      const int64_t vs0 = (k - 1) * S;
+      const int64_t rows = S < V - vs0 ? S : V - vs0;
+      const uint16_t *buf = dbuf + ((k - 1) & 1) * S * p.d_ld;
+      GemmParams g;
+      g.A = buf; g.lda = p.d_ld;
+      g.B = Wp + vs0 * D; g.ldb = D;
+      g.M = n; g.N = D; g.K = rows;
+      g.M_read = p.d_ld; g.N_read = D;
+      g.k_per_split = cdiv(cdiv(rows, sp), PipeMN::BK) * PipeMN::BK;
+      g.tiles_n = tiles_d;
+      g.bad = &ctl->bad;
+      jh.g = to_gemm2<PipeMN>(g);
+      jh.e = StoreEpi<TRP, true>{dhacc, D, 0, n, D, n * D};
+      jh.nb = tiles_t * tiles_d * sp;
+      GemmParams h;
+      h.A = buf; h.lda = p.d_ld;
+      h.B = Ht; h.ldb = p.d_ld;
+      h.M = rows; h.N = D; h.K = n;
+      h.M_read = rows; h.N_read = D;
+      h.k_per_split = cdiv(n, PipeKK::BK) * PipeKK::BK;
+      h.tiles_n = tiles_d;
+      h.bad = &ctl->bad;
+      jw.g = to_gemm2<PipeKK>(h);
+      jw.e = StoreEpi<TRP, ACC_DW>{dW, D, vs0, rows, D, 0};
+      jw.nb = cdiv(rows, 256) * tiles_d;
+    }
+    if (k < p.pn_slabs) {  // slab k: recomputed logits -> logit gradient
+      const int64_t vs0 = k * S;
+      const int64_t rows = S < V - vs0 ? S : V - vs0;
+      uint16_t *buf = dbuf + (k & 1) * S * p.d_ld;
+      GemmParams g;
+      g.A = Wp + vs0 * D; g.lda = D;
+      g.B = Hp; g.ldb = D;
+      g.M = rows; g.N = n; g.K = D;
+      g.M_read = rows; g.N_read = n;
+      g.k_per_split = cdiv(D, PipeKK::BK) * PipeKK::BK;
+      g.tiles_n = tiles_t;
+      g.bad = &ctl->bad;
+      jl.g = to_gemm2<PipeKK>(g);
+      jl.e = DlogitEpi<TRP>{y, mask, lse, n, vs0, rows, ctl, grad_out, z_coef, buf, p.d_ld, zyb};
+      jl.nb = cdiv(rows, 256) * tiles_t;
+    }
+    TimedLaunch tl(tm, LCE_K_BWD_GEMM, st);
+    const int64_t total = jh.nb + jw.nb + jl.nb;
+    hipLaunchKernelGGL((gemm2_multi_kernel<TRP, JH, JW, JL>), dim3(unsigned(total)),
+                       dim3(TRP::NT), 0, st, jh, jw, jl);
+  }
+}
+
 template <class TR>
 static void backward_impl(const CEPlan &p, const void *H, const void *W, const int64_t *y,
                           const uint8_t *mask, const typename TR::Acc *lse, double z_coef,
@@ -788,6 +875,22 @@ static void backward_impl(const CEPlan &p, const void *H, const void *W, const i
       zyb = reinterpret_cast<Acc *>(ws + p.off_zyb);
       hipLaunchKernelGGL(target_logit_kernel<TR>, dim3(unsigned(cdiv(p.n, 4))), dim3(256), 0, st,
                          Hp, Wp, y, p.n, p.D, zyb, (const int32_t *)&ctl->bad);
+      if (p.pslab > 0) {
+        if (accumulate)
+          backward_pipelined<true>(p, Hp, Wp, y, mask, lse, z_coef, grad_out, dW, dbuf, dhacc,
+                                   Ht, zyb, ctl, st, tm);
+        else
+          backward_pipelined<false>(p, Hp, Wp, y, mask, lse, z_coef, grad_out, dW, dbuf, dhacc,
+                                    Ht, zyb, ctl, st, tm);
+        const int64_t count = p.n * p.D;
+        int64_t blocks = cdiv(count, 256);
+        if (blocks > 4096) blocks = 4096;
+        TimedLaunch tl(tm, LCE_K_DH_FINAL, st);
+        hipLaunchKernelGGL(dh_final_kernel<TR>, dim3(unsigned(blocks)), dim3(256), 0, st,
+                           (const Acc *)dhacc, p.pdh_splits, count, dH,
+                           (const int32_t *)&ctl->bad);
+        return;
+      }
     }
   }
   for (int64_t s = 0; s < p.n_slabs; ++s) {

@@ -107,6 +107,53 @@ int32_t plan_ce(int64_t n, int64_t D, int64_t V, int64_t chunk, int32_t dtype, C
   }
   q.dh_splits = dh_splits_for(q.slab);
 
+  // bf16 slab pipeline: two buffers of pslab rows, 2 * pslab * d_ld <= budget.
+  // Modelled per launch as max(total workgroup work / CUs, longest workgroup)
+  // with work = depth (x 1.25 for the MN-major d_hidden operands) + epilogue;
+  // the split count of d_hidden is part of the search.
+  if (bf) {
+    const int64_t half = budget / (2 * q.d_ld) / tile_m * tile_m;
+    const int64_t tn = ceil_div(n, tile_m), td = ceil_div(D, tile_n);
+    const int64_t kEpi = 256, kLaunch = 64;
+    auto launch_cost = [&](int64_t prev_rows, int64_t next_rows, int64_t sp) {
+      int64_t work = 0, longest = 0;
+      if (prev_rows > 0) {
+        const int64_t tm = ceil_div(prev_rows, tile_m);
+        const int64_t dh_wg = (ceil_div(prev_rows, sp) * 5) / 4 + kEpi;
+        work += out_tiles * sp * dh_wg + tm * td * (n + kEpi);
+        longest = dh_wg > n + kEpi ? dh_wg : n + kEpi;
+      }
+      if (next_rows > 0) {
+        const int64_t tm = ceil_div(next_rows, tile_m);
+        work += tm * tn * (D + kEpi);
+        if (D + kEpi > longest) longest = D + kEpi;
+      }
+      const int64_t spread = ceil_div(work, kComputeUnits);
+      return (spread > longest ? spread : longest) + kLaunch;
+    };
+    int64_t best = -1, best_sp = 1, best_cost = 0;
+    for (int64_t S = tile_m; S <= half; S += tile_m) {
+      const int64_t ns = ceil_div(V, S);
+      for (int64_t sp = 1; sp <= 16; sp *= 2) {
+        if (sp > 1 && S / sp < 512) break;
+        // launches: (-, 0), (0, 1), ..., (ns-2, ns-1), (ns-1, -)
+        const int64_t last = V - (ns - 1) * S;
+        int64_t c = launch_cost(0, ns == 1 ? last : S, sp);
+        if (ns >= 3) c += (ns - 2) * launch_cost(S, S, sp);
+        if (ns >= 2) c += launch_cost(S, last, sp);
+        c += launch_cost(last, 0, sp);
+        if (best < 0 || c < best_cost || (c == best_cost && S > best)) {
+          best = S; best_sp = sp; best_cost = c;
+        }
+      }
+    }
+    if (best > 0) {
+      q.pslab = best < V ? best : round_up(V, 1);
+      q.pn_slabs = ceil_div(V, q.pslab);
+      q.pdh_splits = best_sp;
+    }
+  }
+
   // Workspace: [control | forward partials | zy | per-token loss] and the
   // backward's [slab buffer | d_hidden split accumulators] overlap the
   // forward region (the two calls never run on one workspace at once).
@@ -121,9 +168,16 @@ int32_t plan_ce(int64_t n, int64_t D, int64_t V, int64_t chunk, int32_t dtype, C
   size_t fwd_end = off;
   off = fwd_begin;
   q.off_dbuf = off;
-  off = align256(off + size_t(q.slab) * size_t(q.d_ld) * q.elem);
+  {
+    int64_t cells = q.slab * q.d_ld;
+    if (2 * q.pslab * q.d_ld > cells) cells = 2 * q.pslab * q.d_ld;
+    off = align256(off + size_t(cells) * q.elem);
+  }
   q.off_dhacc = off;
-  off = align256(off + size_t(q.dh_splits) * size_t(n) * size_t(D) * q.acc);
+  {
+    const int64_t sp = q.dh_splits > q.pdh_splits ? q.dh_splits : q.pdh_splits;
+    off = align256(off + size_t(sp) * size_t(n) * size_t(D) * q.acc);
+  }
   q.off_ht = off;
   if (bf) off = align256(off + size_t(D) * size_t(q.d_ld) * q.elem);
   q.off_zyb = off;

@@ -211,8 +211,16 @@ struct EpiPrefetch<E, std::void_t<decltype(E::kPrefetchBytes)>> {
   static constexpr int bytes = E::kPrefetchBytes;
 };
 
+// LDS bytes a product needs (ring + epilogue prefetch table).
+template <class CFG, class Epi> constexpr int gemm2_lds_bytes() {
+  return CFG::STAGES * CFG::STAGE_BYTES + EpiPrefetch<Epi>::bytes;
+}
+
+// One workgroup of a product: `bid` of `nb` workgroups of this product, `smem`
+// at least gemm2_lds_bytes<CFG, Epi>() bytes (1 KB aligned).
 template <class CFG, class TR, bool AK, bool BKM, class Epi>
-__global__ void __launch_bounds__(TR::NT) gemm2_kernel(Gemm2Params g, Epi epi) {
+__device__ __forceinline__ void gemm2_block(const Gemm2Params &g, const Epi &epi, int64_t bid,
+                                            int64_t nb, char *smem) {
   constexpr int BK = CFG::BK, STAGES = CFG::STAGES, KSUB = CFG::KSUB;
   constexpr int NWAVES = TR::NT / 64;
   typedef PipeOperand<CFG, NWAVES, AK> OpA;
@@ -224,7 +232,6 @@ __global__ void __launch_bounds__(TR::NT) gemm2_kernel(Gemm2Params g, Epi epi) {
   static_assert(TR::BM == CFG::BM && TR::BN == CFG::BN, "tile");
   if (g.bad && *g.bad) return;
   constexpr int PRE = EpiPrefetch<Epi>::bytes;
-  __shared__ __attribute__((aligned(1024))) char smem[STAGES * CFG::STAGE_BYTES + PRE];
   char *const pre_lds = smem + STAGES * CFG::STAGE_BYTES;
 
   const int tid = threadIdx.x;
@@ -236,7 +243,7 @@ __global__ void __launch_bounds__(TR::NT) gemm2_kernel(Gemm2Params g, Epi epi) {
   // contiguous ranges: an XCD's workgroups share whole K-splits, so each
   // split's operand rows are fetched into one L2 only.
   const int64_t tiles = (g.M + CFG::BM - 1) / CFG::BM * g.tiles_n;
-  const int64_t LS = xcd_remap(blockIdx.x, gridDim.x);
+  const int64_t LS = xcd_remap(bid, nb);
   const int split = int(LS / tiles);
   const int64_t L = LS % tiles;
   const int64_t m0 = (L / g.tiles_n) * CFG::BM;
@@ -362,6 +369,47 @@ __global__ void __launch_bounds__(TR::NT) gemm2_kernel(Gemm2Params g, Epi epi) {
   } else {
     epi(acc, m0_e, n0_e, wm_e, wn_e, lane_e, split);
   }
+}
+
+template <class CFG, class TR, bool AK, bool BKM, class Epi>
+__global__ void __launch_bounds__(TR::NT) gemm2_kernel(Gemm2Params g, Epi epi) {
+  __shared__ __attribute__((aligned(1024))) char smem[gemm2_lds_bytes<CFG, Epi>()];
+  gemm2_block<CFG, TR, AK, BKM, Epi>(g, epi, blockIdx.x, gridDim.x, smem);
+}
+
+// One product of a multi-product launch.
+template <class CFG_, bool AK_, bool BKM_, class Epi_>
+struct Gemm2Job {
+  typedef CFG_ CFG;
+  typedef Epi_ Epi;
+  static constexpr bool AK = AK_, BKM = BKM_;
+  Gemm2Params g;
+  Epi e;
+  int64_t nb;   // workgroups (0: the product is absent from this launch)
+};
+
+// Three independent products in one grid: workgroups [0, j0.nb) run j0, the
+// next j1.nb run j1, then j2.  Longer-running products go first so that the
+// store-bound epilogues of early finishers overlap later products' main loops.
+template <class TR, class J0, class J1, class J2>
+__global__ void __launch_bounds__(TR::NT) gemm2_multi_kernel(J0 j0, J1 j1, J2 j2) {
+  constexpr int B0 = gemm2_lds_bytes<typename J0::CFG, typename J0::Epi>();
+  constexpr int B1 = gemm2_lds_bytes<typename J1::CFG, typename J1::Epi>();
+  constexpr int B2 = gemm2_lds_bytes<typename J2::CFG, typename J2::Epi>();
+  constexpr int B01 = B0 > B1 ? B0 : B1;
+  __shared__ __attribute__((aligned(1024))) char smem[B01 > B2 ? B01 : B2];
+  int64_t b = blockIdx.x;
+  if (b < j0.nb) {
+    gemm2_block<typename J0::CFG, TR, J0::AK, J0::BKM>(j0.g, j0.e, b, j0.nb, smem);
+    return;
+  }
+  b -= j0.nb;
+  if (b < j1.nb) {
+    gemm2_block<typename J1::CFG, TR, J1::AK, J1::BKM>(j1.g, j1.e, b, j1.nb, smem);
+    return;
+  }
+  b -= j1.nb;
+  gemm2_block<typename J2::CFG, TR, J2::AK, J2::BKM>(j2.g, j2.e, b, j2.nb, smem);
 }
 
 }  // namespace lce

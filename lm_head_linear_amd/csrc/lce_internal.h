@@ -45,6 +45,11 @@ struct CEPlan {
   int64_t n_slabs = 0;
   int64_t d_ld = 0;           // row stride (tokens) of the slab buffer
   int64_t dh_splits = 0;      // split-K factor of the d_hidden product
+  // bf16 slab pipeline (two slab buffers; one launch runs d_hidden and
+  // d_weight of slab k with the logit gradient of slab k+1)
+  int64_t pslab = 0;          // vocabulary rows per buffer
+  int64_t pn_slabs = 0;
+  int64_t pdh_splits = 0;
   // workspace layout (byte offsets)
   size_t off_partials = 0, off_zy = 0, off_losstok = 0;
   size_t off_dbuf = 0, off_dhacc = 0;

@@ -44,9 +44,9 @@ class Peak(ctypes.Structure):
                 ("status", ctypes.c_int32)]
 
 
-NUM_KERNELS = 9
+NUM_KERNELS = 10
 KERNEL_KINDS = {"guard": 0, "fwd_gemm": 1, "fwd_merge": 2, "reduce": 3, "dlogit_gemm": 4,
-                "dw_gemm": 5, "dh_gemm": 6, "dh_final": 7, "distill": 8}
+                "dw_gemm": 5, "dh_gemm": 6, "dh_final": 7, "distill": 8, "bwd_gemm": 9}
 
 
 class TimerSlot(ctypes.Structure):
