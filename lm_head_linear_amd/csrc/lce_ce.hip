@@ -758,7 +758,19 @@ static void forward_impl(const CEPlan &p, const void *H, const void *W, const in
     FwdLseEpi<TR> epi{ntok, p.V, p.n_vparts, partials};
     {
       TimedLaunch tl(tm, LCE_K_FWD_GEMM, st);
-      launch_any<TR, true, true>(UsePipe<TR>::ok(vec, p.D, p.d_ld), vec, g, 1, epi, st);
+      bool done = false;
+      if constexpr (std::is_same<TR, TraitsBF16>::value) {
+        if (UsePipe<TR>::ok(vec, p.D, p.d_ld)) {  // persistent: one workgroup per CU
+          typedef TraitsBF16W8 TRP;
+          const int64_t tiles = cdiv(g.M, PipeKK::BM) * g.tiles_n;
+          const int64_t grid = tiles < kComputeUnits ? tiles : kComputeUnits;
+          const auto e = retrait<TRP>(epi);
+          hipLaunchKernelGGL((gemm2_persistent_kernel<PipeKK, TRP, decltype(e)>),
+                             dim3(unsigned(grid)), dim3(TRP::NT), 0, st, to_gemm2<PipeKK>(g), e);
+          done = true;
+        }
+      }
+      if (!done) launch_any<TR, true, true>(false, vec, g, 1, epi, st);
     }
     TimedLaunch tl(tm, LCE_K_FWD_MERGE, st);
     hipLaunchKernelGGL(fwd_merge_kernel<Acc>, dim3(unsigned(cdiv(ntok, 4))), dim3(256), 0, st,

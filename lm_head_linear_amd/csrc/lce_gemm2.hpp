@@ -120,7 +120,13 @@ struct PipeOperand {
     }
   }
 
-  // Issue this wave's 4 loads of k-step k0 into the operand region `dst`.
+  // K-major: point the loads at the tile whose first row is row0_.
+  __device__ inline void retarget(int64_t row0_) {
+    row0 = row0_;
+    rs = make_rsrc(p + row0 * ld, (row_lim - row0) * ld * 2);
+  }
+
+  // Issue this wave's loads of k-step k0 into the operand region `dst`.
   __device__ inline void issue(int64_t k0, char *dst, int wave) const {
     if (KMAJOR) {
 #pragma unroll
@@ -375,6 +381,153 @@ template <class CFG, class TR, bool AK, bool BKM, class Epi>
 __global__ void __launch_bounds__(TR::NT) gemm2_kernel(Gemm2Params g, Epi epi) {
   __shared__ __attribute__((aligned(1024))) char smem[gemm2_lds_bytes<CFG, Epi>()];
   gemm2_block<CFG, TR, AK, BKM, Epi>(g, epi, blockIdx.x, gridDim.x, smem);
+}
+
+// Persistent form for K-major x K-major products with one K-split and a
+// register-only epilogue (the forward's online LSE): one workgroup per CU
+// walks its tiles as a single stream of k-steps, so the operand ring keeps
+// loading the next tile's first stages while the current tile finishes its
+// last k-steps and its epilogue, and no tile starts on an empty pipeline.
+// Tiles are dealt as xcd_remap does: each XCD owns a contiguous range of
+// logical tiles and its workgroups take consecutive tiles of it in rounds.
+template <class CFG, class TR, class Epi>
+__global__ void __launch_bounds__(TR::NT) gemm2_persistent_kernel(Gemm2Params g, Epi epi) {
+  constexpr int BK = CFG::BK, STAGES = CFG::STAGES, KSUB = CFG::KSUB;
+  constexpr int NWAVES = TR::NT / 64;
+  typedef PipeOperand<CFG, NWAVES, true> Op;
+  constexpr int LPS = 2 * Op::INSTR;
+  constexpr int NMF = TR::FM * TR::FN;
+  constexpr int NDS = TR::FM + TR::FN;
+  static_assert(KSUB % 2 == 0 && KSUB >= 2, "fragment double-buffer parity");
+  static_assert(!EpiStaged<Epi>::value && EpiPrefetch<Epi>::bytes == 0, "register epilogue");
+  if (g.bad && *g.bad) return;
+  __shared__ __attribute__((aligned(1024))) char smem[STAGES * CFG::STAGE_BYTES];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int wm = wave / TR::WAVES_N, wn = wave % TR::WAVES_N;
+
+  // this workgroup's tiles: lo + slot + j * per_xcd, j = 0.., below hi
+  const int64_t tiles = (g.M + CFG::BM - 1) / CFG::BM * g.tiles_n;
+  const int64_t X = 8, nb = gridDim.x;
+  const int64_t xcd = blockIdx.x % X, slot = blockIdx.x / X;
+  const int64_t per_xcd = nb / X + (xcd < nb % X ? 1 : 0);
+  const int64_t q8 = tiles / X, r8 = tiles % X;
+  const int64_t lo = xcd < r8 ? xcd * (q8 + 1) : r8 * (q8 + 1) + (xcd - r8) * q8;
+  const int64_t hi = lo + q8 + (xcd < r8 ? 1 : 0);
+  const int64_t my_tiles = lo + slot < hi ? (hi - lo - slot + per_xcd - 1) / per_xcd : 0;
+  const int n_k = int((g.K + BK - 1) / BK);
+  if (my_tiles == 0 || n_k == 0) return;
+  const int64_t total = my_tiles * n_k;
+  auto tile_m0 = [&](int64_t j) { return ((lo + slot + j * per_xcd) / g.tiles_n) * CFG::BM; };
+  auto tile_n0 = [&](int64_t j) { return ((lo + slot + j * per_xcd) % g.tiles_n) * CFG::BN; };
+
+  typename TR::AccBlock acc[TR::FM][TR::FN];
+#pragma unroll
+  for (int fm = 0; fm < TR::FM; ++fm)
+#pragma unroll
+    for (int fn = 0; fn < TR::FN; ++fn)
+#pragma unroll
+      for (int r = 0; r < TR::R; ++r) acc[fm][fn][r] = 0;
+
+  // Load stream: the next global k-step to load is k-step ld_k of tile
+  // ld_t; stage slots rotate with the global step.
+  Op pa, pb;
+  pa.init(static_cast<const uint16_t *>(g.A), g.lda, tile_m0(0), g.M, g.K, wave, lane);
+  pb.init(static_cast<const uint16_t *>(g.B), g.ldb, tile_n0(0), g.N, g.K, wave, lane);
+  int64_t ld_t = 0;
+  int ld_k = 0;
+  auto issue = [&](int64_t q) {
+    if (ld_k == n_k) {
+      ld_k = 0;
+      ++ld_t;
+      pa.retarget(tile_m0(ld_t));
+      pb.retarget(tile_n0(ld_t));
+    }
+    char *st = smem + (q % STAGES) * CFG::STAGE_BYTES;
+    const int64_t k0 = int64_t(ld_k) * BK;
+    pa.issue(k0, st, wave);
+    pb.issue(k0, st + CFG::OP_BYTES, wave);
+    ++ld_k;
+  };
+  int64_t cp_t = 0;   // tile being computed
+  int cp_k = 0;       // its k-step
+
+#pragma unroll
+  for (int s2 = 0; s2 < STAGES; ++s2)
+    if (s2 < total) issue(s2);
+  wait_vm_barrier_stages<LPS, STAGES - 1>(int(total - 1 < STAGES - 1 ? total - 1 : STAGES - 1));
+  u32x4 fa[2][TR::FM], fb[2][TR::FN];
+#pragma unroll
+  for (int f = 0; f < TR::FM; ++f) fa[0][f] = pa.frag(smem, wm * TR::WTM + f * 32, 0, lane);
+#pragma unroll
+  for (int f = 0; f < TR::FN; ++f)
+    fb[0][f] = pb.frag(smem + CFG::OP_BYTES, wn * TR::WTN + f * 32, 0, lane);
+
+  auto step = [&](const int64_t q, auto steady_tag) {
+    constexpr bool STEADY = decltype(steady_tag)::value;
+    char *sa = smem + (q % STAGES) * CFG::STAGE_BYTES;
+    const char *sn = smem + ((q + 1) % STAGES) * CFG::STAGE_BYTES;
+#pragma unroll
+    for (int kk = 0; kk < KSUB; ++kk) {
+      const int cur = kk & 1, nxt = cur ^ 1;
+      const bool last = kk == KSUB - 1;
+      if (!last || STEADY || q + 1 < total) {
+        const char *src = last ? sn : sa;
+        const int ks = last ? 0 : kk + 1;
+#pragma unroll
+        for (int f = 0; f < TR::FM; ++f) fa[nxt][f] = pa.frag(src, wm * TR::WTM + f * 32, ks, lane);
+#pragma unroll
+        for (int f = 0; f < TR::FN; ++f)
+          fb[nxt][f] = pb.frag(src + CFG::OP_BYTES, wn * TR::WTN + f * 32, ks, lane);
+      }
+#pragma unroll
+      for (int fm = 0; fm < TR::FM; ++fm)
+#pragma unroll
+        for (int fn = 0; fn < TR::FN; ++fn)
+          acc[fm][fn] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+              __builtin_bit_cast(bf16x8, fa[cur][fm]), __builtin_bit_cast(bf16x8, fb[cur][fn]),
+              acc[fm][fn], 0, 0, 0);
+      constexpr int NDS_I = NDS < NMF ? NDS : NMF;
+      if (last && STEADY) {
+#pragma unroll
+        for (int i = 0; i < NMF; ++i) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          if (i < LPS) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+          if (i < NDS_I) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        }
+      } else if (!last) {
+#pragma unroll
+        for (int i = 0; i < NMF; ++i) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          if (i < NDS_I) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        }
+      }
+      if (kk == KSUB - 2) {
+        if (STEADY) wait_vm_barrier<LPS * (STAGES - 2)>();
+        else wait_vm_barrier_stages<LPS, STAGES - 2>(int(total - 2 - q));
+        if (STEADY || q + STAGES < total) issue(q + STAGES);
+      }
+    }
+    if (++cp_k == n_k) {   // tile cp_t is complete
+      cp_k = 0;
+      const int64_t j = cp_t++;
+      int lane_e = lane, wm_e = wm, wn_e = wn;
+      int64_t m0_e = tile_m0(j), n0_e = tile_n0(j);
+      asm volatile("" : "+v"(lane_e), "+v"(wm_e), "+v"(wn_e), "+v"(m0_e), "+v"(n0_e));
+      epi(acc, m0_e, n0_e, wm_e, wn_e, lane_e, 0);
+#pragma unroll
+      for (int fm = 0; fm < TR::FM; ++fm)
+#pragma unroll
+        for (int fn = 0; fn < TR::FN; ++fn)
+#pragma unroll
+          for (int r = 0; r < TR::R; ++r) acc[fm][fn][r] = 0;
+    }
+  };
+  int64_t q = 0;
+  for (; q + STAGES < total; ++q) step(q, std::true_type{});
+  for (; q < total; ++q) step(q, std::false_type{});
 }
 
 // One product of a multi-product launch.
