@@ -72,6 +72,51 @@ def traffic_from_profiles(workload: str, kind: str):
     return None
 
 
+def distill_measure(lce, torch, np, dev, steps: int):
+    """lce_distill_fwd_bwd on the 4096 x 151936 bf16 distillation workload
+    (T = 2, 10% masked, z 1e-4) for the three objectives: kernel time from
+    HIP events and HBM throughput on the algorithmic bytes 2*V*(2*C + n) + n
+    (student and teacher read for counted rows, the gradient written for every
+    row, the mask read)."""
+    from tests import synthetic as syn
+    w = syn.DISTILL_BF16
+    log(f"bench: distillation {w.name}: generating inputs")
+    x = syn.distill_inputs(w)
+    S, U = x.student.to(dev), x.teacher.to(dev)
+    mk = torch.from_numpy(x.mask).to(dev)
+    n, V = S.shape
+    C = int(x.mask.sum())
+    g = torch.empty_like(S)
+    ws = torch.empty(lce.lce_distill_workspace_bytes(n, V), dtype=torch.uint8, device=dev)
+    nbytes = 2 * V * (2 * C + n) + n
+    res = {"workload": w.name, "n_tok": n, "vocab": V, "counted": C, "temperature": w.temperature,
+           "algorithmic_bytes": nbytes, "peak_GBs": PEAK_HBM_GBS, "objectives": {}}
+    for obj, name in ((0, "ce"), (1, "forward_kl"), (2, "reverse_kl")):
+        def call(timer=None):
+            st, out = lce.lce_distill_fwd_bwd(S, U, mk, n, V, obj, w.temperature, w.z_coef, 1.0, g,
+                                             ws, timer=timer)
+            if st != lce.OK:
+                raise lce.LceError(st, "lce_distill_fwd_bwd")
+            return out
+        for _ in range(2):
+            call()
+        t0 = time.perf_counter()
+        for _ in range(steps):
+            out = call()
+        wall = (time.perf_counter() - t0) / steps * 1e3
+        timer = lce.KernelTimer(["distill"], capacity=steps * 4)
+        for _ in range(steps):
+            call(timer)
+        torch.cuda.synchronize()
+        d = timer.durations_ms("distill")
+        k_ms = float(np.sum(d)) / steps
+        res["objectives"][name] = {"call_ms": round(wall, 4), "kernel_ms": round(k_ms, 4),
+                                   "GBs": round(nbytes / (k_ms / 1e3) / 1e9, 1),
+                                   "frac": round(nbytes / (k_ms / 1e3) / 1e9 / PEAK_HBM_GBS, 4),
+                                   "loss": out.loss_mean}
+    return res
+
+
 def cpu_baseline(w, x, tokens: int):
     """The oracle, as it stands, on the first `tokens` tokens of the workload:
     forward (all tokens of the prefix) + backward (d_hidden of the prefix and
@@ -108,6 +153,8 @@ def main():
                          "reference for the FETCH_SIZE / WRITE_SIZE counters)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-kernel-events", action="store_true")
+    ap.add_argument("--no-distill", action="store_true",
+                    help="skip the distillation measurement (4096 x 151936 bf16)")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -202,6 +249,30 @@ def main():
             step(timer)
         torch.cuda.synchronize()
 
+    # Split pass: forward and backward device time per step (events between
+    # the calls only); then the same with L2 and the Infinity Cache flushed by
+    # a 512 MB scratch write before every step ("cold").
+    split = {"fwd_ms": [], "bwd_ms": [], "cold_fwd_ms": [], "cold_bwd_ms": []}
+    scratch = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+    for i in range(2 * args.steps):
+        cold = i >= args.steps
+        if cold:
+            scratch.fill_(i & 0xff)
+        ea, eb, ec = (torch.cuda.Event(enable_timing=True) for _ in range(3))
+        ea.record()
+        st, _ = lce.lce_forward(H, W, y, m, n, D, V, chunk, z, lse, ws, sync=False)
+        eb.record()
+        st2 = lce.lce_backward(H, W, y, m, lse, n, D, V, chunk, z, 1.0, dH, dW, 0, ws)
+        ec.record()
+        torch.cuda.synchronize()
+        if st != lce.OK or st2 != lce.OK:
+            raise lce.LceError(st if st != lce.OK else st2, "split pass")
+        split["cold_fwd_ms" if cold else "fwd_ms"].append(ea.elapsed_time(eb))
+        split["cold_bwd_ms" if cold else "bwd_ms"].append(eb.elapsed_time(ec))
+    del scratch
+    split = {k: {"median": round(float(np.median(v)), 4), "min": round(float(np.min(v)), 4)}
+             for k, v in split.items()}
+
     flop_gemm = 2.0 * n * D * V                  # one GEMM pass over every (token, vocab) pair
     f8 = 4 * flop_gemm                            # forward + recompute + dH + dW
     f6 = 3 * flop_gemm
@@ -227,6 +298,10 @@ def main():
         roof = {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak, "unit": "TFLOP/s",
                 "frac": round(achieved / peak, 4), "traffic": traffic_from_profiles(w.name, dom),
                 "kernel": dom, "flops_per_launch": per_launch_flops, "avg_launch_ms": kd["avg_ms"]}
+
+    distill = None
+    if not args.no_distill and w.dtype == "bf16":
+        distill = distill_measure(lce, torch, np, dev, args.steps)
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -256,8 +331,10 @@ def main():
         "gpu_ms_per_step_events": round(gpu_ms / args.steps, 4),
         "workspace_bytes": ws_bytes,
         "peak_extra_bytes": int(peak_extra),
+        "fwd_bwd_split": split,
         "kernels": kernels,
         "roofline": roof,
+        "distill": distill,
         "cpu_baseline": cpu,
     }
     print(json.dumps(res), flush=True)

@@ -195,7 +195,7 @@ struct FwdLseEpi {
 template <class TR>
 __global__ void target_logit_kernel(const typename TR::E *H, const typename TR::E *W,
                                     const int64_t *y, int64_t n, int64_t D,
-                                    typename TR::Acc *zy, const int32_t *bad) {
+                                    typename TR::Acc *zy, const int32_t *bad, int vec8) {
   typedef typename TR::Acc Acc;
   if (*bad) return;
   const int lane = threadIdx.x & 63;
@@ -204,7 +204,25 @@ __global__ void target_logit_kernel(const typename TR::E *H, const typename TR::
   const typename TR::E *h = H + t * D;
   const typename TR::E *w = W + y[t] * D;
   Acc s = 0;
-  for (int64_t d = lane; d < D; d += 64) s += to_acc<TR>(h[d]) * to_acc<TR>(w[d]);
+  if constexpr (std::is_same<typename TR::E, uint16_t>::value) {
+    // 16-byte chunks of 8 bf16 (rows 16-byte aligned and D % 8 == 0: the
+    // host passes vec8 only then), lane-strided, then the scalar remainder
+    if (vec8) {
+      for (int64_t c = lane; c < D / 8; c += 64) {
+        const u32x4 a = *reinterpret_cast<const u32x4 *>(h + 8 * c);
+        const u32x4 b = *reinterpret_cast<const u32x4 *>(w + 8 * c);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          s = fmaf(__uint_as_float(a[j] << 16), __uint_as_float(b[j] << 16), s);
+          s = fmaf(__uint_as_float(a[j] & 0xffff0000u), __uint_as_float(b[j] & 0xffff0000u), s);
+        }
+      }
+    } else {
+      for (int64_t d = lane; d < D; d += 64) s += to_acc<TR>(h[d]) * to_acc<TR>(w[d]);
+    }
+  } else {
+    for (int64_t d = lane; d < D; d += 64) s += to_acc<TR>(h[d]) * to_acc<TR>(w[d]);
+  }
   for (int o = 32; o > 0; o >>= 1) s += __shfl_down(s, o);
   if (lane == 0) zy[t] = s;
 }
@@ -606,9 +624,28 @@ __global__ void zero_f32_kernel(float *p, int64_t count) {
 // d_hidden = sum over splits (ascending) of the split accumulators.
 template <class TR>
 __global__ void dh_final_kernel(const typename TR::Acc *P, int64_t splits, int64_t count,
-                                typename TR::E *out, const int32_t *bad) {
+                                typename TR::E *out, const int32_t *bad, int vec4) {
   if (*bad) return;
-  for (int64_t i = int64_t(blockIdx.x) * blockDim.x + threadIdx.x; i < count;
+  int64_t begin = 0;
+  if constexpr (std::is_same<typename TR::Acc, float>::value) {
+    // four consecutive elements per thread: 16-byte loads, one 8-byte store
+    // (count % 4 == 0 and out 8-byte aligned: the host passes vec4 only then)
+    if (vec4) {
+      typedef float f32x4_t __attribute__((ext_vector_type(4)));
+      for (int64_t i = int64_t(blockIdx.x) * blockDim.x + threadIdx.x; i < count / 4;
+           i += int64_t(gridDim.x) * blockDim.x) {
+        f32x4_t s = {0.f, 0.f, 0.f, 0.f};
+        for (int64_t j = 0; j < splits; ++j)
+          s += *reinterpret_cast<const f32x4_t *>(P + j * count + 4 * i);
+        uint2 o;
+        o.x = uint32_t(to_elem<TR>(s[0])) | (uint32_t(to_elem<TR>(s[1])) << 16);
+        o.y = uint32_t(to_elem<TR>(s[2])) | (uint32_t(to_elem<TR>(s[3])) << 16);
+        *reinterpret_cast<uint2 *>(out + 4 * i) = o;
+      }
+      begin = count / 4 * 4;
+    }
+  }
+  for (int64_t i = begin + int64_t(blockIdx.x) * blockDim.x + threadIdx.x; i < count;
        i += int64_t(gridDim.x) * blockDim.x) {
     typename TR::Acc s = 0;
     for (int64_t j = 0; j < splits; ++j) s += P[j * count + i];
@@ -635,6 +672,10 @@ TimedLaunch::~TimedLaunch() {
 static int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
 static bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+// the d_hidden fold may use 4-element chunks
+static int fold_vec4(int64_t count, const void *out) {
+  return count % 4 == 0 && (reinterpret_cast<uintptr_t>(out) & 7u) == 0;
+}
 
 static uint8_t *ws_base(const lce_tensor *ws) {
   uintptr_t p = reinterpret_cast<uintptr_t>(ws->data);
@@ -743,7 +784,7 @@ static void forward_impl(const CEPlan &p, const void *H, const void *W, const in
     TimedLaunch tl(tm, LCE_K_FWD_MERGE, st);
     hipLaunchKernelGGL(target_logit_kernel<TR>, dim3(unsigned(cdiv(p.n, 4))), dim3(256), 0, st,
                        Hp, static_cast<const typename TR::E *>(W), y, p.n, p.D, zy,
-                       (const int32_t *)&ctl->bad);
+                       (const int32_t *)&ctl->bad, vec ? 1 : 0);
   }
   for (int64_t tok0 = 0; tok0 < p.n; tok0 += p.tok_per_pass) {
     const int64_t ntok = p.tok_per_pass < p.n - tok0 ? p.tok_per_pass : p.n - tok0;
@@ -886,7 +927,7 @@ static void backward_impl(const CEPlan &p, const void *H, const void *W, const i
       // target logits for the staged logit-gradient epilogue
       zyb = reinterpret_cast<Acc *>(ws + p.off_zyb);
       hipLaunchKernelGGL(target_logit_kernel<TR>, dim3(unsigned(cdiv(p.n, 4))), dim3(256), 0, st,
-                         Hp, Wp, y, p.n, p.D, zyb, (const int32_t *)&ctl->bad);
+                         Hp, Wp, y, p.n, p.D, zyb, (const int32_t *)&ctl->bad, vec ? 1 : 0);
       if (p.pslab > 0) {
         if (accumulate)
           backward_pipelined<true>(p, Hp, Wp, y, mask, lse, z_coef, grad_out, dW, dbuf, dhacc,
@@ -900,7 +941,7 @@ static void backward_impl(const CEPlan &p, const void *H, const void *W, const i
         TimedLaunch tl(tm, LCE_K_DH_FINAL, st);
         hipLaunchKernelGGL(dh_final_kernel<TR>, dim3(unsigned(blocks)), dim3(256), 0, st,
                            (const Acc *)dhacc, p.pdh_splits, count, dH,
-                           (const int32_t *)&ctl->bad);
+                           (const int32_t *)&ctl->bad, fold_vec4(count, dH));
         return;
       }
     }
@@ -967,7 +1008,8 @@ static void backward_impl(const CEPlan &p, const void *H, const void *W, const i
   if (blocks > 4096) blocks = 4096;
   TimedLaunch tl(tm, LCE_K_DH_FINAL, st);
   hipLaunchKernelGGL(dh_final_kernel<TR>, dim3(unsigned(blocks)), dim3(256), 0, st,
-                     (const Acc *)dhacc, p.dh_splits, count, dH, (const int32_t *)&ctl->bad);
+                     (const Acc *)dhacc, p.dh_splits, count, dH, (const int32_t *)&ctl->bad,
+                     fold_vec4(count, dH));
 }
 
 }  // namespace lce

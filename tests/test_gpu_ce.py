@@ -7,6 +7,8 @@ relative error <= 2e-3 and gradients max|diff| <= 1e-2 * max|ref|.
 """
 import math
 
+import os
+
 import numpy as np
 import pytest
 import torch
@@ -258,6 +260,54 @@ def test_qwen_head_bf16_full_size():
     th = _sample(rng, c.n, 6)
     vw = _sample(rng, c.V, 6)
     vw = np.unique(np.concatenate([vw, c.x.targets[th]]))
+    _say(f"  oracle d_hidden rows {th.tolist()} and d_weight rows {vw.tolist()}")
+    rdH = oracle.backward_dh_rows(c.H64, c.W64, c.x.targets, ref["lse"], th, mask=c.x.mask,
+                                  z_coef=c.z)
+    rdW = oracle.backward_dw_rows(c.H64, c.W64, c.x.targets, ref["lse"], vw, mask=c.x.mask,
+                                  z_coef=c.z)
+    check_grads(c, dH, dW, rdH, rdW, rows_h=th, rows_w=vw)
+
+
+def read_large_golden():
+    """Oracle lse and loss scalars of the 8192 x 4096 x 128256 workload, written
+    by tests/golden/make_large_bf16_lse.py (a full fp64 forward takes minutes)."""
+    path = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden",
+                        "large_head_bf16_8192x4096x128256_lse.txt")
+    vals, lse = {}, []
+    with open(path) as f:
+        in_lse = False
+        for line in f:
+            if line.startswith("#"):
+                continue
+            if in_lse:
+                lse.append(float(line))
+            elif line.strip() == "lse":
+                in_lse = True
+            else:
+                k, v = line.split()
+                vals[k] = float(v)
+    C = int(vals["n_counted"])
+    return {"n_counted": C, "loss_sum": vals["loss_sum"], "z_sum": vals["z_sum"],
+            "loss_mean": vals["loss_sum"] / C, "z_mean": vals["z_sum"] / C,
+            "lse": np.array(lse)}
+
+
+def test_large_head_bf16_full_size():
+    """8192 x 4096 x 128256 bf16, Zipf targets, chunk 512, z 1e-4: every token's lse
+    and the loss against the stored oracle forward; sampled gradient rows against
+    the oracle computed here."""
+    w = syn.LARGE_BF16
+    _say(f"case {w.name}: generating inputs")
+    c = Case(w)
+    fwd = c.gpu_forward(w.chunk)
+    dH, dW = c.gpu_backward(fwd.lse, w.chunk)
+    torch.cuda.synchronize()
+    ref = read_large_golden()
+    assert ref["lse"].shape == (c.n,)
+    check_forward(c, fwd, ref)
+    rng = np.random.default_rng(97)
+    th = _sample(rng, c.n, 4)
+    vw = np.unique(np.concatenate([_sample(rng, c.V, 4), c.x.targets[th]]))
     _say(f"  oracle d_hidden rows {th.tolist()} and d_weight rows {vw.tolist()}")
     rdH = oracle.backward_dh_rows(c.H64, c.W64, c.x.targets, ref["lse"], th, mask=c.x.mask,
                                   z_coef=c.z)

@@ -490,3 +490,25 @@ def test_distill_refusals_and_rows():
     g, rl, rz = oracle.distill_rows(S[rows], U[rows], full["n_counted"], row_mask=m[rows],
                                     objective=2, temperature=2.0, z_coef=0.1)
     assert np.array_equal(g, full["grad"][rows])
+
+
+def test_large_golden_file_matches_the_oracle():
+    """The stored lse of the 8192 x 4096 x 128256 workload (written by
+    tests/golden/make_large_bf16_lse.py) is the oracle's: three tokens
+    recomputed here agree to the last bit (per-token dots and the vocabulary
+    reduction do not depend on which tokens run together)."""
+    import os
+    from tests import synthetic as syn
+    path = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden",
+                        "large_head_bf16_8192x4096x128256_lse.txt")
+    lines = [l for l in open(path) if not l.startswith("#")]
+    k = lines.index("lse\n")
+    lse = np.array([float(v) for v in lines[k + 1:]])
+    assert lse.shape == (8192,)
+    w = syn.LARGE_BF16
+    x = syn.ce_inputs(w)
+    toks = np.array([0, 4095, 8191])
+    H = x.hidden[toks].double().numpy()
+    r = oracle.fused_forward(H, x.weight64(), x.targets[toks], chunk=3, z_coef=w.z_coef)
+    assert r["status"] == 580
+    assert np.array_equal(r["lse"], lse[toks])
