@@ -7,16 +7,18 @@
 // z term adds lse^2 to the forward and 2*grad_z*lse*p to the gradient and
 // shares the distillation loss mask and divisor.
 //
-// One workgroup per token row, streaming the row twice (HBM-bound):
+// One workgroup per CU walks token rows, streaming each row twice (HBM-bound):
 //   pass 1 reads student s and teacher u once, keeping online (max, sum exp)
 //          for x = s/T and y = u/T plus one objective accumulator tied to one
 //          of the two running maxima:
 //            0 cross-entropy  A = sum e^(y-my) x      L = lse_x - A/sy
 //            1 forward KL     A = sum e^(y-my) (y-x)  L = A/sy + lse_x - lse_y
 //            2 reverse KL     A = sum e^(x-mx) (x-y)  L = A/sx + lse_y - lse_x
-//   pass 2 re-reads the row (from the 256 MB Infinity Cache for rows in
-//          flight) and writes grad = (grad_out/C)(dL/dx + 2 z lse_x p)/T with
-//          dL/dx = p - q (0, 1) or p (ls - lq - L) (2).
+//   pass 2 re-reads the row and writes grad = (grad_out/C)(dL/dx + 2 z lse_x p)/T
+//          with dL/dx = p - q (0, 1) or p (ls - lq - L) (2).
+// With one 1024-thread workgroup per CU only ~256 rows are in flight (155 MB
+// at a 151936 vocabulary), so the re-read is served by the 256 MB Infinity
+// Cache; gradient stores are non-temporal so they do not evict those rows.
 // Masked rows only write zeros.  Per-row L and lse_x go to the workspace; a
 // fixed-order fp64 reduction forms the means.
 #include <hip/hip_runtime.h>
@@ -56,7 +58,7 @@ template <> struct IO<uint16_t> {  // bf16 bits
       const bf16x2_t h = {static_cast<__bf16>(g[2 * i]), static_cast<__bf16>(g[2 * i + 1])};
       v[i] = __builtin_bit_cast(uint32_t, h);
     }
-    *reinterpret_cast<u32x4 *>(p) = v;
+    __builtin_nontemporal_store(v, reinterpret_cast<u32x4 *>(p));
   }
   __device__ static inline void store1(uint16_t *p, float g) { *p = cvt(g); }
 };
@@ -125,7 +127,8 @@ __device__ inline Online<C> shfl_xor_online(const Online<C> &v, int o) {
   return r;
 }
 
-constexpr int kBlock = 256;
+constexpr int kBlock = 1024;
+constexpr int64_t kRowGrid = 256;   // workgroups: one per compute unit
 
 // Reduce within the block in a fixed order; thread 0 gets the result.
 template <class C>
@@ -142,11 +145,26 @@ __device__ inline void block_merge(Online<C> &v, Online<C> *sh) {
 }
 
 template <class T, int OBJ, bool VEC>
+__device__ __forceinline__ void distill_row(const T *S, const T *U, const uint8_t *mask, int64_t t,
+                                            int64_t V, double inv_T, double z_coef,
+                                            double grad_out, const Control *ctl, T *grad,
+                                            double *row_out);
+
+template <class T, int OBJ, bool VEC>
 __global__ void __launch_bounds__(kBlock)
-distill_row_kernel(const T *S, const T *U, const uint8_t *mask, int64_t V, double inv_T,
-                   double z_coef, double grad_out, const Control *ctl, T *grad, double *row_out) {
+distill_row_kernel(const T *S, const T *U, const uint8_t *mask, int64_t n, int64_t V,
+                   double inv_T, double z_coef, double grad_out, const Control *ctl, T *grad,
+                   double *row_out) {
+  for (int64_t t = blockIdx.x; t < n; t += gridDim.x)
+    distill_row<T, OBJ, VEC>(S, U, mask, t, V, inv_T, z_coef, grad_out, ctl, grad, row_out);
+}
+
+template <class T, int OBJ, bool VEC>
+__device__ __forceinline__ void distill_row(const T *S, const T *U, const uint8_t *mask, int64_t t,
+                                            int64_t V, double inv_T, double z_coef,
+                                            double grad_out, const Control *ctl, T *grad,
+                                            double *row_out) {
   typedef typename IO<T>::C C;
-  const int64_t t = blockIdx.x;
   const T *s_row = S + t * V;
   const T *u_row = U + t * V;
   T *g_row = grad + t * V;
@@ -162,6 +180,7 @@ distill_row_kernel(const T *S, const T *U, const uint8_t *mask, int64_t V, doubl
     if (tid == 0) { row_out[2 * t] = 0.0; row_out[2 * t + 1] = 0.0; }
     return;
   }
+  __syncthreads();   // the previous row's statistics are no longer read
 
   // Pass 1: online statistics.  fx tracks x; fy tracks y.  The objective
   // accumulator rides on fy (objectives 0, 1) or fx (objective 2).
@@ -300,12 +319,13 @@ template <class T, int OBJ>
 void launch_rows(bool vec, const T *S, const T *U, const uint8_t *mask, int64_t n, int64_t V,
                  double inv_T, double z, double go, const Control *ctl, T *grad, double *rows,
                  hipStream_t st) {
+  const unsigned grid = unsigned(n < kRowGrid ? n : kRowGrid);
   if (vec)
-    hipLaunchKernelGGL((distill_row_kernel<T, OBJ, true>), dim3(unsigned(n)), dim3(kBlock), 0, st,
-                       S, U, mask, V, inv_T, z, go, ctl, grad, rows);
+    hipLaunchKernelGGL((distill_row_kernel<T, OBJ, true>), dim3(grid), dim3(kBlock), 0, st, S, U,
+                       mask, n, V, inv_T, z, go, ctl, grad, rows);
   else
-    hipLaunchKernelGGL((distill_row_kernel<T, OBJ, false>), dim3(unsigned(n)), dim3(kBlock), 0, st,
-                       S, U, mask, V, inv_T, z, go, ctl, grad, rows);
+    hipLaunchKernelGGL((distill_row_kernel<T, OBJ, false>), dim3(grid), dim3(kBlock), 0, st, S, U,
+                       mask, n, V, inv_T, z, go, ctl, grad, rows);
 }
 
 template <class T>
