@@ -672,6 +672,7 @@ TimedLaunch::~TimedLaunch() {
 static int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
 static bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+static int64_t round_up8(int64_t x) { return (x + 7) / 8 * 8; }
 // the d_hidden fold may use 4-element chunks
 static int fold_vec4(int64_t count, const void *out) {
   return count % 4 == 0 && (reinterpret_cast<uintptr_t>(out) & 7u) == 0;
@@ -863,7 +864,8 @@ static void backward_pipelined(const CEPlan &p, const uint16_t *Hp, const uint16
       g.bad = &ctl->bad;
       jh.g = to_gemm2<PipeMN>(g);
       jh.e = StoreEpi<TRP, true>{dhacc, D, 0, n, D, n * D};
-      jh.nb = tiles_t * tiles_d * sp;
+      jh.nreal = tiles_t * tiles_d * sp;
+      jh.nb = round_up8(jh.nreal);
       GemmParams h;
       h.A = buf; h.lda = p.d_ld;
       h.B = Ht; h.ldb = p.d_ld;
@@ -874,7 +876,8 @@ static void backward_pipelined(const CEPlan &p, const uint16_t *Hp, const uint16
       h.bad = &ctl->bad;
       jw.g = to_gemm2<PipeKK>(h);
       jw.e = StoreEpi<TRP, ACC_DW>{dW, D, vs0, rows, D, 0};
-      jw.nb = cdiv(rows, 256) * tiles_d;
+      jw.nreal = cdiv(rows, 256) * tiles_d;
+      jw.nb = round_up8(jw.nreal);
     }
     if (k < p.pn_slabs) {  // slab k: recomputed logits -> logit gradient
       const int64_t vs0 = k * S;
@@ -890,7 +893,8 @@ static void backward_pipelined(const CEPlan &p, const uint16_t *Hp, const uint16
       g.bad = &ctl->bad;
       jl.g = to_gemm2<PipeKK>(g);
       jl.e = DlogitEpi<TRP>{y, mask, lse, n, vs0, rows, ctl, grad_out, z_coef, buf, p.d_ld, zyb};
-      jl.nb = cdiv(rows, 256) * tiles_t;
+      jl.nreal = cdiv(rows, 256) * tiles_t;
+      jl.nb = round_up8(jl.nreal);
     }
     TimedLaunch tl(tm, LCE_K_BWD_GEMM, st);
     const int64_t total = jh.nb + jw.nb + jl.nb;

@@ -108,9 +108,12 @@ int32_t plan_ce(int64_t n, int64_t D, int64_t V, int64_t chunk, int32_t dtype, C
   q.dh_splits = dh_splits_for(q.slab);
 
   // bf16 slab pipeline: two buffers of pslab rows, 2 * pslab * d_ld <= budget.
-  // Modelled per launch as max(total workgroup work / CUs, longest workgroup)
-  // with work = depth (x 1.25 for the MN-major d_hidden operands) + epilogue;
-  // the split count of d_hidden is part of the search.
+  // The slab is the largest multiple of 256 rows the budget allows (measured:
+  // fewer, larger launches win; each launch pays fixed prologue/epilogue tails
+  // and one d_hidden read-modify-write).  The d_hidden split count comes from
+  // a model of each launch as max(total workgroup work / CUs, longest
+  // workgroup) with work = depth (x 1.25 for the MN-major d_hidden operands)
+  // + epilogue.
   if (bf) {
     const int64_t half = budget / (2 * q.d_ld) / tile_m * tile_m;
     const int64_t tn = ceil_div(n, tile_m), td = ceil_div(D, tile_n);
@@ -131,24 +134,24 @@ int32_t plan_ce(int64_t n, int64_t D, int64_t V, int64_t chunk, int32_t dtype, C
       const int64_t spread = ceil_div(work, kComputeUnits);
       return (spread > longest ? spread : longest) + kLaunch;
     };
-    int64_t best = -1, best_sp = 1, best_cost = 0;
-    for (int64_t S = tile_m; S <= half; S += tile_m) {
+    const int64_t S = half < round_up(V, tile_m) ? half : round_up(V, tile_m);
+    if (S >= tile_m) {
       const int64_t ns = ceil_div(V, S);
+      const int64_t last = V - (ns - 1) * S;
+      int64_t best_sp = 1, best_cost = -1;
       for (int64_t sp = 1; sp <= 16; sp *= 2) {
         if (sp > 1 && S / sp < 512) break;
         // launches: (-, 0), (0, 1), ..., (ns-2, ns-1), (ns-1, -)
-        const int64_t last = V - (ns - 1) * S;
         int64_t c = launch_cost(0, ns == 1 ? last : S, sp);
         if (ns >= 3) c += (ns - 2) * launch_cost(S, S, sp);
         if (ns >= 2) c += launch_cost(S, last, sp);
         c += launch_cost(last, 0, sp);
-        if (best < 0 || c < best_cost || (c == best_cost && S > best)) {
-          best = S; best_sp = sp; best_cost = c;
+        if (best_cost < 0 || c < best_cost) {
+          best_sp = sp;
+          best_cost = c;
         }
       }
-    }
-    if (best > 0) {
-      q.pslab = best < V ? best : round_up(V, 1);
+      q.pslab = S < V ? S : V;
       q.pn_slabs = ceil_div(V, q.pslab);
       q.pdh_splits = best_sp;
     }

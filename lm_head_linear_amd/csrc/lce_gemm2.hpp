@@ -222,11 +222,13 @@ template <class CFG, class Epi> constexpr int gemm2_lds_bytes() {
   return CFG::STAGES * CFG::STAGE_BYTES + EpiPrefetch<Epi>::bytes;
 }
 
-// One workgroup of a product: `bid` of `nb` workgroups of this product, `smem`
-// at least gemm2_lds_bytes<CFG, Epi>() bytes (1 KB aligned).
+// One workgroup of a product: `bid` of `nb` workgroups of this product, of
+// which the first `nreal` logical ones carry work (nb may be padded to a
+// multiple of the XCD count so that a following product keeps its XCD
+// mapping); `smem` at least gemm2_lds_bytes<CFG, Epi>() bytes (1 KB aligned).
 template <class CFG, class TR, bool AK, bool BKM, class Epi>
 __device__ __forceinline__ void gemm2_block(const Gemm2Params &g, const Epi &epi, int64_t bid,
-                                            int64_t nb, char *smem) {
+                                            int64_t nb, int64_t nreal, char *smem) {
   constexpr int BK = CFG::BK, STAGES = CFG::STAGES, KSUB = CFG::KSUB;
   constexpr int NWAVES = TR::NT / 64;
   typedef PipeOperand<CFG, NWAVES, AK> OpA;
@@ -250,6 +252,7 @@ __device__ __forceinline__ void gemm2_block(const Gemm2Params &g, const Epi &epi
   // split's operand rows are fetched into one L2 only.
   const int64_t tiles = (g.M + CFG::BM - 1) / CFG::BM * g.tiles_n;
   const int64_t LS = xcd_remap(bid, nb);
+  if (LS >= nreal) return;   // padding
   const int split = int(LS / tiles);
   const int64_t L = LS % tiles;
   const int64_t m0 = (L / g.tiles_n) * CFG::BM;
@@ -380,7 +383,7 @@ __device__ __forceinline__ void gemm2_block(const Gemm2Params &g, const Epi &epi
 template <class CFG, class TR, bool AK, bool BKM, class Epi>
 __global__ void __launch_bounds__(TR::NT) gemm2_kernel(Gemm2Params g, Epi epi) {
   __shared__ __attribute__((aligned(1024))) char smem[gemm2_lds_bytes<CFG, Epi>()];
-  gemm2_block<CFG, TR, AK, BKM, Epi>(g, epi, blockIdx.x, gridDim.x, smem);
+  gemm2_block<CFG, TR, AK, BKM, Epi>(g, epi, blockIdx.x, gridDim.x, gridDim.x, smem);
 }
 
 // Persistent form for K-major x K-major products with one K-split and a
@@ -538,7 +541,8 @@ struct Gemm2Job {
   static constexpr bool AK = AK_, BKM = BKM_;
   Gemm2Params g;
   Epi e;
-  int64_t nb;   // workgroups (0: the product is absent from this launch)
+  int64_t nb;      // workgroups launched, a multiple of 8 (0: absent from this launch)
+  int64_t nreal;   // workgroups with work (tiles x splits)
 };
 
 // Three independent products in one grid: workgroups [0, j0.nb) run j0, the
@@ -553,16 +557,19 @@ __global__ void __launch_bounds__(TR::NT) gemm2_multi_kernel(J0 j0, J1 j1, J2 j2
   __shared__ __attribute__((aligned(1024))) char smem[B01 > B2 ? B01 : B2];
   int64_t b = blockIdx.x;
   if (b < j0.nb) {
-    gemm2_block<typename J0::CFG, TR, J0::AK, J0::BKM>(j0.g, j0.e, b, j0.nb, smem);
+    gemm2_block<typename J0::CFG, TR, J0::AK, J0::BKM>(j0.g, j0.e, b, j0.nb, j0.nreal,
+                                                                     smem);
     return;
   }
   b -= j0.nb;
   if (b < j1.nb) {
-    gemm2_block<typename J1::CFG, TR, J1::AK, J1::BKM>(j1.g, j1.e, b, j1.nb, smem);
+    gemm2_block<typename J1::CFG, TR, J1::AK, J1::BKM>(j1.g, j1.e, b, j1.nb, j1.nreal,
+                                                                     smem);
     return;
   }
   b -= j1.nb;
-  gemm2_block<typename J2::CFG, TR, J2::AK, J2::BKM>(j2.g, j2.e, b, j2.nb, smem);
+  gemm2_block<typename J2::CFG, TR, J2::AK, J2::BKM>(j2.g, j2.e, b, j2.nb, j2.nreal,
+                                                                     smem);
 }
 
 }  // namespace lce

@@ -105,6 +105,12 @@ SMALL = [
     ("bf16", 517, 256, 2100, 100, None, 1e-3),
     ("bf16", 96, 100, 777, 16, 0.2, 0.0),         # d_model % 8 != 0: element-wise loads
     ("bf16", 1, 64, 33, 1, None, 0.0),            # single token, tiny vocab
+    # bf16 slab pipeline (two slab buffers of the largest 256-row multiple that
+    # fits chunk*vocab): several slabs with a ragged last one, two slabs, one
+    ("bf16", 512, 256, 5000, 256, 0.05, 1e-4),    # 4 x 1024 rows + 904
+    ("bf16", 320, 128, 700, 512, None, 1e-3),     # 512 + 188 rows
+    ("bf16", 256, 64, 300, 512, 0.1, 0.0),        # 256 + 44 rows
+    ("bf16", 130, 96, 500, 1024, None, 1e-4),     # one slab of 500 rows, ragged tokens
 ]
 
 
@@ -122,6 +128,21 @@ def test_small_forward_backward(dt, n, D, V, chunk, mask, z):
     check_grads(c, dH, dW, rdH, rdW)
     if c.m is not None:
         assert not dH[c.m == 0].any()
+
+
+def test_bf16_slab_pipeline_accumulates_d_weight():
+    """accumulate_d_weight through the slab pipeline adds to the given rows."""
+    c = Case(syn.QWEN_BF16, 512, 256, 5000, seed=11, mask_frac=0.05, z=1e-4)
+    f = c.gpu_forward(256)
+    ref = c.oracle_forward(256)
+    dw0 = torch.randn(c.V, c.D, dtype=torch.float32, device=c.H.device)
+    dH, dW = c.gpu_backward(f.lse, 256, d_weight=dw0.clone(), accumulate=True)
+    rdH, rdW = oracle.backward(c.H64, c.W64, c.x.targets, ref["lse"], mask=c.x.mask, z_coef=c.z,
+                               dw_in=dw0.double().cpu().numpy())
+    check_grads(c, dH, dW, rdH, rdW)
+    # the added part alone matches the gradient (not only the large initial rows)
+    d0 = dw0.double().cpu().numpy()
+    assert normwise(dW.double().cpu().numpy() - d0, rdW - d0) <= TOL["bf16"][1]
 
 
 def test_tiny_workload_chunk_invariance_and_accumulate():
