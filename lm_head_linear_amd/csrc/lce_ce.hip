@@ -694,11 +694,10 @@ static void launch_gemm(bool vec, const GemmParams &g, int64_t splits, const Epi
     hipLaunchKernelGGL((gemm_kernel<TR, AK, BKM, false, Epi>), grid, dim3(TR::NT), 0, st, g, epi);
 }
 
-// Pipelined-core stage configurations: K-major x K-major products keep four
-// stages of k 32 (the deeper ring hides more load latency); products with
-// MN-major operands take two stages of k 64 (fewer transposed-read rounds and
-// barriers per k).
-typedef PipeCfg<32, 4> PipeKK;
+// Pipelined-core stage configurations.  With 8 waves per tile two stages of
+// k 64 measured faster than four of k 32 for both operand kinds (K-major rows
+// become whole 128-byte lines; half the barriers per k).
+typedef PipeCfg<64, 2> PipeKK;
 typedef PipeCfg<64, 2> PipeMN;
 
 // The pipelined core runs 8 waves per tile (TraitsBF16W8); its epilogues are

@@ -25,7 +25,7 @@
 //     constants into LDS while the first stages are in flight.
 // Requirements (checked by the host): 16-byte aligned bases, leading
 // dimensions multiple of 8, K-major operands zero-padded (or exact) to a
-// multiple of 32 along K, 256 * ld * 2 bytes below 2^31.
+// multiple of the k-step along K, 256 * ld * 2 bytes below 2^31.
 #pragma once
 
 #include <type_traits>
@@ -179,7 +179,7 @@ struct Gemm2Params {
   int64_t ldb;
   int64_t M, N, K;          // K: valid depth (K-major operands are zero-padded past it)
   int64_t M_read, N_read;   // readable row lengths of MN-major operands
-  int64_t k_per_split;      // multiple of 32
+  int64_t k_per_split;      // multiple of the configuration's k-step
   int64_t tiles_n;
   const int32_t *bad;
 };

@@ -110,7 +110,7 @@ SMALL = [
     ("bf16", 512, 256, 5000, 256, 0.05, 1e-4),    # 4 x 1024 rows + 904
     ("bf16", 320, 128, 700, 512, None, 1e-3),     # 512 + 188 rows
     ("bf16", 256, 64, 300, 512, 0.1, 0.0),        # 256 + 44 rows
-    ("bf16", 130, 96, 500, 1024, None, 1e-4),     # one slab of 500 rows, ragged tokens
+    ("bf16", 130, 128, 500, 1024, None, 1e-4),    # one slab of 500 rows, ragged tokens
 ]
 
 
