@@ -60,6 +60,8 @@ def _load():
         lib.orc_distill.argtypes = [vp, vp, vp, i64, i64, i32, dbl, dbl, dbl, i32, vp, vp]
         lib.orc_distill_rows.argtypes = [vp, vp, vp, i64, i32, dbl, dbl, dbl, i64, vp, i64,
                                          i32, vp, vp, vp]
+        lib.orc_ce_logits.argtypes = [vp, vp, vp, i64, i64, dbl, dbl, i32, vp, vp]
+        lib.orc_ce_logits_rows.argtypes = [vp, vp, vp, i64, i64, dbl, dbl, i64, i32, vp, vp, vp]
         _lib = lib
     return _lib
 
@@ -255,5 +257,41 @@ def distill_rows(S_rows, U_rows, n_counted, row_mask=None, objective=0, temperat
                                   int(n_counted), rows.ctypes.data, k,
                                   nthreads or default_threads(), g.ctypes.data,
                                   rl.ctypes.data, rz.ctypes.data)
+    assert st == OK, st
+    return g, rl, rz
+
+
+def ce_logits(Z, targets, mask=None, z_coef=0.0, grad_out=1.0, want_grad=True, nthreads=None):
+    """Label cross-entropy + z-loss from materialized logits [n][V], forward
+    and backward (the lossk reference function with the mask and z term)."""
+    Z = _f64(Z)
+    y = _i64(targets)
+    m = _mask(mask)
+    n, V = Z.shape
+    grad = np.zeros((n, V), dtype=np.float64) if want_grad else None
+    out = np.zeros(5, dtype=np.float64)
+    st = _load().orc_ce_logits(Z.ctypes.data, y.ctypes.data, _p(m), n, V, float(z_coef),
+                               float(grad_out), nthreads or default_threads(), _p(grad),
+                               out.ctypes.data)
+    return {"status": int(st), "loss": float(out[0]), "z_loss": float(out[1]),
+            "n_counted": int(out[2]), "loss_sum": float(out[3]), "z_sum": float(out[4]),
+            "grad": grad}
+
+
+def ce_logits_rows(Z_rows, targets_rows, n_counted, row_mask=None, z_coef=0.0, grad_out=1.0,
+                   nthreads=None):
+    """ce_logits on selected rows of a larger batch (n_counted = its divisor C).
+    Returns (grad_rows [k][V], row_loss [k], row_lse [k])."""
+    Z = _f64(Z_rows)
+    y = _i64(targets_rows)
+    m = _mask(row_mask)
+    k, V = Z.shape
+    g = np.zeros((k, V), dtype=np.float64)
+    rl = np.zeros(k, dtype=np.float64)
+    rz = np.zeros(k, dtype=np.float64)
+    st = _load().orc_ce_logits_rows(Z.ctypes.data, y.ctypes.data, _p(m), k, V, float(z_coef),
+                                    float(grad_out), int(n_counted),
+                                    nthreads or default_threads(), g.ctypes.data,
+                                    rl.ctypes.data, rz.ctypes.data)
     assert st == OK, st
     return g, rl, rz

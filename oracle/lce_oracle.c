@@ -13,7 +13,7 @@
  *        different questions", "Chunk invariance is checked to the last bit",
  *        "The backward's gradient check is a cancellation identity".
  *   [P3] "Fuse distillation + z-loss in the triton monolithic path"
- *        (Fast-LLM pull request 566), section "What it does".
+ *        (Fast-LLM pull request 566), sections "What it does" and "Changes".
  *
  * Conventions:
  *   - IEEE fp64, round to nearest even, built with -O2 -ffp-contract=off and
@@ -532,6 +532,110 @@ int orc_distill(const double *S, const double *U, const uint8_t *mask, int64_t n
   out5[4] = z_sum;
   free(rows);
   free(rl);
+  return ORC_OK;
+}
+
+/* ------------------------------------------------------------------------ */
+/* Label cross-entropy with z-loss from materialized logits: the lossk       */
+/* reference (ce_from_logits_flat, [P1] lossk table) with the loss mask and  */
+/* the z term of [P3] ("What it does", "Changes"), forward and backward.     */
+/*   lse_t = log sum_v exp(z[t][v]),  L_t = lse_t - z[t][y_t]                */
+/*   dL_t/dz_v = p_v - [v == y_t],  d(lse_t^2)/dz_v = 2 lse_t p_v,           */
+/*   p_v = exp(z[t][v] - lse_t)                                              */
+/*   grad[t][v] = (grad_out/C) (dL_t/dz_v + z_coef d(lse_t^2)/dz_v)          */
+/* loss = sum L_t / C, z_loss = sum lse_t^2 / C over counted rows; masked    */
+/* rows get zeros.                                                          */
+/* ------------------------------------------------------------------------ */
+
+typedef struct {
+  const double *Z;
+  const int64_t *targets;
+  const uint8_t *mask;
+  int64_t V;
+  double z_coef, scale;     /* scale = grad_out / C */
+  const int64_t *rows;
+  double *grad;             /* [n_rows][V] or NULL */
+  double *row_loss, *row_lse;
+} lbl_ctx;
+
+static void lbl_item(void *p, int64_t i) {
+  lbl_ctx *c = (lbl_ctx *)p;
+  int64_t t = c->rows[i];
+  int64_t V = c->V;
+  double *g = c->grad ? c->grad + i * V : NULL;
+  if (c->mask && !c->mask[t]) {
+    if (g) for (int64_t v = 0; v < V; ++v) g[v] = 0.0;
+    c->row_loss[i] = 0.0;
+    c->row_lse[i] = 0.0;
+    return;
+  }
+  const double *z = c->Z + t * V;
+  int64_t y = c->targets[t];
+  double lse = row_lse(z, V);
+  if (g) {
+    for (int64_t v = 0; v < V; ++v) {
+      double pv = exp(z[v] - lse);
+      double dce = pv - (v == y ? 1.0 : 0.0);
+      double dz = 2.0 * lse * pv;
+      g[v] = c->scale * (dce + c->z_coef * dz);
+    }
+  }
+  c->row_loss[i] = lse - z[y];
+  c->row_lse[i] = lse;
+}
+
+/* Full call: grad is [n_tok][vocab] (may be NULL to skip gradients);
+ * out5 = {loss, z_loss, n_counted, loss_sum, z_sum}. */
+int orc_ce_logits(const double *Z, const int64_t *targets, const uint8_t *mask, int64_t n_tok,
+                  int64_t vocab, double z_coef, double grad_out, int nthreads, double *grad,
+                  double *out5) {
+  if (n_tok < 1 || vocab < 1) return ORC_EMPTY_DIMENSION;
+  if (n_tok > ORC_MAX_N_TOK || vocab > ORC_MAX_VOCAB) return ORC_DIMENSION_TOO_LARGE;
+  if (!is_fin(z_coef) || !is_fin(grad_out)) return ORC_NON_FINITE_SCALAR;
+  if (!orc_targets_in_range(targets, n_tok, vocab)) return ORC_TARGET_OUT_OF_RANGE;
+  int64_t counted = 0;
+  for (int64_t t = 0; t < n_tok; ++t) counted += (!mask || mask[t]) ? 1 : 0;
+  int64_t *rows = (int64_t *)malloc(sizeof(int64_t) * (size_t)n_tok);
+  double *rl = (double *)malloc(sizeof(double) * (size_t)n_tok * 2);
+  for (int64_t t = 0; t < n_tok; ++t) rows[t] = t;
+  lbl_ctx c;
+  c.Z = Z; c.targets = targets; c.mask = mask; c.V = vocab; c.z_coef = z_coef;
+  c.scale = counted ? grad_out / (double)counted : 0.0;
+  c.rows = rows; c.grad = grad; c.row_loss = rl; c.row_lse = rl + n_tok;
+  orc_parallel_for(nthreads, n_tok, lbl_item, &c);
+  double loss_sum = 0.0, z_sum = 0.0;
+  for (int64_t t = 0; t < n_tok; ++t) {
+    if (mask && !mask[t]) continue;
+    loss_sum = loss_sum + c.row_loss[t];
+    z_sum = z_sum + c.row_lse[t] * c.row_lse[t];
+  }
+  out5[0] = counted ? loss_sum / (double)counted : 0.0;
+  out5[1] = counted ? z_sum / (double)counted : 0.0;
+  out5[2] = (double)counted;
+  out5[3] = loss_sum;
+  out5[4] = z_sum;
+  free(rows);
+  free(rl);
+  return ORC_OK;
+}
+
+/* Selected rows of a larger batch: Z_rows, targets_rows and mask_rows hold
+ * only the listed rows; n_counted is the divisor C of the whole batch. */
+int orc_ce_logits_rows(const double *Z_rows, const int64_t *targets_rows,
+                       const uint8_t *mask_rows, int64_t n_rows, int64_t vocab, double z_coef,
+                       double grad_out, int64_t n_counted, int nthreads, double *grad_rows,
+                       double *row_loss, double *row_lse) {
+  if (n_rows < 1 || vocab < 1) return ORC_EMPTY_DIMENSION;
+  if (!is_fin(z_coef) || !is_fin(grad_out)) return ORC_NON_FINITE_SCALAR;
+  if (!orc_targets_in_range(targets_rows, n_rows, vocab)) return ORC_TARGET_OUT_OF_RANGE;
+  int64_t *rows = (int64_t *)malloc(sizeof(int64_t) * (size_t)n_rows);
+  for (int64_t t = 0; t < n_rows; ++t) rows[t] = t;
+  lbl_ctx c;
+  c.Z = Z_rows; c.targets = targets_rows; c.mask = mask_rows; c.V = vocab; c.z_coef = z_coef;
+  c.scale = n_counted ? grad_out / (double)n_counted : 0.0;
+  c.rows = rows; c.grad = grad_rows; c.row_loss = row_loss; c.row_lse = row_lse;
+  orc_parallel_for(nthreads, n_rows, lbl_item, &c);
+  free(rows);
   return ORC_OK;
 }
 

@@ -492,6 +492,120 @@ def test_distill_refusals_and_rows():
     assert np.array_equal(g, full["grad"][rows])
 
 
+# ------------------------------------ label cross-entropy + z from logits --
+
+def test_ce_logits_uniform_golden_and_closed_form():
+    """The lossk worked example (9 equal logits -> log 9, bit-exact) and the
+    closed form of every term for equal logits c: lse = c + log V, z = lse^2,
+    grad = (g/C)((1 + 2 z_coef lse)/V - onehot)."""
+    g = dict(r.split(None, 1) for r in _read_golden("p1_uniform_logits.txt"))
+    n, V = int(g["n_tok"]), int(g["vocab"])
+    y = [int(x) for x in g["targets"].split()]
+    r = oracle.ce_logits(np.full((n, V), float(g["logit"])), y)
+    assert r["status"] == 580 and r["loss"] == float(g["mean_loss"])
+    c, V, zc, go = 1.5, 7, 0.25, 1.75
+    y = np.array([0, 3, 6, 2])
+    m = np.array([1, 1, 0, 1], dtype=np.uint8)
+    r = oracle.ce_logits(np.full((4, V), c), y, mask=m, z_coef=zc, grad_out=go)
+    lse = c + math.log(V)
+    assert r["n_counted"] == 3
+    assert abs(r["loss"] - math.log(V)) <= 1e-15
+    assert abs(r["z_loss"] - lse * lse) <= 1e-14
+    want = np.full((4, V), (go / 3) * (1 + 2 * zc * lse) / V)
+    want[np.arange(4), y] -= go / 3
+    want[2] = 0.0
+    assert np.max(np.abs(r["grad"] - want)) <= 1e-15
+
+
+def test_ce_logits_loss_matches_ce_from_logits():
+    rng = np.random.default_rng(21)
+    Z = rng.standard_normal((13, 301)) * 4.0
+    y = rng.integers(0, 301, 13)
+    r = oracle.ce_logits(Z, y, want_grad=False)
+    st, mean, per = oracle.ce_from_logits(Z, y)
+    assert r["status"] == st == 580 and r["loss"] == mean
+
+
+@pytest.mark.parametrize("z_coef,mask_frac", [(0.0, 0.0), (0.3, 0.34)])
+def test_ce_logits_finite_differences(z_coef, mask_frac):
+    rng = np.random.default_rng(22)
+    n, V, go = 3, 8, 1.3
+    Z = rng.standard_normal((n, V)) * 2.0
+    y = rng.integers(0, V, n)
+    m = (rng.random(n) >= mask_frac).astype(np.uint8)
+    m[0] = 1
+    r = oracle.ce_logits(Z, y, mask=m, z_coef=z_coef, grad_out=go)
+    h = 1e-5
+
+    def f():
+        q = oracle.ce_logits(Z, y, mask=m, z_coef=z_coef, grad_out=go, want_grad=False)
+        return go * (q["loss"] + z_coef * q["z_loss"])
+
+    fd = np.zeros_like(Z)
+    for idx in np.ndindex(*Z.shape):
+        old = Z[idx]
+        Z[idx] = old + h
+        fp = f()
+        Z[idx] = old - h
+        fm = f()
+        Z[idx] = old
+        fd[idx] = (fp - fm) / (2 * h)
+    assert np.max(np.abs(fd - r["grad"])) <= 1e-8
+
+
+def test_ce_logits_matches_torch_autograd():
+    rng = np.random.default_rng(23)
+    n, V, zc, go = 9, 57, 1e-2, 0.7
+    Z = rng.standard_normal((n, V)) * 3.0
+    y = rng.integers(0, V, n)
+    m = (rng.random(n) > 0.2).astype(np.uint8)
+    r = oracle.ce_logits(Z, y, mask=m, z_coef=zc, grad_out=go)
+    Zt = torch.from_numpy(Z.copy()).requires_grad_(True)
+    keep = torch.from_numpy(m.astype(bool))
+    lse = torch.logsumexp(Zt, 1)
+    ce = lse - Zt[torch.arange(n), torch.from_numpy(y)]
+    C = int(keep.sum())
+    loss = ce[keep].sum() / C
+    zl = (lse[keep] ** 2).sum() / C
+    (go * (loss + zc * zl)).backward()
+    assert abs(r["loss"] - float(loss)) <= 1e-14 * abs(float(loss))
+    assert abs(r["z_loss"] - float(zl)) <= 1e-14 * abs(float(zl))
+    g = Zt.grad.numpy()
+    assert np.max(np.abs(r["grad"] - g)) <= 1e-14 * np.max(np.abs(g))
+
+
+def test_ce_logits_equals_distill_with_one_hot_teacher():
+    """A teacher with all its mass on the label (exp(-800) underflows to 0)
+    makes the distillation cross-entropy the label loss, term for term."""
+    rng = np.random.default_rng(24)
+    n, V = 7, 33
+    Z = rng.standard_normal((n, V)) * 2.0
+    y = rng.integers(0, V, n)
+    m = (rng.random(n) > 0.3).astype(np.uint8)
+    U = np.zeros((n, V))
+    U[np.arange(n), y] = 800.0
+    d = oracle.distill(Z, U, mask=m, objective=0, temperature=1.0, z_coef=0.2, grad_out=1.1)
+    r = oracle.ce_logits(Z, y, mask=m, z_coef=0.2, grad_out=1.1)
+    assert abs(r["loss"] - d["loss"]) <= 1e-14 and r["z_loss"] == d["z_loss"]
+    assert np.max(np.abs(r["grad"] - d["grad"])) <= 1e-16
+
+
+def test_ce_logits_refusals_and_rows():
+    rng = np.random.default_rng(25)
+    Z = rng.standard_normal((8, 16))
+    y = rng.integers(0, 16, 8)
+    m = (rng.random(8) > 0.3).astype(np.uint8)
+    assert oracle.ce_logits(Z, np.where(np.arange(8) == 3, 16, y))["status"] == 586
+    assert oracle.ce_logits(Z, np.where(np.arange(8) == 5, -1, y))["status"] == 586
+    assert oracle.ce_logits(Z, y, z_coef=float("nan"))["status"] == 585
+    assert oracle.ce_logits(Z, y, grad_out=float("inf"))["status"] == 585
+    full = oracle.ce_logits(Z, y, mask=m, z_coef=0.1, grad_out=2.0)
+    rows = np.array([0, 2, 7])
+    g, rl, rz = oracle.ce_logits_rows(Z[rows], y[rows], full["n_counted"], row_mask=m[rows],
+                                      z_coef=0.1, grad_out=2.0)
+    assert np.array_equal(g, full["grad"][rows])
+
+
 def test_large_golden_file_matches_the_oracle():
     """The stored lse of the 8192 x 4096 x 128256 workload (written by
     tests/golden/make_large_bf16_lse.py) is the oracle's: three tokens
