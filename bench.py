@@ -117,6 +117,51 @@ def distill_measure(lce, torch, np, dev, steps: int):
     return res
 
 
+def label_measure(lce, torch, np, dev, steps: int):
+    """lce_ce_logits_fwd_bwd on 4096 x 151936 bf16 logits (10% masked, z
+    1e-4), with the gradient and loss only: kernel time from HIP events and
+    HBM throughput on the algorithmic bytes (logits read once for counted
+    rows, the gradient written for every row, targets and mask read)."""
+    from tests import synthetic as syn
+    w = syn.LABEL_BF16
+    log(f"bench: label cross-entropy {w.name}: generating inputs")
+    x = syn.label_inputs(w)
+    Z = x.logits.to(dev)
+    y = torch.from_numpy(x.targets).to(dev)
+    mk = torch.from_numpy(x.mask).to(dev)
+    n, V = Z.shape
+    C = int(x.mask.sum())
+    g = torch.empty_like(Z)
+    ws = torch.empty(lce.lce_distill_workspace_bytes(n, V), dtype=torch.uint8, device=dev)
+    res = {"workload": w.name, "n_tok": n, "vocab": V, "counted": C, "peak_GBs": PEAK_HBM_GBS,
+           "modes": {}}
+    for mode, grad, nbytes in (("fwd_bwd", g, 2 * V * (C + n) + 9 * n),
+                               ("loss_only", None, 2 * V * C + 9 * n)):
+        def call(timer=None):
+            st, out = lce.lce_ce_logits_fwd_bwd(Z, y, mk, n, V, w.z_coef, 1.0, grad, ws,
+                                                timer=timer)
+            if st != lce.OK:
+                raise lce.LceError(st, "lce_ce_logits_fwd_bwd")
+            return out
+        for _ in range(2):
+            call()
+        t0 = time.perf_counter()
+        for _ in range(steps):
+            out = call()
+        wall = (time.perf_counter() - t0) / steps * 1e3
+        timer = lce.KernelTimer(["label_ce"], capacity=steps * 4)
+        for _ in range(steps):
+            call(timer)
+        torch.cuda.synchronize()
+        k_ms = float(np.sum(timer.durations_ms("label_ce"))) / steps
+        res["modes"][mode] = {"algorithmic_bytes": nbytes, "call_ms": round(wall, 4),
+                              "kernel_ms": round(k_ms, 4),
+                              "GBs": round(nbytes / (k_ms / 1e3) / 1e9, 1),
+                              "frac": round(nbytes / (k_ms / 1e3) / 1e9 / PEAK_HBM_GBS, 4),
+                              "loss": out.loss_mean}
+    return res
+
+
 def cpu_baseline(w, x, tokens: int):
     """The oracle, as it stands, on the first `tokens` tokens of the workload:
     forward (all tokens of the prefix) + backward (d_hidden of the prefix and
@@ -154,11 +199,11 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-kernel-events", action="store_true")
     ap.add_argument("--no-distill", action="store_true",
-                    help="skip the distillation measurement (4096 x 151936 bf16)")
+                    help="skip the logits-in measurements (distillation, label CE; 4096 x 151936 bf16)")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path "
+        print("bench.py measures one GPU only: there is no multi-GPU path "
               "(run with --gpus 1)", file=sys.stderr)
         sys.exit(2)
 
@@ -299,9 +344,10 @@ def main():
                 "frac": round(achieved / peak, 4), "traffic": traffic_from_profiles(w.name, dom),
                 "kernel": dom, "flops_per_launch": per_launch_flops, "avg_launch_ms": kd["avg_ms"]}
 
-    distill = None
+    distill = label = None
     if not args.no_distill and w.dtype == "bf16":
         distill = distill_measure(lce, torch, np, dev, args.steps)
+        label = label_measure(lce, torch, np, dev, args.steps)
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -335,6 +381,7 @@ def main():
         "kernels": kernels,
         "roofline": roof,
         "distill": distill,
+        "label_ce": label,
         "cpu_baseline": cpu,
     }
     print(json.dumps(res), flush=True)

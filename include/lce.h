@@ -210,6 +210,29 @@ int32_t lce_distill_fwd_bwd(const lce_tensor *student, const lce_tensor *teacher
                             double grad_out, lce_tensor *grad_logits, lce_tensor *workspace,
                             lce_loss *out, void *stream);
 
+/* Label cross-entropy with z-loss from materialized logits, fused forward +
+ * backward: the lossk page's ce_from_logits reference function ("Loss
+ * functions and resident-context kernels", lossk table) on the device, with
+ * the loss mask and z term of Fast-LLM 566 ("What it does", "Changes").
+ *   logits       [n_tok*vocab] LCE_BF16, LCE_F32 or LCE_F64, row-major
+ *                [n_tok][vocab]
+ *   targets      [n_tok] LCE_I64, each 0 <= y < vocab (else 586, with
+ *                grad_logits untouched)
+ *   loss_mask    [n_tok] LCE_U8 or data == NULL (all rows counted)
+ *   grad_logits  [n_tok*vocab] in the logits' dtype, overwritten with
+ *                (grad_out/C)((1 + 2 z_coef lse) softmax - onehot(y)), masked
+ *                rows 0; NULL or data == NULL computes the loss only (the
+ *                logits are then read once)
+ *   workspace    LCE_U8, numel >= lce_distill_workspace_bytes(n_tok, vocab)
+ *   out          host; loss_sum/loss_mean = sum/mean over counted rows of
+ *                lse - z[y], z_sum/z_mean = unscaled lse^2, n_counted = C
+ * Statuses as lce_distill_fwd_bwd (no objective or temperature); returns
+ * after the scalars reach the host. */
+int32_t lce_ce_logits_fwd_bwd(const lce_tensor *logits, const lce_tensor *targets,
+                              const lce_tensor *loss_mask, int64_t n_tok, int64_t vocab,
+                              double z_coef, double grad_out, lce_tensor *grad_logits,
+                              lce_tensor *workspace, lce_loss *out, void *stream);
+
 /* ---- optional kernel timing (for benchmarks and profilers) ------------- */
 
 /* Kernel kinds a timed call can bracket with events. */
@@ -225,7 +248,8 @@ int32_t lce_distill_fwd_bwd(const lce_tensor *student, const lce_tensor *teacher
 #define LCE_K_BWD_GEMM 9     /* one launch of the slab-pipelined bf16 backward: */
                              /* d_hidden and d_weight of slab k with the logit  */
                              /* gradient of slab k+1                            */
-#define LCE_NUM_KERNELS 10
+#define LCE_K_LABEL_CE 10    /* label cross-entropy row kernel (logits in)      */
+#define LCE_NUM_KERNELS 11
 
 /* One slot per kernel kind.  start/stop hold `capacity` caller-created
  * hipEvent_t handles (as void*); a timed call records start[i]/stop[i] on
@@ -262,6 +286,11 @@ int32_t lce_distill_fwd_bwd_timed(const lce_tensor *student, const lce_tensor *t
                                   double grad_out, lce_tensor *grad_logits,
                                   lce_tensor *workspace, lce_loss *out, void *stream,
                                   lce_timers *timers);
+int32_t lce_ce_logits_fwd_bwd_timed(const lce_tensor *logits, const lce_tensor *targets,
+                                    const lce_tensor *loss_mask, int64_t n_tok, int64_t vocab,
+                                    double z_coef, double grad_out, lce_tensor *grad_logits,
+                                    lce_tensor *workspace, lce_loss *out, void *stream,
+                                    lce_timers *timers);
 
 #ifdef __cplusplus
 }

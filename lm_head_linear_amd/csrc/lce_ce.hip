@@ -769,6 +769,11 @@ static void launch_guard(const int64_t *y, const uint8_t *mask, int64_t n, int64
   hipLaunchKernelGGL(guard_kernel, dim3(unsigned(blocks)), dim3(256), 0, st, y, mask, n, V, ctl);
 }
 
+void launch_target_guard(const int64_t *targets, const uint8_t *mask, int64_t n, int64_t V,
+                         Control *ctl, void *stream, lce_timers *tm) {
+  launch_guard(targets, mask, n, V, ctl, static_cast<hipStream_t>(stream), tm, 0);
+}
+
 template <class TR>
 static void forward_impl(const CEPlan &p, const void *H, const void *W, const int64_t *y,
                          const uint8_t *mask, typename TR::Acc *lse_out, uint8_t *ws, bool vec,

@@ -21,6 +21,14 @@
 // Cache; gradient stores are non-temporal so they do not evict those rows.
 // Masked rows only write zeros.  Per-row L and lse_x go to the workspace; a
 // fixed-order fp64 reduction forms the means.
+//
+// Label cross-entropy from materialized logits (the lossk page's
+// ce_from_logits reference function on the device, with the loss mask and the
+// z term of Fast-LLM 566) runs the same row walk with a one-hot target:
+// pass 1 keeps (max, sum exp) of z and reads z[y_t] once, L = lse - z[y_t];
+// pass 2, when a gradient is asked for, writes
+// (grad_out/C)((1 + 2 z_coef lse) p - onehot(y_t)).  Without a gradient the
+// row is read once.
 #include <hip/hip_runtime.h>
 
 #include <climits>
@@ -264,6 +272,87 @@ __device__ __forceinline__ void distill_row(const T *S, const T *U, const uint8_
     IO<T>::store1(g_row + v, grad_of(IO<T>::load1(s_row + v) * iT, IO<T>::load1(u_row + v) * iT));
 }
 
+template <class T, bool VEC, bool GRAD>
+__device__ __forceinline__ void label_row(const T *Z, const int64_t *y, const uint8_t *mask,
+                                          int64_t t, int64_t V, double z_coef, double grad_out,
+                                          const Control *ctl, T *grad, double *row_out) {
+  typedef typename IO<T>::C C;
+  const T *z_row = Z + t * V;
+  const int tid = threadIdx.x;
+  const int64_t nvec = VEC ? V / 8 : 0;
+  const int64_t tail0 = nvec * 8;
+
+  if (mask && !mask[t]) {
+    if constexpr (GRAD) {
+      T *g_row = grad + t * V;
+      const C z[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+      for (int64_t i = tid; i < nvec; i += kBlock) IO<T>::store8(g_row + i * 8, z);
+      for (int64_t v = tail0 + tid; v < V; v += kBlock) IO<T>::store1(g_row + v, C(0));
+    }
+    if (tid == 0) { row_out[2 * t] = 0.0; row_out[2 * t + 1] = 0.0; }
+    return;
+  }
+  __syncthreads();   // the previous row's statistics are no longer read
+
+  Online<C> f;
+  f.init();
+  auto consume = [&](const C *xs, int cnt) {
+    C lm = -INFINITY;
+    for (int i = 0; i < cnt; ++i) lm = xs[i] > lm ? xs[i] : lm;
+    const C nm = f.m > lm ? f.m : lm;
+    f.s *= dexp<C>(f.m - nm);
+    f.m = nm;
+    for (int i = 0; i < cnt; ++i) f.s += dexp<C>(xs[i] - nm);
+  };
+  for (int64_t i = tid; i < nvec; i += kBlock) {
+    C xs[8];
+    IO<T>::load8(z_row + i * 8, xs);
+    consume(xs, 8);
+  }
+  for (int64_t v = tail0 + tid; v < V; v += kBlock) {
+    const C xs[1] = {IO<T>::load1(z_row + v)};
+    consume(xs, 1);
+  }
+  __shared__ Online<C> sh_f[kBlock / 64];
+  __shared__ C sh_lse;
+  block_merge(f, sh_f);
+  const int64_t yt = y[t];
+  if (tid == 0) {
+    const C lse = f.m + dlog<C>(f.s);
+    sh_lse = lse;
+    row_out[2 * t] = double(lse - IO<T>::load1(z_row + yt));
+    row_out[2 * t + 1] = double(lse);
+  }
+  if constexpr (GRAD) {
+    __syncthreads();
+    T *g_row = grad + t * V;
+    const C lse = sh_lse;
+    const int64_t cnt = ctl->count;
+    const C g = cnt ? C(grad_out / double(cnt)) : C(0);
+    const C a = g * (C(1) + C(2.0 * z_coef) * lse);
+    for (int64_t i = tid; i < nvec; i += kBlock) {
+      C xs[8], gs[8];
+      IO<T>::load8(z_row + i * 8, xs);
+#pragma unroll
+      for (int j = 0; j < 8; ++j) gs[j] = a * dexp<C>(xs[j] - lse) - (i * 8 + j == yt ? g : C(0));
+      IO<T>::store8(g_row + i * 8, gs);
+    }
+    for (int64_t v = tail0 + tid; v < V; v += kBlock)
+      IO<T>::store1(g_row + v, a * dexp<C>(IO<T>::load1(z_row + v) - lse) - (v == yt ? g : C(0)));
+  }
+}
+
+// Rows t = blockIdx.x, + gridDim.x, ...; nothing runs when the guard found
+// an out-of-range target (the outputs stay untouched).
+template <class T, bool VEC, bool GRAD>
+__global__ void __launch_bounds__(kBlock)
+label_row_kernel(const T *Z, const int64_t *y, const uint8_t *mask, int64_t n, int64_t V,
+                 double z_coef, double grad_out, const Control *ctl, T *grad, double *row_out) {
+  if (ctl->bad) return;
+  for (int64_t t = blockIdx.x; t < n; t += gridDim.x)
+    label_row<T, VEC, GRAD>(Z, y, mask, t, V, z_coef, grad_out, ctl, grad, row_out);
+}
+
 __global__ void distill_init_kernel(Control *ctl) {
   if (threadIdx.x == 0) {
     ctl->bad = 0;
@@ -352,6 +441,32 @@ void distill_impl(int objective, bool vec, const T *S, const T *U, const uint8_t
                      n, ctl);
 }
 
+template <class T>
+void label_impl(bool vec, bool want_grad, const T *Z, const int64_t *y, const uint8_t *mask,
+                int64_t n, int64_t V, double z, double go, Control *ctl, T *grad, double *rows,
+                hipStream_t st, lce_timers *tm) {
+  launch_target_guard(y, mask, n, V, ctl, st, tm);
+  const unsigned grid = unsigned(n < kRowGrid ? n : kRowGrid);
+  {
+    TimedLaunch tl(tm, LCE_K_LABEL_CE, st);
+    if (vec && want_grad)
+      hipLaunchKernelGGL((label_row_kernel<T, true, true>), dim3(grid), dim3(kBlock), 0, st, Z, y,
+                         mask, n, V, z, go, ctl, grad, rows);
+    else if (vec)
+      hipLaunchKernelGGL((label_row_kernel<T, true, false>), dim3(grid), dim3(kBlock), 0, st, Z,
+                         y, mask, n, V, z, go, ctl, grad, rows);
+    else if (want_grad)
+      hipLaunchKernelGGL((label_row_kernel<T, false, true>), dim3(grid), dim3(kBlock), 0, st, Z,
+                         y, mask, n, V, z, go, ctl, grad, rows);
+    else
+      hipLaunchKernelGGL((label_row_kernel<T, false, false>), dim3(grid), dim3(kBlock), 0, st, Z,
+                         y, mask, n, V, z, go, ctl, grad, rows);
+  }
+  TimedLaunch tl(tm, LCE_K_REDUCE, st);
+  hipLaunchKernelGGL(distill_final_kernel, dim3(1), dim3(1024), 0, st, (const double *)rows, mask,
+                     n, ctl);
+}
+
 bool has(const lce_tensor *t) { return t && t->data; }
 bool aligned(const void *p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
@@ -427,6 +542,81 @@ extern "C" int32_t lce_distill_fwd_bwd_timed(const lce_tensor *student, const lc
   if (hipMemcpyAsync(&hc, ctl, sizeof(Control), hipMemcpyDeviceToHost, s) != hipSuccess)
     return LCE_DEVICE_ERROR;
   if (hipStreamSynchronize(s) != hipSuccess) return LCE_DEVICE_ERROR;
+  out->loss_sum = hc.loss_sum;
+  out->z_sum = hc.z_sum;
+  out->n_counted = hc.count;
+  out->loss_mean = hc.count ? hc.loss_sum / double(hc.count) : 0.0;
+  out->z_mean = hc.count ? hc.z_sum / double(hc.count) : 0.0;
+  return LCE_OK;
+}
+
+extern "C" int32_t lce_ce_logits_fwd_bwd(const lce_tensor *logits, const lce_tensor *targets,
+                                         const lce_tensor *loss_mask, int64_t n_tok,
+                                         int64_t vocab, double z_coef, double grad_out,
+                                         lce_tensor *grad_logits, lce_tensor *workspace,
+                                         lce_loss *out, void *stream) {
+  return lce_ce_logits_fwd_bwd_timed(logits, targets, loss_mask, n_tok, vocab, z_coef, grad_out,
+                                     grad_logits, workspace, out, stream, nullptr);
+}
+
+extern "C" int32_t lce_ce_logits_fwd_bwd_timed(const lce_tensor *logits,
+                                               const lce_tensor *targets,
+                                               const lce_tensor *loss_mask, int64_t n_tok,
+                                               int64_t vocab, double z_coef, double grad_out,
+                                               lce_tensor *grad_logits, lce_tensor *workspace,
+                                               lce_loss *out, void *stream, lce_timers *timers) {
+  DistillPlan p;
+  int32_t st = plan_distill(n_tok, vocab, &p);
+  if (st != LCE_OK) return st;
+  if (!finite_scalar(z_coef) || !finite_scalar(grad_out)) return LCE_NON_FINITE_SCALAR;
+  if (!logits || !targets || !workspace) return LCE_LENGTH_MISMATCH;
+  const int32_t dt = logits->dtype;
+  const bool want_grad = has(grad_logits);
+  if (dt != LCE_BF16 && dt != LCE_F32 && dt != LCE_F64) return LCE_DTYPE_MISMATCH;
+  if (targets->dtype != LCE_I64) return LCE_DTYPE_MISMATCH;
+  if (want_grad && grad_logits->dtype != dt) return LCE_DTYPE_MISMATCH;
+  if (has(loss_mask) && loss_mask->dtype != LCE_U8) return LCE_DTYPE_MISMATCH;
+  if (workspace->dtype != LCE_U8) return LCE_DTYPE_MISMATCH;
+  const int64_t cells = n_tok * vocab;
+  if (!has(logits) || logits->numel < cells || !has(targets) || targets->numel < n_tok)
+    return LCE_LENGTH_MISMATCH;
+  if (want_grad && grad_logits->numel < cells) return LCE_LENGTH_MISMATCH;
+  if (has(loss_mask) && loss_mask->numel < n_tok) return LCE_LENGTH_MISMATCH;
+  if (!has(workspace) || workspace->numel < int64_t(p.total) + 256) return LCE_LENGTH_MISMATCH;
+  if (!out) return LCE_LENGTH_MISMATCH;
+
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  uintptr_t base = (reinterpret_cast<uintptr_t>(workspace->data) + 255) & ~uintptr_t(255);
+  uint8_t *ws = reinterpret_cast<uint8_t *>(base);
+  Control *ctl = reinterpret_cast<Control *>(ws);
+  double *rows = reinterpret_cast<double *>(ws + p.off_rows);
+  const uint8_t *mask = has(loss_mask) ? static_cast<const uint8_t *>(loss_mask->data) : nullptr;
+  const int64_t *y = static_cast<const int64_t *>(targets->data);
+  const size_t esz = dtype_size(dt);
+  const bool vec = (vocab % 8 == 0) && aligned(logits->data, 16) &&
+                   (!want_grad || aligned(grad_logits->data, 16)) && (esz * 8) % 16 == 0;
+  (void)hipGetLastError();
+  if (dt == LCE_BF16)
+    label_impl<uint16_t>(vec, want_grad, static_cast<const uint16_t *>(logits->data), y, mask,
+                         n_tok, vocab, z_coef, grad_out, ctl,
+                         want_grad ? static_cast<uint16_t *>(grad_logits->data) : nullptr, rows,
+                         s, timers);
+  else if (dt == LCE_F32)
+    label_impl<float>(vec, want_grad, static_cast<const float *>(logits->data), y, mask, n_tok,
+                      vocab, z_coef, grad_out, ctl,
+                      want_grad ? static_cast<float *>(grad_logits->data) : nullptr, rows, s,
+                      timers);
+  else
+    label_impl<double>(vec, want_grad, static_cast<const double *>(logits->data), y, mask, n_tok,
+                       vocab, z_coef, grad_out, ctl,
+                       want_grad ? static_cast<double *>(grad_logits->data) : nullptr, rows, s,
+                       timers);
+  if (hipGetLastError() != hipSuccess) return LCE_DEVICE_ERROR;
+  Control hc;
+  if (hipMemcpyAsync(&hc, ctl, sizeof(Control), hipMemcpyDeviceToHost, s) != hipSuccess)
+    return LCE_DEVICE_ERROR;
+  if (hipStreamSynchronize(s) != hipSuccess) return LCE_DEVICE_ERROR;
+  if (hc.bad) return LCE_TARGET_OUT_OF_RANGE;
   out->loss_sum = hc.loss_sum;
   out->z_sum = hc.z_sum;
   out->n_counted = hc.count;

@@ -71,6 +71,12 @@ int32_t plan_distill(int64_t n, int64_t V, DistillPlan *p);
 bool finite_scalar(double x);
 size_t dtype_size(int32_t dtype);
 
+// Clears the control block and enqueues the target-range guard and the
+// counted-token count (defined with the CE kernels); `stream` is a
+// hipStream_t.
+void launch_target_guard(const int64_t *targets, const uint8_t *mask, int64_t n, int64_t V,
+                         Control *ctl, void *stream, lce_timers *tm);
+
 // Brackets one launch of kernel kind `kind` with the caller's events.
 struct TimedLaunch {
   lce_timer_slot *slot;

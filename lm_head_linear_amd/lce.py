@@ -44,9 +44,10 @@ class Peak(ctypes.Structure):
                 ("status", ctypes.c_int32)]
 
 
-NUM_KERNELS = 10
+NUM_KERNELS = 11
 KERNEL_KINDS = {"guard": 0, "fwd_gemm": 1, "fwd_merge": 2, "reduce": 3, "dlogit_gemm": 4,
-                "dw_gemm": 5, "dh_gemm": 6, "dh_final": 7, "distill": 8, "bwd_gemm": 9}
+                "dw_gemm": 5, "dh_gemm": 6, "dh_final": 7, "distill": 8, "bwd_gemm": 9,
+                "label_ce": 10}
 
 
 class TimerSlot(ctypes.Structure):
@@ -146,6 +147,9 @@ def lib():
         L.lce_distill_fwd_bwd.restype = i32
         L.lce_distill_fwd_bwd.argtypes = [PT, PT, PT, i64, i64, i32, dbl, dbl, dbl, PT, PT,
                                           ctypes.POINTER(Loss), vp]
+        L.lce_ce_logits_fwd_bwd.restype = i32
+        L.lce_ce_logits_fwd_bwd.argtypes = [PT, PT, PT, i64, i64, dbl, dbl, PT, PT,
+                                            ctypes.POINTER(Loss), vp]
         PTM = ctypes.POINTER(Timers)
         L.lce_forward_timed.restype = i32
         L.lce_forward_timed.argtypes = L.lce_forward.argtypes + [PTM]
@@ -153,6 +157,8 @@ def lib():
         L.lce_backward_timed.argtypes = L.lce_backward.argtypes + [PTM]
         L.lce_distill_fwd_bwd_timed.restype = i32
         L.lce_distill_fwd_bwd_timed.argtypes = L.lce_distill_fwd_bwd.argtypes + [PTM]
+        L.lce_ce_logits_fwd_bwd_timed.restype = i32
+        L.lce_ce_logits_fwd_bwd_timed.argtypes = L.lce_ce_logits_fwd_bwd.argtypes + [PTM]
         _lib = L
     return _lib
 
@@ -273,6 +279,24 @@ def lce_distill_fwd_bwd(student, teacher, loss_mask, n_tok, vocab, objective, te
     return st, out
 
 
+def lce_ce_logits_fwd_bwd(logits, targets, loss_mask, n_tok, vocab, z_coef, grad_out,
+                          grad_logits, workspace, stream: Optional[int] = None,
+                          timer: Optional[KernelTimer] = None):
+    """Direct call of the C entry point (the _timed variant when a timer is
+    given); grad_logits None computes the loss only.  Returns (status, Loss)."""
+    out = Loss()
+    ts = [_t(logits), _t(targets), _t(loss_mask)]
+    g, ws = _t(grad_logits), _t(workspace)
+    call = [*[ctypes.byref(a) for a in ts], n_tok, vocab, float(z_coef), float(grad_out),
+            ctypes.byref(g), ctypes.byref(ws), ctypes.byref(out),
+            stream if stream is not None else _stream(logits.device)]
+    if timer is None:
+        st = lib().lce_ce_logits_fwd_bwd(*call)
+    else:
+        st = lib().lce_ce_logits_fwd_bwd_timed(*call, ctypes.byref(timer.struct))
+    return st, out
+
+
 # ------------------------------------------------- allocating conveniences
 
 def _acc_dtype(dt: torch.dtype) -> torch.dtype:
@@ -336,4 +360,22 @@ def distill(student, teacher, loss_mask=None, objective=0, temperature=1.0, z_co
                                   z_coef, grad_out, g, ws)
     if st != OK:
         raise LceError(st, "lce_distill_fwd_bwd")
+    return out.as_dict(), g
+
+
+def ce_logits(logits, targets, loss_mask=None, z_coef=0.0, grad_out=1.0, want_grad=True,
+              workspace=None):
+    """Label cross-entropy + z-loss from materialized logits [n][V]: allocate
+    grad_logits (unless want_grad is False) and the workspace, call
+    lce_ce_logits_fwd_bwd.  Returns (loss dict, grad_logits or None)."""
+    n, V = logits.shape
+    g = torch.empty_like(logits) if want_grad else None
+    nbytes = lce_distill_workspace_bytes(n, V)
+    if nbytes < 0:
+        raise LceError(int(-nbytes), "lce_distill_workspace_bytes")
+    ws = workspace if workspace is not None else torch.empty(nbytes, dtype=torch.uint8,
+                                                             device=logits.device)
+    st, out = lce_ce_logits_fwd_bwd(logits, targets, loss_mask, n, V, z_coef, grad_out, g, ws)
+    if st != OK:
+        raise LceError(st, "lce_ce_logits_fwd_bwd")
     return out.as_dict(), g

@@ -46,8 +46,8 @@
 #include <stdlib.h>
 #include <string.h>
 
-/* Status vocabulary of lossk, [P1] "Status codes"; 589 and 590 are this
- * build's own extensions inside lossk's 580-599 range. */
+/* Status vocabulary of lossk, [P1] "Status codes"; 589 and 590 are
+ * extensions inside lossk's 580-599 range. */
 enum {
   ORC_OK = 580,
   ORC_EMPTY_DIMENSION = 581,
@@ -63,7 +63,7 @@ enum {
 };
 
 /* [P1] lossk table: total-work ceiling 2^46 cells, peak-logit ceiling 2^27
- * cells.  The per-dimension ceilings are this build's reading (the page says
+ * cells.  The per-dimension ceilings are a reading (the page says
  * only that each dimension is "under its ceiling"). */
 #define ORC_MAX_WORK_CELLS (((int64_t)1) << 46)
 #define ORC_MAX_LOGIT_CELLS (((int64_t)1) << 27)

@@ -13,6 +13,8 @@ bf16 workloads draw in fp32 and round to bf16 (round to nearest even, done by
 torch); the oracle reads exactly those bf16 values widened to fp64.
 Distillation: student ~ N(0, 4^2), teacher = student + N(0, 1), both rounded
 to the workload dtype after the sum.
+Label cross-entropy from logits: logits ~ N(0, 4^2) rounded to the dtype,
+then targets uniform in [0, vocab), then the mask.
 """
 from __future__ import annotations
 
@@ -62,6 +64,21 @@ LARGE_BF16 = CEWorkload("large_head_bf16_8192x4096x128256", 8192, 4096, 128256, 
                         0.02, 1e-4, 0.0, "zipf1.1", 4)
 DISTILL_BF16 = DistillWorkload("distill_bf16_4096x151936", 4096, 151936, "bf16", 2.0, 1e-4,
                                0.10, 5)
+
+
+@dataclass(frozen=True)
+class LabelWorkload:
+    name: str
+    n_tok: int
+    vocab: int
+    dtype: str
+    z_coef: float
+    mask_frac: float
+    seed: int
+
+
+# Label cross-entropy over materialized logits at the distillation shape.
+LABEL_BF16 = LabelWorkload("label_ce_bf16_4096x151936", 4096, 151936, "bf16", 1e-4, 0.10, 6)
 
 
 def torch_dtype(name: str):
@@ -155,3 +172,27 @@ def distill_inputs(w: DistillWorkload, n_tok: Optional[int] = None,
         S, U = torch.from_numpy(s).to(torch_dtype(dt)), torch.from_numpy(u).to(torch_dtype(dt))
     m = exact_mask(rng, n, w.mask_frac)
     return DistillInputs(S, U, m)
+
+
+@dataclass
+class LabelInputs:
+    logits: torch.Tensor      # CPU tensor in the workload dtype
+    targets: np.ndarray       # int64
+    mask: Optional[np.ndarray]
+
+
+def label_inputs(w: LabelWorkload, n_tok: Optional[int] = None, vocab: Optional[int] = None,
+                 seed: Optional[int] = None, dtype: Optional[str] = None) -> LabelInputs:
+    n = n_tok or w.n_tok
+    V = vocab or w.vocab
+    dt = dtype or w.dtype
+    rng = np.random.default_rng(w.seed if seed is None else seed)
+    if dt == "f64":
+        Z = torch.from_numpy(rng.standard_normal((n, V), dtype=np.float64) * 4.0)
+    else:
+        z = rng.standard_normal((n, V), dtype=np.float32)
+        z *= np.float32(4.0)
+        Z = torch.from_numpy(z).to(torch_dtype(dt))
+    y = rng.integers(0, V, n, dtype=np.int64)
+    m = exact_mask(rng, n, w.mask_frac)
+    return LabelInputs(Z, y, m)

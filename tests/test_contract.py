@@ -88,3 +88,24 @@ def test_loss_fetch_refuses_short_workspace_without_device():
     ws = torch.zeros(100, dtype=torch.uint8)
     assert lce.lce_loss_fetch(ws, stream=0)[0] == 582
     assert lce.lce_loss_fetch(torch.zeros(1024, dtype=torch.int32), stream=0)[0] == 590
+
+
+def test_ce_logits_refusals_without_device():
+    """Host-side validation of lce_ce_logits_fwd_bwd returns before any
+    device call (dims, scalars, dtypes, lengths in that order)."""
+    Z = torch.zeros(4, 16, dtype=torch.bfloat16)
+    y = torch.zeros(4, dtype=torch.int64)
+    ws = torch.zeros(lce.lce_distill_workspace_bytes(4, 16) + 256, dtype=torch.uint8)
+    call = lambda **kw: lce.lce_ce_logits_fwd_bwd(**{**dict(
+        logits=Z, targets=y, loss_mask=None, n_tok=4, vocab=16, z_coef=0.0, grad_out=1.0,
+        grad_logits=Z, workspace=ws, stream=0), **kw})[0]
+    assert call(n_tok=0) == 581
+    assert call(vocab=0) == 581
+    assert call(z_coef=float("inf")) == 585
+    assert call(grad_out=float("nan")) == 585
+    assert call(targets=y.int()) == 590
+    assert call(grad_logits=Z.float()) == 590
+    assert call(loss_mask=torch.zeros(4, dtype=torch.int32)) == 590
+    assert call(logits=Z[:3]) == 582
+    assert call(targets=y[:3]) == 582
+    assert call(workspace=ws[:16]) == 582

@@ -1,0 +1,121 @@
+"""GPU parity of lce_ce_logits_fwd_bwd (label cross-entropy + z-loss from
+materialized logits) against the CPU fp64 oracle, through the C ABI.
+bf16/fp32: loss relative error <= 2e-3, gradient max|diff| <= 1e-2 * max|ref|;
+fp64: 1e-10 for both."""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from lm_head_linear_amd import lce
+from tests import synthetic as syn
+
+pytestmark = pytest.mark.gpu
+TOL = {"bf16": (2e-3, 1e-2), "f32": (2e-3, 1e-2), "f64": (1e-10, 1e-10)}
+
+
+def _dev():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    return torch.device("cuda:0")
+
+
+def normwise(a, ref):
+    return float(np.max(np.abs(a - ref)) / max(float(np.max(np.abs(ref))), 1e-300))
+
+
+@pytest.mark.parametrize("dt", ["bf16", "f32", "f64"])
+@pytest.mark.parametrize("n,V,mask_frac", [(37, 1000, 0.2), (20, 1003, 0.0), (3, 4096, 0.34)])
+def test_small_label_ce(dt, n, V, mask_frac):
+    print(f"case label {dt} n={n} V={V} mask {mask_frac}", flush=True)
+    dev = _dev()
+    w = syn.LabelWorkload("small", n, V, dt, 1e-3, mask_frac, 40 + n)
+    d = syn.label_inputs(w)
+    Z = d.logits.to(dev)
+    y = torch.from_numpy(d.targets).to(dev)
+    m = torch.from_numpy(d.mask).to(dev) if d.mask is not None else None
+    out, g = lce.ce_logits(Z, y, m, z_coef=1e-3, grad_out=1.3)
+    r = oracle.ce_logits(d.logits.double().numpy(), d.targets, mask=d.mask, z_coef=1e-3,
+                         grad_out=1.3)
+    lt, gt = TOL[dt]
+    assert out["n_counted"] == r["n_counted"]
+    el = abs(out["loss_mean"] - r["loss"]) / abs(r["loss"])
+    ez = abs(out["z_mean"] - r["z_loss"]) / abs(r["z_loss"])
+    eg = normwise(g.double().cpu().numpy(), r["grad"])
+    print(f"  loss rel {el:.2e} z rel {ez:.2e} grad {eg:.2e}", flush=True)
+    assert el <= lt and ez <= lt and eg <= gt
+    if m is not None:
+        assert not g[m == 0].any()
+    # loss only: the same scalars without a gradient pass
+    out2, g2 = lce.ce_logits(Z, y, m, z_coef=1e-3, grad_out=1.3, want_grad=False)
+    assert g2 is None
+    assert out2["loss_sum"] == out["loss_sum"] and out2["z_sum"] == out["z_sum"]
+
+
+def test_uniform_logits_give_log_vocab():
+    dev = _dev()
+    n, V = 5, 151936
+    Z = torch.zeros(n, V, dtype=torch.bfloat16, device=dev)
+    y = torch.tensor([0, 1, V // 2, V - 2, V - 1], device=dev)
+    out, g = lce.ce_logits(Z, y)
+    assert abs(out["loss_mean"] - math.log(V)) <= 2e-3 * math.log(V)
+    want = np.full((n, V), 1.0 / (n * V))
+    want[np.arange(n), y.cpu().numpy()] -= 1.0 / n
+    assert normwise(g.double().cpu().numpy(), want) <= 1e-2
+
+
+def test_label_refusals_leave_outputs_untouched():
+    dev = _dev()
+    d = syn.label_inputs(syn.LABEL_BF16, n_tok=8, vocab=64, seed=7)
+    Z = d.logits.to(dev)
+    y = torch.from_numpy(d.targets).to(dev)
+    g = torch.full_like(Z, 9.0)
+    ws = torch.empty(lce.lce_distill_workspace_bytes(8, 64), dtype=torch.uint8, device=dev)
+    call = lambda **kw: lce.lce_ce_logits_fwd_bwd(**{**dict(
+        logits=Z, targets=y, loss_mask=None, n_tok=8, vocab=64, z_coef=0.0, grad_out=1.0,
+        grad_logits=g, workspace=ws), **kw})[0]
+    bad = y.clone()
+    bad[5] = 64
+    assert call(targets=bad) == 586
+    bad[5] = -1
+    assert call(targets=bad) == 586
+    assert call(z_coef=float("nan")) == 585
+    assert call(grad_logits=g.float()) == 590
+    assert call(targets=y.int()) == 590
+    assert call(grad_logits=g[:4]) == 582
+    assert call(workspace=ws[:64]) == 582
+    assert call(n_tok=0) == 581
+    torch.cuda.synchronize()
+    assert torch.all(g == 9.0)
+    assert call() == 580
+
+
+def test_label_ce_full_size_sampled_rows():
+    """4096 x 151936 bf16 logits, 10% masked, z 1e-4: the loss of every row
+    and the gradient of sampled rows against the oracle."""
+    w = syn.LABEL_BF16
+    dev = _dev()
+    print(f"case {w.name}: generating inputs", flush=True)
+    d = syn.label_inputs(w)
+    Z = d.logits.to(dev)
+    y = torch.from_numpy(d.targets).to(dev)
+    m = torch.from_numpy(d.mask).to(dev)
+    out, g = lce.ce_logits(Z, y, m, z_coef=w.z_coef)
+    torch.cuda.synchronize()
+    Z64 = d.logits.double().numpy()
+    full = oracle.ce_logits(Z64, d.targets, mask=d.mask, z_coef=w.z_coef, want_grad=False)
+    el = abs(out["loss_mean"] - full["loss"]) / abs(full["loss"])
+    ez = abs(out["z_mean"] - full["z_loss"]) / abs(full["z_loss"])
+    print(f"  loss {out['loss_mean']:.6g} rel {el:.2e} z rel {ez:.2e}", flush=True)
+    assert out["n_counted"] == full["n_counted"]
+    assert el <= 2e-3 and ez <= 2e-3
+    rng = np.random.default_rng(6)
+    rows = np.unique(np.concatenate([[0, w.n_tok - 1], rng.choice(w.n_tok, 10, replace=False),
+                                     np.flatnonzero(d.mask == 0)[:2]]))
+    gr, rl, rz = oracle.ce_logits_rows(Z64[rows], d.targets[rows], full["n_counted"],
+                                       row_mask=d.mask[rows], z_coef=w.z_coef)
+    eg = normwise(g[torch.from_numpy(rows).to(dev)].double().cpu().numpy(), gr)
+    print(f"  sampled grad {eg:.2e}", flush=True)
+    assert eg <= 1e-2
