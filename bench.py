@@ -162,6 +162,58 @@ def label_measure(lce, torch, np, dev, steps: int):
     return res
 
 
+def shard_measure(lce, torch, np, dev, w, H, W, y, m, steps: int, shards: int):
+    """The same training step as vocabulary shards run one after another on
+    this GPU (each shard's forward, the exchange, each shard's backward with
+    its d_hidden partial added up): what one GPU's share of a vocab-parallel
+    head costs, and the exchange's overhead against the unsharded step."""
+    n, D = H.shape
+    V = W.shape[0]
+    bounds = [V * q // shards // 256 * 256 for q in range(shards)] + [V]
+    acc = torch.float32 if H.dtype == torch.bfloat16 else torch.float64
+    stats = torch.empty(shards, 3, n, dtype=acc, device=dev)
+    lse = torch.empty(n, dtype=acc, device=dev)
+    part = torch.empty(n, D, dtype=acc, device=dev)
+    dH = torch.empty(n, D, dtype=acc, device=dev)
+    dW = torch.empty(V, D, dtype=acc, device=dev)
+    rows = max(bounds[q + 1] - bounds[q] for q in range(shards))
+    ws = torch.empty(lce.lce_workspace_bytes(n, D, rows, w.chunk, H.dtype), dtype=torch.uint8,
+                     device=dev)
+    mws = torch.empty(lce.lce_distill_workspace_bytes(n, 1), dtype=torch.uint8, device=dev)
+
+    def step():
+        for q in range(shards):
+            a, b = bounds[q], bounds[q + 1]
+            st = lce.lce_shard_forward(H, W[a:b], y, n, D, b - a, a, V, w.chunk, stats[q], ws)
+            if st != lce.OK:
+                raise lce.LceError(st, "lce_shard_forward")
+        st, out = lce.lce_shard_merge(stats, shards, m, n, lse, mws)
+        if st != lce.OK:
+            raise lce.LceError(st, "lce_shard_merge")
+        for q in range(shards):
+            a, b = bounds[q], bounds[q + 1]
+            st = lce.lce_shard_backward(H, W[a:b], y, m, lse, n, D, b - a, a, V, w.chunk,
+                                        w.z_coef, 1.0, part, dW[a:b], 0, ws)
+            if st != lce.OK:
+                raise lce.LceError(st, "lce_shard_backward")
+            if q == 0:
+                dH.copy_(part)
+            else:
+                dH.add_(part)
+        return out
+
+    for _ in range(2):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        out = step()
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) / steps * 1e3
+    return {"shards": shards, "bounds": bounds, "ms_per_step": round(ms, 4),
+            "tokens_per_s": round(n / (ms / 1e3), 1), "loss": out.loss_mean}
+
+
 def cpu_baseline(w, x, tokens: int):
     """The oracle, as it stands, on the first `tokens` tokens of the workload:
     forward (all tokens of the prefix) + backward (d_hidden of the prefix and
@@ -199,7 +251,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-kernel-events", action="store_true")
     ap.add_argument("--no-distill", action="store_true",
-                    help="skip the logits-in measurements (distillation, label CE; 4096 x 151936 bf16)")
+                    help="skip the side measurements (vocabulary shards; distillation and label CE at 4096 x 151936 bf16)")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -344,6 +396,12 @@ def main():
                 "frac": round(achieved / peak, 4), "traffic": traffic_from_profiles(w.name, dom),
                 "kernel": dom, "flops_per_launch": per_launch_flops, "avg_launch_ms": kd["avg_ms"]}
 
+    shard = None
+    if w.dtype == "bf16" and not args.no_distill:
+        log("bench: the same step in 4 vocabulary shards")
+        shard = shard_measure(lce, torch, np, dev, w, H, W, y, m, args.steps, 4)
+        shard["vs_unsharded"] = round(ms_per_step / shard["ms_per_step"], 4)
+
     distill = label = None
     if not args.no_distill and w.dtype == "bf16":
         distill = distill_measure(lce, torch, np, dev, args.steps)
@@ -382,6 +440,7 @@ def main():
         "roofline": roof,
         "distill": distill,
         "label_ce": label,
+        "vocab_shards": shard,
         "cpu_baseline": cpu,
     }
     print(json.dumps(res), flush=True)

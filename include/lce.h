@@ -210,6 +210,60 @@ int32_t lce_distill_fwd_bwd(const lce_tensor *student, const lce_tensor *teacher
                             double grad_out, lce_tensor *grad_logits, lce_tensor *workspace,
                             lce_loss *out, void *stream);
 
+/* ---- vocabulary shards: one GPU's rows of a vocabulary-parallel head ---- */
+
+/* The lossk reduction (per token lse and target logit, "Loss functions and
+ * resident-context kernels", lossk table) split over row ranges of the head:
+ * each shard reports per-token {m, s, z} and an exchange folds them, in the
+ * form the Fast-LLM 566 tensor-parallel tests exercise ("Changes",
+ * "Validation").  Shards must partition [0, vocab_total).
+ *   weight_shard rows [vocab_offset, vocab_offset + vocab_shard) of the head,
+ *                [vocab_shard*d_model], dtype as hidden
+ *   targets      global ids, each 0 <= y < vocab_total (else 586)
+ *   vocab_total  rows of the whole head; vocab_offset >= 0 and
+ *                vocab_offset + vocab_shard <= vocab_total (else 582;
+ *                vocab_total > LCE_MAX_VOCAB: 583)
+ *   chunk        bounds the shard's logit buffers: chunk * vocab_shard cells
+ *   workspace    numel >= lce_workspace_bytes(n_tok, d_model, vocab_shard,
+ *                chunk, dtype)
+ * lce_shard_forward writes stats[3*n_tok] in the accumulator dtype (LCE_F32
+ * for bf16 inputs, LCE_F64 for fp64): stats[t] = m_t, the shard's largest
+ * logit of token t; stats[n_tok + t] = s_t = sum over the shard's rows of
+ * exp(z - m_t); stats[2*n_tok + t] = z[t][y_t] when the shard holds row y_t,
+ * else 0.  It synchronizes the stream (target guard). */
+int32_t lce_shard_forward(const lce_tensor *hidden, const lce_tensor *weight_shard,
+                          const lce_tensor *targets, int64_t n_tok, int64_t d_model,
+                          int64_t vocab_shard, int64_t vocab_offset, int64_t vocab_total,
+                          int64_t chunk, lce_tensor *stats, lce_tensor *workspace, void *stream);
+
+/* The exchange: stats holds n_shards records of 3*n_tok values each (shard q
+ * at stats[q*3*n_tok], any order of shards gives the same rows; they are
+ * folded in index order): lse_t = M + log sum_q s_q exp(m_q - M) with M the
+ * largest m_q, z_y = sum_q z_q; loss and z-loss over counted tokens as
+ * lce_forward.
+ *   stats     LCE_F32 or LCE_F64, numel >= n_shards*3*n_tok
+ *   loss_mask [n_tok] LCE_U8 or data == NULL
+ *   lse_out   [n_tok], stats' dtype (the backward's lse)
+ *   workspace LCE_U8, numel >= lce_distill_workspace_bytes(n_tok, 1)
+ *   out       host loss scalars; synchronizes the stream. */
+int32_t lce_shard_merge(const lce_tensor *stats, int32_t n_shards, const lce_tensor *loss_mask,
+                        int64_t n_tok, lce_tensor *lse_out, lce_tensor *workspace, lce_loss *out,
+                        void *stream);
+
+/* A shard's backward with the merged lse: d_weight_shard [vocab_shard *
+ * d_model] (LCE_F32 | LCE_F64; overwritten, or added to when
+ * accumulate_d_weight != 0) and the shard's d_hidden partial
+ * sum over its rows of dlogit * W, [n_tok*d_model] in the accumulator dtype
+ * (overwritten); the sum of the partials over all shards is d_hidden.
+ * Other arguments and statuses as lce_backward. */
+int32_t lce_shard_backward(const lce_tensor *hidden, const lce_tensor *weight_shard,
+                           const lce_tensor *targets, const lce_tensor *loss_mask,
+                           const lce_tensor *lse, int64_t n_tok, int64_t d_model,
+                           int64_t vocab_shard, int64_t vocab_offset, int64_t vocab_total,
+                           int64_t chunk, double z_coef, double grad_out,
+                           lce_tensor *d_hidden_partial, lce_tensor *d_weight_shard,
+                           int32_t accumulate_d_weight, lce_tensor *workspace, void *stream);
+
 /* Label cross-entropy with z-loss from materialized logits, fused forward +
  * backward: the lossk page's ce_from_logits reference function ("Loss
  * functions and resident-context kernels", lossk table) on the device, with

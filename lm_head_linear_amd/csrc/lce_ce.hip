@@ -48,7 +48,8 @@ __global__ void ctl_init_kernel(Control *ctl, int keep_loss) {
 }
 
 // Target-range guard (lossk table, loss_targets_in_range) and the count of
-// counted tokens.  Integer work only, so the atomics are order-free.
+// counted tokens (y == nullptr: the count only).  Integer work only, so the
+// atomics are order-free.
 __global__ void guard_kernel(const int64_t *y, const uint8_t *mask, int64_t n, int64_t V,
                              Control *ctl) {
   __shared__ unsigned long long s_first[4];
@@ -56,7 +57,7 @@ __global__ void guard_kernel(const int64_t *y, const uint8_t *mask, int64_t n, i
   unsigned long long first = ULLONG_MAX, count = 0;
   for (int64_t t = int64_t(blockIdx.x) * blockDim.x + threadIdx.x; t < n;
        t += int64_t(gridDim.x) * blockDim.x) {
-    const int64_t v = y[t];
+    const int64_t v = y ? y[t] : 0;
     if (v < 0 || v >= V) first = first < (unsigned long long)t ? first : (unsigned long long)t;
     count += mask ? (mask[t] != 0) : 1;
   }
@@ -78,6 +79,17 @@ __global__ void guard_kernel(const int64_t *y, const uint8_t *mask, int64_t n, i
       atomicMin(reinterpret_cast<unsigned long long *>(&ctl->first_bad), first);
       atomicExch(&ctl->bad, 1);
     }
+  }
+}
+
+// Vocabulary shard of rows [offset, offset + rows): a token's target id
+// relative to the shard, or -1 when another shard holds the target row.
+__global__ void localize_targets_kernel(const int64_t *y, int64_t n, int64_t offset, int64_t rows,
+                                        int64_t *yl) {
+  for (int64_t t = int64_t(blockIdx.x) * blockDim.x + threadIdx.x; t < n;
+       t += int64_t(gridDim.x) * blockDim.x) {
+    const int64_t v = y[t] - offset;
+    yl[t] = (v >= 0 && v < rows) ? v : -1;
   }
 }
 
@@ -191,7 +203,8 @@ struct FwdLseEpi {
 };
 
 // zy[t] = <H[t], W[y_t]> for every token: one wave per token, lane-strided
-// partial sums in the accumulator type and a fixed shuffle tree.
+// partial sums in the accumulator type and a fixed shuffle tree.  A negative
+// id (target in another vocabulary shard) gives 0.
 template <class TR>
 __global__ void target_logit_kernel(const typename TR::E *H, const typename TR::E *W,
                                     const int64_t *y, int64_t n, int64_t D,
@@ -201,6 +214,10 @@ __global__ void target_logit_kernel(const typename TR::E *H, const typename TR::
   const int lane = threadIdx.x & 63;
   const int64_t t = int64_t(blockIdx.x) * (blockDim.x >> 6) + (threadIdx.x >> 6);
   if (t >= n) return;
+  if (y[t] < 0) {   // target row held by another vocabulary shard
+    if (lane == 0) zy[t] = 0;
+    return;
+  }
   const typename TR::E *h = H + t * D;
   const typename TR::E *w = W + y[t] * D;
   Acc s = 0;
@@ -228,10 +245,13 @@ __global__ void target_logit_kernel(const typename TR::E *H, const typename TR::
 }
 
 // One wave per token: fold the token's (max, sum) pairs in a fixed order.
+// stats == nullptr: lse and the per-token loss; otherwise the vocabulary
+// shard's exchange record {m, s, z_target} at stats[0/1/2][t] (row stride
+// stride).
 template <class Acc>
 __global__ void fwd_merge_kernel(const Acc *partials, const Acc *zy, int64_t n_vparts,
                                  int64_t ntok, Acc *lse_out, double *loss_tok,
-                                 const int32_t *bad) {
+                                 const int32_t *bad, Acc *stats, int64_t stride) {
   if (*bad) return;
   const int lane = threadIdx.x & 63;
   const int64_t t = int64_t(blockIdx.x) * (blockDim.x >> 6) + (threadIdx.x >> 6);
@@ -248,9 +268,41 @@ __global__ void fwd_merge_kernel(const Acc *partials, const Acc *zy, int64_t n_v
   // Fixed tree; lane 0 holds the result.
   for (int o = 32; o > 0; o >>= 1) s += __shfl_down(s, o);
   if (lane == 0) {
-    const Acc lse = m + flog<Acc>(s);
+    if (stats) {
+      stats[t] = m;
+      stats[stride + t] = s;
+      stats[2 * stride + t] = zy[t];
+    } else {
+      const Acc lse = m + flog<Acc>(s);
+      lse_out[t] = lse;
+      loss_tok[t] = double(lse) - double(zy[t]);
+    }
+  }
+}
+
+// Exchange of vocabulary shards: per token, fold the shards' {m, s, z}
+// records (stats[p][0/1/2][t], shards in ascending order):
+//   M = max m_p,  lse = M + log sum_p s_p exp(m_p - M),  z_y = sum_p z_p
+// (z_p is 0 except in the shard that holds the target row).
+template <class Acc>
+__global__ void shard_merge_kernel(const Acc *stats, int64_t n_shards, int64_t n, Acc *lse_out,
+                                   double *loss_tok) {
+  for (int64_t t = int64_t(blockIdx.x) * blockDim.x + threadIdx.x; t < n;
+       t += int64_t(gridDim.x) * blockDim.x) {
+    Acc M = neg_inf<Acc>();
+    for (int64_t q = 0; q < n_shards; ++q) {
+      const Acc mq = stats[q * 3 * n + t];
+      M = mq > M ? mq : M;
+    }
+    Acc S = 0, Z = 0;
+    for (int64_t q = 0; q < n_shards; ++q) {
+      const Acc *r = stats + q * 3 * n;
+      S += r[n + t] * fexp<Acc>(r[t] - M);
+      Z += r[2 * n + t];
+    }
+    const Acc lse = M + flog<Acc>(S);
     lse_out[t] = lse;
-    loss_tok[t] = double(lse) - double(zy[t]);
+    loss_tok[t] = double(lse) - double(Z);
   }
 }
 
@@ -621,13 +673,16 @@ __global__ void zero_f32_kernel(float *p, int64_t count) {
     p[i] = 0.f;
 }
 
-// d_hidden = sum over splits (ascending) of the split accumulators.
-template <class TR>
+// d_hidden = sum over splits (ascending) of the split accumulators, in the
+// input dtype (OUT = TR::E) or unrounded (OUT = TR::Acc, a vocabulary shard's
+// partial).
+template <class TR, class OUT>
 __global__ void dh_final_kernel(const typename TR::Acc *P, int64_t splits, int64_t count,
-                                typename TR::E *out, const int32_t *bad, int vec4) {
+                                OUT *out, const int32_t *bad, int vec4) {
   if (*bad) return;
   int64_t begin = 0;
-  if constexpr (std::is_same<typename TR::Acc, float>::value) {
+  if constexpr (std::is_same<typename TR::Acc, float>::value &&
+                std::is_same<OUT, typename TR::E>::value) {
     // four consecutive elements per thread: 16-byte loads, one 8-byte store
     // (count % 4 == 0 and out 8-byte aligned: the host passes vec4 only then)
     if (vec4) {
@@ -649,7 +704,8 @@ __global__ void dh_final_kernel(const typename TR::Acc *P, int64_t splits, int64
        i += int64_t(gridDim.x) * blockDim.x) {
     typename TR::Acc s = 0;
     for (int64_t j = 0; j < splits; ++j) s += P[j * count + i];
-    out[i] = to_elem<TR>(s);
+    if constexpr (std::is_same<OUT, typename TR::Acc>::value) out[i] = s;
+    else out[i] = to_elem<TR>(s);
   }
 }
 
@@ -774,17 +830,42 @@ void launch_target_guard(const int64_t *targets, const uint8_t *mask, int64_t n,
   launch_guard(targets, mask, n, V, ctl, static_cast<hipStream_t>(stream), tm, 0);
 }
 
+// A vocabulary-shard call covers rows [offset, offset + V) of a head of
+// `total` rows (total == 0: the whole head).  Targets are checked against
+// `total` and used relative to the shard; the forward then ends with the
+// shard's exchange records instead of the loss.
+template <class Acc>
+struct Shard {
+  int64_t offset = 0, total = 0;
+  Acc *stats = nullptr;   // forward: {m, s, z_target} rows of n tokens
+};
+
+// Guard against the head's rows; for a shard, the targets relative to it.
+template <class Acc>
+static const int64_t *guard_targets(const CEPlan &p, const int64_t *y, const uint8_t *mask,
+                                    const Shard<Acc> &sh, Control *ctl, uint8_t *ws,
+                                    hipStream_t st, lce_timers *tm, int keep_loss) {
+  launch_guard(y, mask, p.n, sh.total ? sh.total : p.V, ctl, st, tm, keep_loss);
+  if (!sh.total) return y;
+  int64_t *yl = reinterpret_cast<int64_t *>(ws + p.off_yloc);
+  int64_t blocks = cdiv(p.n, 256);
+  if (blocks > 1024) blocks = 1024;
+  hipLaunchKernelGGL(localize_targets_kernel, dim3(unsigned(blocks)), dim3(256), 0, st, y, p.n,
+                     sh.offset, p.V, yl);
+  return yl;
+}
+
 template <class TR>
-static void forward_impl(const CEPlan &p, const void *H, const void *W, const int64_t *y,
+static void forward_impl(const CEPlan &p, const void *H, const void *W, const int64_t *y_in,
                          const uint8_t *mask, typename TR::Acc *lse_out, uint8_t *ws, bool vec,
-                         hipStream_t st, lce_timers *tm) {
+                         hipStream_t st, lce_timers *tm, const Shard<typename TR::Acc> &sh) {
   typedef typename TR::Acc Acc;
   Control *ctl = reinterpret_cast<Control *>(ws);
   Acc *partials = reinterpret_cast<Acc *>(ws + p.off_partials);
   Acc *zy = reinterpret_cast<Acc *>(ws + p.off_zy);
   double *loss_tok = reinterpret_cast<double *>(ws + p.off_losstok);
   const typename TR::E *Hp = static_cast<const typename TR::E *>(H);
-  launch_guard(y, mask, p.n, p.V, ctl, st, tm, 0);
+  const int64_t *y = guard_targets(p, y_in, mask, sh, ctl, ws, st, tm, 0);
   {
     TimedLaunch tl(tm, LCE_K_FWD_MERGE, st);
     hipLaunchKernelGGL(target_logit_kernel<TR>, dim3(unsigned(cdiv(p.n, 4))), dim3(256), 0, st,
@@ -821,8 +902,10 @@ static void forward_impl(const CEPlan &p, const void *H, const void *W, const in
     TimedLaunch tl(tm, LCE_K_FWD_MERGE, st);
     hipLaunchKernelGGL(fwd_merge_kernel<Acc>, dim3(unsigned(cdiv(ntok, 4))), dim3(256), 0, st,
                        (const Acc *)partials, (const Acc *)(zy + tok0), p.n_vparts, ntok,
-                       lse_out + tok0, loss_tok + tok0, (const int32_t *)&ctl->bad);
+                       lse_out ? lse_out + tok0 : nullptr, loss_tok + tok0,
+                       (const int32_t *)&ctl->bad, sh.stats ? sh.stats + tok0 : nullptr, p.n);
   }
+  if (sh.stats) return;   // a shard's records; the exchange forms the loss
   TimedLaunch tl(tm, LCE_K_REDUCE, st);
   hipLaunchKernelGGL(fwd_final_kernel<Acc>, dim3(1), dim3(1024), 0, st, (const double *)loss_tok,
                      (const Acc *)lse_out, mask, p.n, ctl);
@@ -908,11 +991,27 @@ static void backward_pipelined(const CEPlan &p, const uint16_t *Hp, const uint16
 }
 
 template <class TR>
-static void backward_impl(const CEPlan &p, const void *H, const void *W, const int64_t *y,
+static void launch_dh_final(const typename TR::Acc *P, int64_t splits, int64_t count, void *dH,
+                            bool acc_out, const int32_t *bad, hipStream_t st, lce_timers *tm) {
+  int64_t blocks = cdiv(count, 256);
+  if (blocks > 4096) blocks = 4096;
+  TimedLaunch tl(tm, LCE_K_DH_FINAL, st);
+  typedef typename TR::Acc Acc;
+  typedef typename TR::E E;
+  if (acc_out)
+    hipLaunchKernelGGL((dh_final_kernel<TR, Acc>), dim3(unsigned(blocks)), dim3(256), 0, st, P,
+                       splits, count, static_cast<Acc *>(dH), bad, 0);
+  else
+    hipLaunchKernelGGL((dh_final_kernel<TR, E>), dim3(unsigned(blocks)), dim3(256), 0, st, P,
+                       splits, count, static_cast<E *>(dH), bad, fold_vec4(count, dH));
+}
+
+template <class TR>
+static void backward_impl(const CEPlan &p, const void *H, const void *W, const int64_t *y_in,
                           const uint8_t *mask, const typename TR::Acc *lse, double z_coef,
-                          double grad_out, typename TR::E *dH, typename TR::Acc *dW,
+                          double grad_out, void *dH, bool dh_acc, typename TR::Acc *dW,
                           int accumulate, uint8_t *ws, bool vec, hipStream_t st,
-                          lce_timers *tm) {
+                          lce_timers *tm, const Shard<typename TR::Acc> &sh) {
   typedef typename TR::Acc Acc;
   typedef typename TR::E E;
   Control *ctl = reinterpret_cast<Control *>(ws);
@@ -920,7 +1019,7 @@ static void backward_impl(const CEPlan &p, const void *H, const void *W, const i
   Acc *dhacc = reinterpret_cast<Acc *>(ws + p.off_dhacc);
   const E *Hp = static_cast<const E *>(H);
   const E *Wp = static_cast<const E *>(W);
-  launch_guard(y, mask, p.n, p.V, ctl, st, tm, 1);
+  const int64_t *y = guard_targets(p, y_in, mask, sh, ctl, ws, st, tm, 1);
   const bool pipe = UsePipe<TR>::ok(vec, p.D, p.d_ld);
   E *Ht = nullptr;
   Acc *zyb = nullptr;
@@ -943,13 +1042,8 @@ static void backward_impl(const CEPlan &p, const void *H, const void *W, const i
         else
           backward_pipelined<false>(p, Hp, Wp, y, mask, lse, z_coef, grad_out, dW, dbuf, dhacc,
                                     Ht, zyb, ctl, st, tm);
-        const int64_t count = p.n * p.D;
-        int64_t blocks = cdiv(count, 256);
-        if (blocks > 4096) blocks = 4096;
-        TimedLaunch tl(tm, LCE_K_DH_FINAL, st);
-        hipLaunchKernelGGL(dh_final_kernel<TR>, dim3(unsigned(blocks)), dim3(256), 0, st,
-                           (const Acc *)dhacc, p.pdh_splits, count, dH,
-                           (const int32_t *)&ctl->bad, fold_vec4(count, dH));
+        launch_dh_final<TR>(dhacc, p.pdh_splits, p.n * p.D, dH, dh_acc,
+                            (const int32_t *)&ctl->bad, st, tm);
         return;
       }
     }
@@ -1011,13 +1105,8 @@ static void backward_impl(const CEPlan &p, const void *H, const void *W, const i
       else launch_any<TR, false, false>(pipe, vec, g, p.dh_splits, e_set, st);
     }
   }
-  int64_t count = p.n * p.D;
-  int64_t blocks = cdiv(count, 256);
-  if (blocks > 4096) blocks = 4096;
-  TimedLaunch tl(tm, LCE_K_DH_FINAL, st);
-  hipLaunchKernelGGL(dh_final_kernel<TR>, dim3(unsigned(blocks)), dim3(256), 0, st,
-                     (const Acc *)dhacc, p.dh_splits, count, dH, (const int32_t *)&ctl->bad,
-                     fold_vec4(count, dH));
+  launch_dh_final<TR>(dhacc, p.dh_splits, p.n * p.D, dH, dh_acc, (const int32_t *)&ctl->bad,
+                      st, tm);
 }
 
 }  // namespace lce
@@ -1050,6 +1139,29 @@ int32_t check_ce_lengths(const lce_tensor *hidden, const lce_tensor *weight,
   if (has(loss_mask) && loss_mask->numel < n) return LCE_LENGTH_MISMATCH;
   return LCE_OK;
 }
+
+// A vocabulary shard: rows [offset, offset + vocab) inside a head of `total`
+// rows (total == 0: the call covers the whole head).
+int32_t check_shard(int64_t vocab, int64_t offset, int64_t total) {
+  if (total == 0) return LCE_OK;
+  if (total < 0) return LCE_EMPTY_DIMENSION;
+  if (total > LCE_MAX_VOCAB) return LCE_DIMENSION_TOO_LARGE;
+  if (offset < 0 || offset > total - vocab) return LCE_LENGTH_MISMATCH;
+  return LCE_OK;
+}
+
+int32_t forward_call(const lce_tensor *hidden, const lce_tensor *weight,
+                     const lce_tensor *targets, const lce_tensor *loss_mask, int64_t n_tok,
+                     int64_t d_model, int64_t vocab, int64_t chunk, double z_coef,
+                     lce_tensor *lse_out, lce_tensor *workspace, lce_loss *out, void *stream,
+                     lce_timers *timers, int64_t offset, int64_t total, lce_tensor *stats);
+int32_t backward_call(const lce_tensor *hidden, const lce_tensor *weight,
+                      const lce_tensor *targets, const lce_tensor *loss_mask,
+                      const lce_tensor *lse, int64_t n_tok, int64_t d_model, int64_t vocab,
+                      int64_t chunk, double z_coef, double grad_out, lce_tensor *d_hidden,
+                      lce_tensor *d_weight, int32_t accumulate_d_weight,
+                      lce_tensor *workspace, void *stream, lce_timers *timers, int64_t offset,
+                      int64_t total);
 
 int32_t finish(hipStream_t st, Control *dev_ctl, Control *host_ctl) {
   if (hipGetLastError() != hipSuccess) return LCE_DEVICE_ERROR;
@@ -1084,7 +1196,84 @@ int32_t lce_forward_timed(const lce_tensor *hidden, const lce_tensor *weight,
                           int64_t d_model, int64_t vocab, int64_t chunk, double z_coef,
                           lce_tensor *lse_out, lce_tensor *workspace, lce_loss *out,
                           void *stream, lce_timers *timers) {
+  return forward_call(hidden, weight, targets, loss_mask, n_tok, d_model, vocab, chunk, z_coef,
+                      lse_out, workspace, out, stream, timers, 0, 0, nullptr);
+}
+
+int32_t lce_shard_forward(const lce_tensor *hidden, const lce_tensor *weight_shard,
+                          const lce_tensor *targets, int64_t n_tok, int64_t d_model,
+                          int64_t vocab_shard, int64_t vocab_offset, int64_t vocab_total,
+                          int64_t chunk, lce_tensor *stats, lce_tensor *workspace, void *stream) {
+  lce_loss unused;
+  return forward_call(hidden, weight_shard, targets, nullptr, n_tok, d_model, vocab_shard, chunk,
+                      0.0, nullptr, workspace, &unused, stream, nullptr, vocab_offset, vocab_total,
+                      stats);
+}
+
+int32_t lce_shard_merge(const lce_tensor *stats, int32_t n_shards, const lce_tensor *loss_mask,
+                        int64_t n_tok, lce_tensor *lse_out, lce_tensor *workspace, lce_loss *out,
+                        void *stream) {
+  if (n_tok < 1 || n_shards < 1) return LCE_EMPTY_DIMENSION;
+  if (n_tok > LCE_MAX_N_TOK) return LCE_DIMENSION_TOO_LARGE;
+  if (!stats || !lse_out || !workspace || !out) return LCE_LENGTH_MISMATCH;
+  const int32_t adt = stats->dtype;
+  if (adt != LCE_F32 && adt != LCE_F64) return LCE_DTYPE_MISMATCH;
+  if (lse_out->dtype != adt) return LCE_DTYPE_MISMATCH;
+  if (has(loss_mask) && loss_mask->dtype != LCE_U8) return LCE_DTYPE_MISMATCH;
+  if (workspace->dtype != LCE_U8) return LCE_DTYPE_MISMATCH;
+  DistillPlan p;   // {control | n per-token doubles | ...} fits the same layout
+  int32_t st = plan_distill(n_tok, 1, &p);
+  if (st != LCE_OK) return st;
+  if (!has(stats) || stats->numel / 3 / n_shards < n_tok) return LCE_LENGTH_MISMATCH;
+  if (!has(lse_out) || lse_out->numel < n_tok) return LCE_LENGTH_MISMATCH;
+  if (has(loss_mask) && loss_mask->numel < n_tok) return LCE_LENGTH_MISMATCH;
+  if (!has(workspace) || workspace->numel < int64_t(p.total) + 256) return LCE_LENGTH_MISMATCH;
+
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  uint8_t *ws = ws_base(workspace);
+  Control *ctl = reinterpret_cast<Control *>(ws);
+  double *loss_tok = reinterpret_cast<double *>(ws + p.off_rows);
+  const uint8_t *mask = has(loss_mask) ? static_cast<const uint8_t *>(loss_mask->data) : nullptr;
+  (void)hipGetLastError();
+  launch_guard(nullptr, mask, n_tok, 1, ctl, s, nullptr, 0);   // counted tokens
+  int64_t blocks = cdiv(n_tok, 256);
+  if (blocks > 1024) blocks = 1024;
+  if (adt == LCE_F32) {
+    hipLaunchKernelGGL(shard_merge_kernel<float>, dim3(unsigned(blocks)), dim3(256), 0, s,
+                       static_cast<const float *>(stats->data), int64_t(n_shards), n_tok,
+                       static_cast<float *>(lse_out->data), loss_tok);
+    hipLaunchKernelGGL(fwd_final_kernel<float>, dim3(1), dim3(1024), 0, s,
+                       (const double *)loss_tok, static_cast<const float *>(lse_out->data), mask,
+                       n_tok, ctl);
+  } else {
+    hipLaunchKernelGGL(shard_merge_kernel<double>, dim3(unsigned(blocks)), dim3(256), 0, s,
+                       static_cast<const double *>(stats->data), int64_t(n_shards), n_tok,
+                       static_cast<double *>(lse_out->data), loss_tok);
+    hipLaunchKernelGGL(fwd_final_kernel<double>, dim3(1), dim3(1024), 0, s,
+                       (const double *)loss_tok, static_cast<const double *>(lse_out->data), mask,
+                       n_tok, ctl);
+  }
+  Control hc;
+  st = finish(s, ctl, &hc);
+  if (st != LCE_OK) return st;
+  fill_loss(hc, out);
+  return LCE_OK;
+}
+
+}  // extern "C"
+
+namespace {
+
+// The whole head (total == 0) or a vocabulary shard of rows [offset, offset
+// + vocab) of a `total`-row head (exchange records to `stats`).
+int32_t forward_call(const lce_tensor *hidden, const lce_tensor *weight,
+                     const lce_tensor *targets, const lce_tensor *loss_mask, int64_t n_tok,
+                     int64_t d_model, int64_t vocab, int64_t chunk, double z_coef,
+                     lce_tensor *lse_out, lce_tensor *workspace, lce_loss *out, void *stream,
+                     lce_timers *timers, int64_t offset, int64_t total, lce_tensor *stats) {
   int32_t st = lce_dims_check(n_tok, d_model, vocab);
+  if (st != LCE_OK) return st;
+  st = check_shard(vocab, offset, total);
   if (st != LCE_OK) return st;
   st = lce_chunk_check(chunk, vocab);
   if (st != LCE_OK) return st;
@@ -1092,15 +1281,16 @@ int32_t lce_forward_timed(const lce_tensor *hidden, const lce_tensor *weight,
   int32_t dt = 0;
   st = check_ce_tensors(hidden, weight, targets, loss_mask, n_tok, d_model, vocab, &dt);
   if (st != LCE_OK) return st;
-  if (!lse_out || !workspace) return LCE_LENGTH_MISMATCH;
-  if (lse_out->dtype != (dt == LCE_BF16 ? LCE_F32 : LCE_F64)) return LCE_DTYPE_MISMATCH;
+  lce_tensor *res = total ? stats : lse_out;   // [3 n] records or [n] lse
+  if (!res || !workspace) return LCE_LENGTH_MISMATCH;
+  if (res->dtype != (dt == LCE_BF16 ? LCE_F32 : LCE_F64)) return LCE_DTYPE_MISMATCH;
   if (workspace->dtype != LCE_U8) return LCE_DTYPE_MISMATCH;
   CEPlan p;
   st = plan_ce(n_tok, d_model, vocab, chunk, dt, &p);
   if (st != LCE_OK) return st;
   st = check_ce_lengths(hidden, weight, targets, loss_mask, n_tok, d_model, vocab);
   if (st != LCE_OK) return st;
-  if (!has(lse_out) || lse_out->numel < n_tok) return LCE_LENGTH_MISMATCH;
+  if (!has(res) || res->numel < (total ? 3 : 1) * n_tok) return LCE_LENGTH_MISMATCH;
   if (!has(workspace) || workspace->numel < int64_t(p.total) + 256) return LCE_LENGTH_MISMATCH;
 
   hipStream_t s = static_cast<hipStream_t>(stream);
@@ -1110,21 +1300,33 @@ int32_t lce_forward_timed(const lce_tensor *hidden, const lce_tensor *weight,
   (void)hipGetLastError();
   if (dt == LCE_BF16) {
     const bool vec = d_model % 8 == 0 && aligned16(hidden->data) && aligned16(weight->data);
+    Shard<float> sh;
+    sh.offset = offset; sh.total = total;
+    sh.stats = total ? static_cast<float *>(stats->data) : nullptr;
     forward_impl<TraitsBF16>(p, hidden->data, weight->data, y, mask,
-                             static_cast<float *>(lse_out->data), ws, vec, s, timers);
+                             total ? nullptr : static_cast<float *>(lse_out->data), ws, vec, s,
+                             timers, sh);
   } else {
     const bool vec = d_model % 2 == 0 && aligned16(hidden->data) && aligned16(weight->data);
+    Shard<double> sh;
+    sh.offset = offset; sh.total = total;
+    sh.stats = total ? static_cast<double *>(stats->data) : nullptr;
     forward_impl<TraitsF64>(p, hidden->data, weight->data, y, mask,
-                            static_cast<double *>(lse_out->data), ws, vec, s, timers);
+                            total ? nullptr : static_cast<double *>(lse_out->data), ws, vec, s,
+                            timers, sh);
   }
   if (!out)  // asynchronous: the scalars stay in the workspace (lce_loss_fetch)
     return hipGetLastError() == hipSuccess ? LCE_OK : LCE_DEVICE_ERROR;
   Control hc;
   st = finish(s, reinterpret_cast<Control *>(ws), &hc);
   if (st != LCE_OK) return st;
-  fill_loss(hc, out);
+  if (!total) fill_loss(hc, out);
   return LCE_OK;
 }
+
+}  // namespace
+
+extern "C" {
 
 int32_t lce_loss_fetch(const lce_tensor *workspace, lce_loss *out, void *stream) {
   if (!out || !has(workspace) || workspace->numel < int64_t(kControlBytes) + 256)
@@ -1155,7 +1357,38 @@ int32_t lce_backward_timed(const lce_tensor *hidden, const lce_tensor *weight,
                            int64_t chunk, double z_coef, double grad_out, lce_tensor *d_hidden,
                            lce_tensor *d_weight, int32_t accumulate_d_weight,
                            lce_tensor *workspace, void *stream, lce_timers *timers) {
+  return backward_call(hidden, weight, targets, loss_mask, lse, n_tok, d_model, vocab, chunk,
+                       z_coef, grad_out, d_hidden, d_weight, accumulate_d_weight, workspace,
+                       stream, timers, 0, 0);
+}
+
+int32_t lce_shard_backward(const lce_tensor *hidden, const lce_tensor *weight_shard,
+                           const lce_tensor *targets, const lce_tensor *loss_mask,
+                           const lce_tensor *lse, int64_t n_tok, int64_t d_model,
+                           int64_t vocab_shard, int64_t vocab_offset, int64_t vocab_total,
+                           int64_t chunk, double z_coef, double grad_out,
+                           lce_tensor *d_hidden_partial, lce_tensor *d_weight_shard,
+                           int32_t accumulate_d_weight, lce_tensor *workspace, void *stream) {
+  return backward_call(hidden, weight_shard, targets, loss_mask, lse, n_tok, d_model, vocab_shard,
+                       chunk, z_coef, grad_out, d_hidden_partial, d_weight_shard,
+                       accumulate_d_weight, workspace, stream, nullptr, vocab_offset,
+                       vocab_total);
+}
+
+}  // extern "C"
+
+namespace {
+
+int32_t backward_call(const lce_tensor *hidden, const lce_tensor *weight,
+                      const lce_tensor *targets, const lce_tensor *loss_mask,
+                      const lce_tensor *lse, int64_t n_tok, int64_t d_model, int64_t vocab,
+                      int64_t chunk, double z_coef, double grad_out, lce_tensor *d_hidden,
+                      lce_tensor *d_weight, int32_t accumulate_d_weight,
+                      lce_tensor *workspace, void *stream, lce_timers *timers, int64_t offset,
+                      int64_t total) {
   int32_t st = lce_dims_check(n_tok, d_model, vocab);
+  if (st != LCE_OK) return st;
+  st = check_shard(vocab, offset, total);
   if (st != LCE_OK) return st;
   st = lce_chunk_check(chunk, vocab);
   if (st != LCE_OK) return st;
@@ -1165,7 +1398,9 @@ int32_t lce_backward_timed(const lce_tensor *hidden, const lce_tensor *weight,
   if (st != LCE_OK) return st;
   if (!lse || !d_hidden || !d_weight || !workspace) return LCE_LENGTH_MISMATCH;
   const int32_t acc_dt = dt == LCE_BF16 ? LCE_F32 : LCE_F64;
-  if (lse->dtype != acc_dt || d_weight->dtype != acc_dt || d_hidden->dtype != dt)
+  // a shard's d_hidden is its unrounded partial (the shards' sum is the gradient)
+  if (lse->dtype != acc_dt || d_weight->dtype != acc_dt ||
+      d_hidden->dtype != (total ? acc_dt : dt))
     return LCE_DTYPE_MISMATCH;
   if (workspace->dtype != LCE_U8) return LCE_DTYPE_MISMATCH;
   CEPlan p;
@@ -1184,24 +1419,26 @@ int32_t lce_backward_timed(const lce_tensor *hidden, const lce_tensor *weight,
   const int64_t *y = static_cast<const int64_t *>(targets->data);
   (void)hipGetLastError();
   if (dt == LCE_BF16) {
+    Shard<float> sh;
+    sh.offset = offset; sh.total = total;
     // the staged d_weight epilogue writes 16-byte chunks
     const bool vec = d_model % 8 == 0 && aligned16(hidden->data) && aligned16(weight->data) &&
                      aligned16(d_weight->data);
     backward_impl<TraitsBF16>(p, hidden->data, weight->data, y, mask,
                               static_cast<const float *>(lse->data), z_coef, grad_out,
-                              static_cast<uint16_t *>(d_hidden->data),
-                              static_cast<float *>(d_weight->data), accumulate_d_weight != 0, ws,
-                              vec, s, timers);
+                              d_hidden->data, total != 0, static_cast<float *>(d_weight->data),
+                              accumulate_d_weight != 0, ws, vec, s, timers, sh);
   } else {
+    Shard<double> sh;
+    sh.offset = offset; sh.total = total;
     const bool vec = d_model % 2 == 0 && aligned16(hidden->data) && aligned16(weight->data);
     backward_impl<TraitsF64>(p, hidden->data, weight->data, y, mask,
                              static_cast<const double *>(lse->data), z_coef, grad_out,
-                             static_cast<double *>(d_hidden->data),
-                             static_cast<double *>(d_weight->data), accumulate_d_weight != 0, ws,
-                             vec, s, timers);
+                             d_hidden->data, total != 0, static_cast<double *>(d_weight->data),
+                             accumulate_d_weight != 0, ws, vec, s, timers, sh);
   }
   Control hc;
   return finish(s, reinterpret_cast<Control *>(ws), &hc);
 }
 
-}  // extern "C"
+}  // namespace

@@ -185,7 +185,10 @@ int32_t plan_ce(int64_t n, int64_t D, int64_t V, int64_t chunk, int32_t dtype, C
   if (bf) off = align256(off + size_t(D) * size_t(q.d_ld) * q.elem);
   q.off_zyb = off;
   if (bf) off = align256(off + size_t(n) * q.acc);
-  q.total = off > fwd_end ? off : fwd_end;
+  // shard-local target ids (vocabulary-shard calls), past both regions
+  off = off > fwd_end ? off : fwd_end;
+  q.off_yloc = off;
+  q.total = align256(off + size_t(n) * sizeof(int64_t));
   *p = q;
   return LCE_OK;
 }

@@ -55,6 +55,7 @@ struct CEPlan {
   size_t off_dbuf = 0, off_dhacc = 0;
   size_t off_ht = 0;          // bf16: H^T [D][d_ld] (zero past n); 0 bytes for fp64
   size_t off_zyb = 0;         // bf16: target logits for the backward; 0 bytes for fp64
+  size_t off_yloc = 0;        // [n] int64 shard-local target ids (shard calls)
   size_t total = 0;
 };
 

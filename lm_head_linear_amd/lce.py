@@ -150,6 +150,13 @@ def lib():
         L.lce_ce_logits_fwd_bwd.restype = i32
         L.lce_ce_logits_fwd_bwd.argtypes = [PT, PT, PT, i64, i64, dbl, dbl, PT, PT,
                                             ctypes.POINTER(Loss), vp]
+        L.lce_shard_forward.restype = i32
+        L.lce_shard_forward.argtypes = [PT, PT, PT, i64, i64, i64, i64, i64, i64, PT, PT, vp]
+        L.lce_shard_merge.restype = i32
+        L.lce_shard_merge.argtypes = [PT, i32, PT, i64, PT, PT, ctypes.POINTER(Loss), vp]
+        L.lce_shard_backward.restype = i32
+        L.lce_shard_backward.argtypes = [PT, PT, PT, PT, PT, i64, i64, i64, i64, i64, i64, dbl,
+                                         dbl, PT, PT, i32, PT, vp]
         PTM = ctypes.POINTER(Timers)
         L.lce_forward_timed.restype = i32
         L.lce_forward_timed.argtypes = L.lce_forward.argtypes + [PTM]
@@ -295,6 +302,42 @@ def lce_ce_logits_fwd_bwd(logits, targets, loss_mask, n_tok, vocab, z_coef, grad
     else:
         st = lib().lce_ce_logits_fwd_bwd_timed(*call, ctypes.byref(timer.struct))
     return st, out
+
+
+def lce_shard_forward(hidden, weight_shard, targets, n_tok, d_model, vocab_shard, vocab_offset,
+                      vocab_total, chunk, stats, workspace, stream: Optional[int] = None) -> int:
+    """Direct call of the C entry point; returns the status."""
+    ts = [_t(hidden), _t(weight_shard), _t(targets)]
+    st_t, ws = _t(stats), _t(workspace)
+    return lib().lce_shard_forward(*[ctypes.byref(a) for a in ts], n_tok, d_model, vocab_shard,
+                                   vocab_offset, vocab_total, chunk, ctypes.byref(st_t),
+                                   ctypes.byref(ws),
+                                   stream if stream is not None else _stream(hidden.device))
+
+
+def lce_shard_merge(stats, n_shards, loss_mask, n_tok, lse_out, workspace,
+                    stream: Optional[int] = None):
+    """Direct call of the C entry point.  Returns (status, Loss)."""
+    out = Loss()
+    a, m, l, ws = _t(stats), _t(loss_mask), _t(lse_out), _t(workspace)
+    st = lib().lce_shard_merge(ctypes.byref(a), int(n_shards), ctypes.byref(m), n_tok,
+                               ctypes.byref(l), ctypes.byref(ws), ctypes.byref(out),
+                               stream if stream is not None else _stream(stats.device))
+    return st, out
+
+
+def lce_shard_backward(hidden, weight_shard, targets, loss_mask, lse, n_tok, d_model, vocab_shard,
+                       vocab_offset, vocab_total, chunk, z_coef, grad_out, d_hidden_partial,
+                       d_weight_shard, accumulate_d_weight, workspace,
+                       stream: Optional[int] = None) -> int:
+    """Direct call of the C entry point; returns the status."""
+    ts = [_t(hidden), _t(weight_shard), _t(targets), _t(loss_mask), _t(lse)]
+    dh, dw, ws = _t(d_hidden_partial), _t(d_weight_shard), _t(workspace)
+    return lib().lce_shard_backward(*[ctypes.byref(a) for a in ts], n_tok, d_model, vocab_shard,
+                                    vocab_offset, vocab_total, chunk, float(z_coef),
+                                    float(grad_out), ctypes.byref(dh), ctypes.byref(dw),
+                                    int(accumulate_d_weight), ctypes.byref(ws),
+                                    stream if stream is not None else _stream(hidden.device))
 
 
 # ------------------------------------------------- allocating conveniences
