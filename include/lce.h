@@ -28,9 +28,11 @@
  *   lengths and workspace size -> objective id -> device-side target guard
  *   -> compute.  The target guard runs on the device; when it fails, every
  *   compute kernel exits before writing and 586 is returned.
- * Precision: bf16 inputs are multiplied on the matrix cores with fp32
- *   accumulation; every softmax statistic is fp32 and every token sum fp64.
- *   fp64 inputs run end to end in fp64.
+ * Precision: bf16 and fp16 inputs are multiplied on the matrix cores with
+ *   fp32 accumulation; every softmax statistic is fp32 and every token sum
+ *   fp64.  fp64 inputs run end to end in fp64.  16-bit gradients (d_hidden,
+ *   logit gradients) are rounded to the input type; with fp16, grad_out is
+ *   where a loss scale goes (fp16's exponent range is narrow).
  */
 #ifndef LCE_H
 #define LCE_H
@@ -68,6 +70,7 @@ extern "C" {
 #define LCE_F32 2
 #define LCE_F64 3
 #define LCE_I64 4
+#define LCE_F16 5
 #define LCE_U8 6
 
 /* A flat buffer: data points to numel contiguous elements of dtype.
@@ -129,7 +132,7 @@ int32_t lce_work_fits(int64_t n, int64_t d, int64_t v, int64_t ceiling);
 int32_t lce_peak_cells(int64_t n_tok, int64_t vocab, int64_t chunk, lce_peak *out);
 
 /* Bytes of device workspace lce_forward and lce_backward need for this
- * shape and compute dtype (LCE_BF16 or LCE_F64).  Negative = -status when
+ * shape and compute dtype (LCE_BF16, LCE_F16 or LCE_F64).  Negative = -status when
  * the shape, chunk or dtype is refused.  The logit-derived part of the
  * workspace never exceeds chunk*vocab cells. */
 int64_t lce_workspace_bytes(int64_t n_tok, int64_t d_model, int64_t vocab, int64_t chunk,
@@ -143,14 +146,14 @@ int64_t lce_distill_workspace_bytes(int64_t n_tok, int64_t vocab);
 /* Fused projection + chunked cross-entropy, forward (lossk table,
  * fused_linear_ce_flat; "lossk: the loss is where the memory goes"), with
  * z-loss and a loss mask (Fast-LLM 566, "What it does").
- *   hidden    [n_tok*d_model] LCE_BF16 or LCE_F64, row-major [n_tok][d_model]
+ *   hidden    [n_tok*d_model] LCE_BF16, LCE_F16 or LCE_F64, row-major [n_tok][d_model]
  *   weight    [vocab*d_model] same dtype, row-major [vocab][d_model]
  *   targets   [n_tok] LCE_I64, each must satisfy 0 <= y < vocab (586)
  *   loss_mask [n_tok] LCE_U8 (1 = counted) or data == NULL (all counted)
  *   chunk     tokens whose logits may exist at once: the call holds at most
  *             chunk*vocab logit-derived cells (587 above 2^27)
  *   z_coef    z-loss coefficient; only validated here (z_sum is unscaled)
- *   lse_out   [n_tok] per-token log-sum-exp, LCE_F32 for bf16 inputs,
+ *   lse_out   [n_tok] per-token log-sum-exp, LCE_F32 for 16-bit inputs,
  *             LCE_F64 for fp64 inputs; lce_backward takes it back
  *   workspace LCE_U8, numel >= lce_workspace_bytes(...)
  *   out       host pointer; receives the scalars after the call synchronizes
@@ -179,7 +182,7 @@ int32_t lce_loss_fetch(const lce_tensor *workspace, lce_loss *out, void *stream)
  *   d_hidden = d W,  d_weight (+)= d^T H.
  *   lse        [n_tok] from lce_forward on the same inputs (F32 / F64)
  *   d_hidden   [n_tok*d_model] in hidden's dtype (overwritten)
- *   d_weight   [vocab*d_model] LCE_F32 for bf16 inputs, LCE_F64 for fp64;
+ *   d_weight   [vocab*d_model] LCE_F32 for 16-bit inputs, LCE_F64 for fp64;
  *              overwritten, or added to when accumulate_d_weight != 0
  * Logits are recomputed from H and W; the logit-gradient buffer holds at
  * most chunk*vocab cells at once. */
@@ -193,7 +196,7 @@ int32_t lce_backward(const lce_tensor *hidden, const lce_tensor *weight,
 /* Distillation against a teacher distribution, fused forward + backward,
  * with z-loss over the same student softmax (Fast-LLM 566, "What it does"
  * and "Changes": returns loss, z-loss and the logit gradient).
- *   student, teacher [n_tok*vocab] logits, LCE_BF16, LCE_F32 or LCE_F64
+ *   student, teacher [n_tok*vocab] logits, LCE_BF16, LCE_F16, LCE_F32 or LCE_F64
  *                    (same dtype), row-major [n_tok][vocab]
  *   loss_mask        [n_tok] LCE_U8 or data == NULL
  *   objective        0 soft-target cross-entropy -sum q log p,
@@ -227,7 +230,7 @@ int32_t lce_distill_fwd_bwd(const lce_tensor *student, const lce_tensor *teacher
  *   workspace    numel >= lce_workspace_bytes(n_tok, d_model, vocab_shard,
  *                chunk, dtype)
  * lce_shard_forward writes stats[3*n_tok] in the accumulator dtype (LCE_F32
- * for bf16 inputs, LCE_F64 for fp64): stats[t] = m_t, the shard's largest
+ * for 16-bit inputs, LCE_F64 for fp64): stats[t] = m_t, the shard's largest
  * logit of token t; stats[n_tok + t] = s_t = sum over the shard's rows of
  * exp(z - m_t); stats[2*n_tok + t] = z[t][y_t] when the shard holds row y_t,
  * else 0.  It synchronizes the stream (target guard). */
@@ -268,7 +271,7 @@ int32_t lce_shard_backward(const lce_tensor *hidden, const lce_tensor *weight_sh
  * backward: the lossk page's ce_from_logits reference function ("Loss
  * functions and resident-context kernels", lossk table) on the device, with
  * the loss mask and z term of Fast-LLM 566 ("What it does", "Changes").
- *   logits       [n_tok*vocab] LCE_BF16, LCE_F32 or LCE_F64, row-major
+ *   logits       [n_tok*vocab] LCE_BF16, LCE_F16, LCE_F32 or LCE_F64, row-major
  *                [n_tok][vocab]
  *   targets      [n_tok] LCE_I64, each 0 <= y < vocab (else 586, with
  *                grad_logits untouched)
@@ -299,7 +302,7 @@ int32_t lce_ce_logits_fwd_bwd(const lce_tensor *logits, const lce_tensor *target
 #define LCE_K_DH_GEMM 6      /* split-K d_hidden accumulation                   */
 #define LCE_K_DH_FINAL 7     /* fold of the d_hidden splits                     */
 #define LCE_K_DISTILL 8      /* distillation row kernel                         */
-#define LCE_K_BWD_GEMM 9     /* one launch of the slab-pipelined bf16 backward: */
+#define LCE_K_BWD_GEMM 9     /* one launch of the slab-pipelined 16-bit backward:*/
                              /* d_hidden and d_weight of slab k with the logit  */
                              /* gradient of slab k+1                            */
 #define LCE_K_LABEL_CE 10    /* label cross-entropy row kernel (logits in)      */

@@ -128,11 +128,13 @@ template <class TR, class T> __device__ inline T col_sum(T x) {
 }
 
 template <class TR> __device__ inline typename TR::E to_elem(typename TR::Acc x) {
-  if constexpr (std::is_same<typename TR::Acc, float>::value) return f32_to_bf16_rne(x);
+  if constexpr (std::is_same<typename TR::Acc, float>::value)
+    return TR::F16 ? f32_to_f16_rne(x) : f32_to_bf16_rne(x);
   else return x;
 }
 template <class TR> __device__ inline typename TR::Acc to_acc(typename TR::E x) {
-  if constexpr (std::is_same<typename TR::Acc, float>::value) return bf16_to_f32(x);
+  if constexpr (std::is_same<typename TR::Acc, float>::value)
+    return TR::F16 ? f16_to_f32(x) : bf16_to_f32(x);
   else return x;
 }
 
@@ -222,7 +224,7 @@ __global__ void target_logit_kernel(const typename TR::E *H, const typename TR::
   const typename TR::E *w = W + y[t] * D;
   Acc s = 0;
   if constexpr (std::is_same<typename TR::E, uint16_t>::value) {
-    // 16-byte chunks of 8 bf16 (rows 16-byte aligned and D % 8 == 0: the
+    // 16-byte chunks of 8 elements (rows 16-byte aligned and D % 8 == 0: the
     // host passes vec8 only then), lane-strided, then the scalar remainder
     if (vec8) {
       for (int64_t c = lane; c < D / 8; c += 64) {
@@ -230,8 +232,8 @@ __global__ void target_logit_kernel(const typename TR::E *H, const typename TR::
         const u32x4 b = *reinterpret_cast<const u32x4 *>(w + 8 * c);
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-          s = fmaf(__uint_as_float(a[j] << 16), __uint_as_float(b[j] << 16), s);
-          s = fmaf(__uint_as_float(a[j] & 0xffff0000u), __uint_as_float(b[j] & 0xffff0000u), s);
+          s = fmaf(to_acc<TR>(uint16_t(a[j])), to_acc<TR>(uint16_t(b[j])), s);
+          s = fmaf(to_acc<TR>(uint16_t(a[j] >> 16)), to_acc<TR>(uint16_t(b[j] >> 16)), s);
         }
       }
     } else {
@@ -756,7 +758,7 @@ static void launch_gemm(bool vec, const GemmParams &g, int64_t splits, const Epi
 typedef PipeCfg<64, 2> PipeKK;
 typedef PipeCfg<64, 2> PipeMN;
 
-// The pipelined core runs 8 waves per tile (TraitsBF16W8); its epilogues are
+// The pipelined core runs 8 waves per tile (TraitsH16W8); its epilogues are
 // the same structs instantiated on those traits (same members, so the fields
 // carry over bit for bit).
 template <class TR2, class TR> FwdLseEpi<TR2> retrait(const FwdLseEpi<TR> &e) {
@@ -778,38 +780,38 @@ template <class CFG> static Gemm2Params to_gemm2(const GemmParams &g0) {
   return g;
 }
 
-template <class CFG, bool AK, bool BKM, class Epi>
+template <class CFG, class TR, bool AK, bool BKM, class Epi>
 static void launch_gemm2(const GemmParams &g0, int64_t splits, const Epi &epi, hipStream_t st) {
   const Gemm2Params g = to_gemm2<CFG>(g0);
   const int64_t tiles = cdiv(g.M, CFG::BM) * g.tiles_n;
   const dim3 grid{unsigned(tiles * splits), 1u, 1u};
-  typedef TraitsBF16W8 TRP;
+  typedef typename W8Of<TR>::type TRP;
   const auto e = retrait<TRP>(epi);
   hipLaunchKernelGGL((gemm2_kernel<CFG, TRP, AK, BKM, decltype(e)>), grid, dim3(TRP::NT), 0, st, g,
                      e);
 }
 
-// The pipelined bf16 core applies when every operand is 16-byte aligned with
+// The pipelined 16-bit core applies when every operand is 16-byte aligned with
 // leading dimensions that are multiples of 8, d_model is a multiple of the
 // K-major configuration's k-step (K-major operands are read in whole steps)
 // and 256 rows of any operand span less than 2 GiB (buffer offsets are 32-bit).
 template <class TR> struct UsePipe { static bool ok(bool, int64_t, int64_t) { return false; } };
-template <> struct UsePipe<TraitsBF16> {
+template <bool F> struct UsePipe<TraitsH16<F>> {
   static bool ok(bool vec, int64_t D, int64_t d_ld) {
     return vec && D % PipeKK::BK == 0 && 256 * D * 2 < (int64_t(1) << 31) &&
            256 * d_ld * 2 < (int64_t(1) << 31);
   }
 };
 
-// bf16 with `pipe`: the pipelined core (both operands K-major: PipeKK, else
-// PipeMN); otherwise the generic one.
+// 16-bit inputs with `pipe`: the pipelined core (both operands K-major:
+// PipeKK, else PipeMN); otherwise the generic one.
 template <class TR, bool AK, bool BKM, class Epi>
 static void launch_any(bool pipe, bool vec, const GemmParams &g, int64_t splits, const Epi &epi,
                        hipStream_t st) {
-  if constexpr (std::is_same<TR, TraitsBF16>::value) {
+  if constexpr (IsH16<TR>::value) {
     if (pipe) {
-      if constexpr (AK && BKM) launch_gemm2<PipeKK, AK, BKM>(g, splits, epi, st);
-      else launch_gemm2<PipeMN, AK, BKM>(g, splits, epi, st);
+      if constexpr (AK && BKM) launch_gemm2<PipeKK, TR, AK, BKM>(g, splits, epi, st);
+      else launch_gemm2<PipeMN, TR, AK, BKM>(g, splits, epi, st);
       return;
     }
   }
@@ -886,9 +888,9 @@ static void forward_impl(const CEPlan &p, const void *H, const void *W, const in
     {
       TimedLaunch tl(tm, LCE_K_FWD_GEMM, st);
       bool done = false;
-      if constexpr (std::is_same<TR, TraitsBF16>::value) {
+      if constexpr (IsH16<TR>::value) {
         if (UsePipe<TR>::ok(vec, p.D, p.d_ld)) {  // persistent: one workgroup per CU
-          typedef TraitsBF16W8 TRP;
+          typedef typename W8Of<TR>::type TRP;
           const int64_t tiles = cdiv(g.M, PipeKK::BM) * g.tiles_n;
           const int64_t grid = tiles < kComputeUnits ? tiles : kComputeUnits;
           const auto e = retrait<TRP>(epi);
@@ -911,17 +913,17 @@ static void forward_impl(const CEPlan &p, const void *H, const void *W, const in
                      (const Acc *)lse_out, mask, p.n, ctl);
 }
 
-// bf16 backward as a slab pipeline: launch k runs d_hidden and d_weight of
+// 16-bit backward as a slab pipeline: launch k runs d_hidden and d_weight of
 // slab k-1 (from slab buffer (k-1) % 2) together with the logit gradient of
 // slab k (into buffer k % 2), longest products first.  The d_hidden split
 // accumulators start at zero and every launch adds to them.
-template <bool ACC_DW>
+template <class TR, bool ACC_DW>
 static void backward_pipelined(const CEPlan &p, const uint16_t *Hp, const uint16_t *Wp,
                                const int64_t *y, const uint8_t *mask, const float *lse,
                                double z_coef, double grad_out, float *dW, uint16_t *dbuf,
                                float *dhacc, const uint16_t *Ht, const float *zyb, Control *ctl,
                                hipStream_t st, lce_timers *tm) {
-  typedef TraitsBF16W8 TRP;
+  typedef typename W8Of<TR>::type TRP;
   typedef Gemm2Job<PipeMN, false, false, StoreEpi<TRP, true>> JH;
   typedef Gemm2Job<PipeKK, true, true, StoreEpi<TRP, ACC_DW>> JW;
   typedef Gemm2Job<PipeKK, true, true, DlogitEpi<TRP>> JL;
@@ -1023,7 +1025,7 @@ static void backward_impl(const CEPlan &p, const void *H, const void *W, const i
   const bool pipe = UsePipe<TR>::ok(vec, p.D, p.d_ld);
   E *Ht = nullptr;
   Acc *zyb = nullptr;
-  if constexpr (std::is_same<TR, TraitsBF16>::value) {
+  if constexpr (IsH16<TR>::value) {
     if (pipe) {
       // K-major operands of the d_weight product: H^T and the slab buffer,
       // both zero in token columns [n, d_ld).
@@ -1037,11 +1039,11 @@ static void backward_impl(const CEPlan &p, const void *H, const void *W, const i
                          Hp, Wp, y, p.n, p.D, zyb, (const int32_t *)&ctl->bad, vec ? 1 : 0);
       if (p.pslab > 0) {
         if (accumulate)
-          backward_pipelined<true>(p, Hp, Wp, y, mask, lse, z_coef, grad_out, dW, dbuf, dhacc,
-                                   Ht, zyb, ctl, st, tm);
+          backward_pipelined<TR, true>(p, Hp, Wp, y, mask, lse, z_coef, grad_out, dW, dbuf,
+                                       dhacc, Ht, zyb, ctl, st, tm);
         else
-          backward_pipelined<false>(p, Hp, Wp, y, mask, lse, z_coef, grad_out, dW, dbuf, dhacc,
-                                    Ht, zyb, ctl, st, tm);
+          backward_pipelined<TR, false>(p, Hp, Wp, y, mask, lse, z_coef, grad_out, dW, dbuf,
+                                        dhacc, Ht, zyb, ctl, st, tm);
         launch_dh_final<TR>(dhacc, p.pdh_splits, p.n * p.D, dH, dh_acc,
                             (const int32_t *)&ctl->bad, st, tm);
         return;
@@ -1123,7 +1125,7 @@ int32_t check_ce_tensors(const lce_tensor *hidden, const lce_tensor *weight,
                          int64_t D, int64_t V, int32_t *dtype) {
   if (!hidden || !weight || !targets) return LCE_LENGTH_MISMATCH;
   const int32_t dt = hidden->dtype;
-  if (dt != LCE_BF16 && dt != LCE_F64) return LCE_DTYPE_MISMATCH;
+  if (dt != LCE_BF16 && dt != LCE_F16 && dt != LCE_F64) return LCE_DTYPE_MISMATCH;
   if (weight->dtype != dt || targets->dtype != LCE_I64) return LCE_DTYPE_MISMATCH;
   if (has(loss_mask) && loss_mask->dtype != LCE_U8) return LCE_DTYPE_MISMATCH;
   *dtype = dt;
@@ -1283,7 +1285,7 @@ int32_t forward_call(const lce_tensor *hidden, const lce_tensor *weight,
   if (st != LCE_OK) return st;
   lce_tensor *res = total ? stats : lse_out;   // [3 n] records or [n] lse
   if (!res || !workspace) return LCE_LENGTH_MISMATCH;
-  if (res->dtype != (dt == LCE_BF16 ? LCE_F32 : LCE_F64)) return LCE_DTYPE_MISMATCH;
+  if (res->dtype != (dt == LCE_F64 ? LCE_F64 : LCE_F32)) return LCE_DTYPE_MISMATCH;
   if (workspace->dtype != LCE_U8) return LCE_DTYPE_MISMATCH;
   CEPlan p;
   st = plan_ce(n_tok, d_model, vocab, chunk, dt, &p);
@@ -1298,14 +1300,16 @@ int32_t forward_call(const lce_tensor *hidden, const lce_tensor *weight,
   const uint8_t *mask = has(loss_mask) ? static_cast<const uint8_t *>(loss_mask->data) : nullptr;
   const int64_t *y = static_cast<const int64_t *>(targets->data);
   (void)hipGetLastError();
-  if (dt == LCE_BF16) {
+  if (dt != LCE_F64) {
     const bool vec = d_model % 8 == 0 && aligned16(hidden->data) && aligned16(weight->data);
     Shard<float> sh;
     sh.offset = offset; sh.total = total;
     sh.stats = total ? static_cast<float *>(stats->data) : nullptr;
-    forward_impl<TraitsBF16>(p, hidden->data, weight->data, y, mask,
-                             total ? nullptr : static_cast<float *>(lse_out->data), ws, vec, s,
-                             timers, sh);
+    float *lo = total ? nullptr : static_cast<float *>(lse_out->data);
+    if (dt == LCE_F16)
+      forward_impl<TraitsF16>(p, hidden->data, weight->data, y, mask, lo, ws, vec, s, timers, sh);
+    else
+      forward_impl<TraitsBF16>(p, hidden->data, weight->data, y, mask, lo, ws, vec, s, timers, sh);
   } else {
     const bool vec = d_model % 2 == 0 && aligned16(hidden->data) && aligned16(weight->data);
     Shard<double> sh;
@@ -1397,7 +1401,7 @@ int32_t backward_call(const lce_tensor *hidden, const lce_tensor *weight,
   st = check_ce_tensors(hidden, weight, targets, loss_mask, n_tok, d_model, vocab, &dt);
   if (st != LCE_OK) return st;
   if (!lse || !d_hidden || !d_weight || !workspace) return LCE_LENGTH_MISMATCH;
-  const int32_t acc_dt = dt == LCE_BF16 ? LCE_F32 : LCE_F64;
+  const int32_t acc_dt = dt == LCE_F64 ? LCE_F64 : LCE_F32;
   // a shard's d_hidden is its unrounded partial (the shards' sum is the gradient)
   if (lse->dtype != acc_dt || d_weight->dtype != acc_dt ||
       d_hidden->dtype != (total ? acc_dt : dt))
@@ -1418,16 +1422,22 @@ int32_t backward_call(const lce_tensor *hidden, const lce_tensor *weight,
   const uint8_t *mask = has(loss_mask) ? static_cast<const uint8_t *>(loss_mask->data) : nullptr;
   const int64_t *y = static_cast<const int64_t *>(targets->data);
   (void)hipGetLastError();
-  if (dt == LCE_BF16) {
+  if (dt != LCE_F64) {
     Shard<float> sh;
     sh.offset = offset; sh.total = total;
     // the staged d_weight epilogue writes 16-byte chunks
     const bool vec = d_model % 8 == 0 && aligned16(hidden->data) && aligned16(weight->data) &&
                      aligned16(d_weight->data);
-    backward_impl<TraitsBF16>(p, hidden->data, weight->data, y, mask,
-                              static_cast<const float *>(lse->data), z_coef, grad_out,
-                              d_hidden->data, total != 0, static_cast<float *>(d_weight->data),
-                              accumulate_d_weight != 0, ws, vec, s, timers, sh);
+    const float *l = static_cast<const float *>(lse->data);
+    float *dw = static_cast<float *>(d_weight->data);
+    if (dt == LCE_F16)
+      backward_impl<TraitsF16>(p, hidden->data, weight->data, y, mask, l, z_coef, grad_out,
+                               d_hidden->data, total != 0, dw, accumulate_d_weight != 0, ws, vec,
+                               s, timers, sh);
+    else
+      backward_impl<TraitsBF16>(p, hidden->data, weight->data, y, mask, l, z_coef, grad_out,
+                                d_hidden->data, total != 0, dw, accumulate_d_weight != 0, ws,
+                                vec, s, timers, sh);
   } else {
     Shard<double> sh;
     sh.offset = offset; sh.total = total;

@@ -16,6 +16,7 @@ bool finite_scalar(double x) { return std::isfinite(x); }
 size_t dtype_size(int32_t dtype) {
   switch (dtype) {
     case LCE_BF16: return 2;
+    case LCE_F16: return 2;
     case LCE_F32: return 4;
     case LCE_F64: return 8;
     case LCE_I64: return 8;
@@ -33,12 +34,12 @@ int32_t plan_ce(int64_t n, int64_t D, int64_t V, int64_t chunk, int32_t dtype, C
   if (st != LCE_OK) return st;
   st = lce_chunk_check(chunk, V);
   if (st != LCE_OK) return st;
-  if (dtype != LCE_BF16 && dtype != LCE_F64) return LCE_DTYPE_MISMATCH;
+  if (dtype != LCE_BF16 && dtype != LCE_F16 && dtype != LCE_F64) return LCE_DTYPE_MISMATCH;
 
   CEPlan q;
   q.dtype = dtype;
   q.n = n; q.D = D; q.V = V; q.chunk = chunk;
-  const bool bf = dtype == LCE_BF16;
+  const bool bf = dtype != LCE_F64;   // 16-bit inputs (bf16 or fp16)
   q.elem = bf ? 2 : 8;
   q.acc = bf ? 4 : 8;
   const int64_t tile_m = bf ? kBf16TileM : kF64TileM;

@@ -70,6 +70,23 @@ template <> struct IO<uint16_t> {  // bf16 bits
   }
   __device__ static inline void store1(uint16_t *p, float g) { *p = cvt(g); }
 };
+template <> struct IO<_Float16> {  // IEEE half; v_cvt_f16_f32 rounds to nearest even
+  typedef float C;
+  typedef _Float16 h8 __attribute__((ext_vector_type(8)));
+  __device__ static inline void load8(const _Float16 *p, float *o) {
+    const h8 v = *reinterpret_cast<const h8 *>(p);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) o[i] = static_cast<float>(v[i]);
+  }
+  __device__ static inline float load1(const _Float16 *p) { return static_cast<float>(*p); }
+  __device__ static inline void store8(_Float16 *p, const float *g) {
+    h8 v;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) v[i] = static_cast<_Float16>(g[i]);
+    __builtin_nontemporal_store(__builtin_bit_cast(u32x4, v), reinterpret_cast<u32x4 *>(p));
+  }
+  __device__ static inline void store1(_Float16 *p, float g) { *p = static_cast<_Float16>(g); }
+};
 template <> struct IO<float> {
   typedef float C;
   __device__ static inline void load8(const float *p, float *o) {
@@ -499,7 +516,8 @@ extern "C" int32_t lce_distill_fwd_bwd_timed(const lce_tensor *student, const lc
     return LCE_NON_FINITE_SCALAR;
   if (!student || !teacher || !grad_logits || !workspace) return LCE_LENGTH_MISMATCH;
   const int32_t dt = student->dtype;
-  if (dt != LCE_BF16 && dt != LCE_F32 && dt != LCE_F64) return LCE_DTYPE_MISMATCH;
+  if (dt != LCE_BF16 && dt != LCE_F16 && dt != LCE_F32 && dt != LCE_F64)
+    return LCE_DTYPE_MISMATCH;
   if (teacher->dtype != dt || grad_logits->dtype != dt) return LCE_DTYPE_MISMATCH;
   if (has(loss_mask) && loss_mask->dtype != LCE_U8) return LCE_DTYPE_MISMATCH;
   if (workspace->dtype != LCE_U8) return LCE_DTYPE_MISMATCH;
@@ -522,7 +540,12 @@ extern "C" int32_t lce_distill_fwd_bwd_timed(const lce_tensor *student, const lc
   const bool vec = (vocab % 8 == 0) && aligned(student->data, 16) && aligned(teacher->data, 16) &&
                    aligned(grad_logits->data, 16) && (esz * 8) % 16 == 0;
   (void)hipGetLastError();
-  if (dt == LCE_BF16)
+  if (dt == LCE_F16)
+    distill_impl<_Float16>(objective, vec, static_cast<const _Float16 *>(student->data),
+                           static_cast<const _Float16 *>(teacher->data), mask, n_tok, vocab,
+                           temperature, z_coef, grad_out, ctl,
+                           static_cast<_Float16 *>(grad_logits->data), rows, s, timers);
+  else if (dt == LCE_BF16)
     distill_impl<uint16_t>(objective, vec, static_cast<const uint16_t *>(student->data),
                            static_cast<const uint16_t *>(teacher->data), mask, n_tok, vocab,
                            temperature, z_coef, grad_out, ctl,
@@ -572,7 +595,8 @@ extern "C" int32_t lce_ce_logits_fwd_bwd_timed(const lce_tensor *logits,
   if (!logits || !targets || !workspace) return LCE_LENGTH_MISMATCH;
   const int32_t dt = logits->dtype;
   const bool want_grad = has(grad_logits);
-  if (dt != LCE_BF16 && dt != LCE_F32 && dt != LCE_F64) return LCE_DTYPE_MISMATCH;
+  if (dt != LCE_BF16 && dt != LCE_F16 && dt != LCE_F32 && dt != LCE_F64)
+    return LCE_DTYPE_MISMATCH;
   if (targets->dtype != LCE_I64) return LCE_DTYPE_MISMATCH;
   if (want_grad && grad_logits->dtype != dt) return LCE_DTYPE_MISMATCH;
   if (has(loss_mask) && loss_mask->dtype != LCE_U8) return LCE_DTYPE_MISMATCH;
@@ -596,7 +620,12 @@ extern "C" int32_t lce_ce_logits_fwd_bwd_timed(const lce_tensor *logits,
   const bool vec = (vocab % 8 == 0) && aligned(logits->data, 16) &&
                    (!want_grad || aligned(grad_logits->data, 16)) && (esz * 8) % 16 == 0;
   (void)hipGetLastError();
-  if (dt == LCE_BF16)
+  if (dt == LCE_F16)
+    label_impl<_Float16>(vec, want_grad, static_cast<const _Float16 *>(logits->data), y, mask,
+                         n_tok, vocab, z_coef, grad_out, ctl,
+                         want_grad ? static_cast<_Float16 *>(grad_logits->data) : nullptr, rows,
+                         s, timers);
+  else if (dt == LCE_BF16)
     label_impl<uint16_t>(vec, want_grad, static_cast<const uint16_t *>(logits->data), y, mask,
                          n_tok, vocab, z_coef, grad_out, ctl,
                          want_grad ? static_cast<uint16_t *>(grad_logits->data) : nullptr, rows,

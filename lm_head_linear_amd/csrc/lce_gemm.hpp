@@ -11,8 +11,9 @@
 // 16-byte MFMA operand reads and both kinds of tile stores free of bank
 // conflicts.
 //
-// bf16: v_mfma_f32_32x32x16_bf16, tile 256x256x64, 4 waves (2 x 2), wave tile
-//       128x128, fp32 accumulators (256 per lane, held in AGPRs).
+// bf16 / fp16: v_mfma_f32_32x32x16_bf16 / _f16, tile 256x256x64, 4 waves
+//       (2 x 2), wave tile 128x128, fp32 accumulators (256 per lane, held in
+//       AGPRs).
 // fp64: v_mfma_f64_16x16x4_f64, tile 128x128x16, 4 waves (2 x 2), wave tile
 //       64x64, fp64 accumulators.
 #pragma once
@@ -24,6 +25,7 @@ namespace lce {
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef double f64x4 __attribute__((ext_vector_type(4)));
 
@@ -31,8 +33,12 @@ struct Control;
 
 // ---------------------------------------------------------------- traits --
 
-struct TraitsBF16 {
-  typedef uint16_t E;        // bf16 bits
+// 16-bit float inputs held as their bits (F16: IEEE half, else bf16) with
+// fp32 accumulation.
+template <bool F16_>
+struct TraitsH16 {
+  static constexpr bool F16 = F16_;
+  typedef uint16_t E;        // bf16 or fp16 bits
   typedef float Acc;
   typedef f32x16 AccBlock;
   static constexpr int BM = 256, BN = 256, BK = 64;
@@ -49,8 +55,25 @@ struct TraitsBF16 {
   }
   __device__ static inline int col_of(int lane) { return lane & 31; }
 };
+typedef TraitsH16<false> TraitsBF16;
+typedef TraitsH16<true> TraitsF16;
+
+template <class TR> struct IsH16 { static constexpr bool value = false; };
+template <bool F> struct IsH16<TraitsH16<F>> { static constexpr bool value = true; };
+
+// The 32x32x16 MFMA of the 16-bit input type.
+template <class TR>
+__device__ inline f32x16 mfma32(u32x4 a, u32x4 b, f32x16 c) {
+  if constexpr (TR::F16)
+    return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a),
+                                                  __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
+  else
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
+                                                   __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+}
 
 struct TraitsF64 {
+  static constexpr bool F16 = false;
   typedef double E;
   typedef double Acc;
   typedef f64x4 AccBlock;
@@ -87,9 +110,16 @@ __device__ inline uint16_t f32_to_bf16_rne(float f) {
   return __builtin_bit_cast(uint16_t, static_cast<__bf16>(f));
 }
 __device__ inline float bf16_to_f32(uint16_t h) { return __uint_as_float(uint32_t(h) << 16); }
+// fp16: v_cvt_f16_f32 rounds to nearest even.
+__device__ inline uint16_t f32_to_f16_rne(float f) {
+  return __builtin_bit_cast(uint16_t, static_cast<_Float16>(f));
+}
+__device__ inline float f16_to_f32(uint16_t h) {
+  return static_cast<float>(__builtin_bit_cast(_Float16, h));
+}
 
 template <class TR> struct Elem;
-template <> struct Elem<TraitsBF16> {
+template <bool F> struct Elem<TraitsH16<F>> {
   __device__ static inline u32x4 pack(const uint16_t *v) {
     u32x4 r;
     r[0] = uint32_t(v[0]) | (uint32_t(v[1]) << 16);
@@ -255,10 +285,9 @@ struct MNMajorTile {
 template <class TR>
 __device__ inline void transpose_block(const u32x4 *in, u32x4 *out);
 
-// bf16: 8x8 transpose of 16-bit elements.  in[r] holds k = r with tile rows
-// 0..7 in dword pairs; out[j] gets tile row j with k = 0..7.
-template <>
-__device__ inline void transpose_block<TraitsBF16>(const u32x4 *in, u32x4 *out) {
+// 16-bit: 8x8 transpose.  in[r] holds k = r with tile rows 0..7 in dword
+// pairs; out[j] gets tile row j with k = 0..7.
+__device__ inline void transpose_block16(const u32x4 *in, u32x4 *out) {
 #pragma unroll
   for (int j = 0; j < 8; ++j) {
     const int w = j >> 1;
@@ -268,6 +297,14 @@ __device__ inline void transpose_block<TraitsBF16>(const u32x4 *in, u32x4 *out) 
       out[j][pw] = (j & 1) ? ((a >> 16) | (b & 0xffff0000u)) : ((a & 0xffffu) | (b << 16));
     }
   }
+}
+template <>
+__device__ inline void transpose_block<TraitsBF16>(const u32x4 *in, u32x4 *out) {
+  transpose_block16(in, out);
+}
+template <>
+__device__ inline void transpose_block<TraitsF16>(const u32x4 *in, u32x4 *out) {
+  transpose_block16(in, out);
 }
 
 template <>
@@ -305,11 +342,11 @@ struct TileLoader<TR, ROWS, false, VEC> : MNMajorTile<TR, ROWS, VEC> {};
 
 template <class TR> struct Mma;
 
-template <> struct Mma<TraitsBF16> {
-  typedef TraitsBF16 TR;
+template <bool F> struct Mma<TraitsH16<F>> {
+  typedef TraitsH16<F> TR;
   // One BK = 64 slab from LDS: 4 MFMA k-steps of 16.
   __device__ static inline void step(const u32x4 *As, const u32x4 *Bs, int wm, int wn, int lane,
-                                     TR::AccBlock (&acc)[TR::FM][TR::FN]) {
+                                     typename TR::AccBlock (&acc)[TR::FM][TR::FN]) {
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk) {
       u32x4 a[TR::FM], b[TR::FN];
@@ -328,9 +365,7 @@ template <> struct Mma<TraitsBF16> {
       for (int fm = 0; fm < TR::FM; ++fm)
 #pragma unroll
         for (int fn = 0; fn < TR::FN; ++fn)
-          acc[fm][fn] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-              __builtin_bit_cast(bf16x8, a[fm]), __builtin_bit_cast(bf16x8, b[fn]), acc[fm][fn], 0,
-              0, 0);
+          acc[fm][fn] = mfma32<TR>(a[fm], b[fn], acc[fm][fn]);
       // Bound how far the scheduler hoists operand reads of later k-steps:
       // one step of operands in flight keeps the arch VGPRs for staging.
       __builtin_amdgcn_sched_barrier(0);

@@ -1,4 +1,4 @@
-// lce_gemm2.hpp -- pipelined bf16 GEMM core for gfx950 (CDNA4).
+// lce_gemm2.hpp -- pipelined 16-bit (bf16 / fp16) GEMM core for gfx950 (CDNA4).
 //
 // Same contract as gemm_kernel in lce_gemm.hpp (C = A(m,k) B(n,k) per
 // 256x256 tile, accumulators handed to an epilogue in the 32x32x16 MFMA
@@ -50,13 +50,20 @@ struct PipeCfg {
 
 // 256x256 tile on 8 waves (two per SIMD), each 128 x 64: while one wave of a
 // SIMD waits on LDS or the stage barrier the other keeps the matrix core busy.
-struct TraitsBF16W8 : TraitsBF16 {
+template <bool F16_>
+struct TraitsH16W8 : TraitsH16<F16_> {
+  typedef TraitsH16<F16_> Base;
   static constexpr int WAVES_M = 2, WAVES_N = 4;
   static constexpr int NT = WAVES_M * WAVES_N * 64;
-  static constexpr int WTM = BM / WAVES_M, WTN = BN / WAVES_N;
-  static constexpr int FM = WTM / MF, FN = WTN / MF;
+  static constexpr int WTM = Base::BM / WAVES_M, WTN = Base::BN / WAVES_N;
+  static constexpr int FM = WTM / Base::MF, FN = WTN / Base::MF;
 };
-typedef PipeCfg<32, 4> Pipe;   // the configuration the library launches
+typedef TraitsH16W8<false> TraitsBF16W8;
+typedef TraitsH16W8<true> TraitsF16W8;
+
+// The 8-wave traits of a 16-bit input type.
+template <class TR> struct W8Of;
+template <bool F> struct W8Of<TraitsH16<F>> { typedef TraitsH16W8<F> type; };
 
 // Chunk swizzles.  K-major rows of 64 bytes (BK 32) or 128 bytes (BK 64): the
 // rows read by 16 consecutive lanes land in 16 distinct 16-byte bank groups of
@@ -329,9 +336,7 @@ __device__ __forceinline__ void gemm2_block(const Gemm2Params &g, const Epi &epi
       for (int fm = 0; fm < TR::FM; ++fm)
 #pragma unroll
         for (int fn = 0; fn < TR::FN; ++fn)
-          acc[fm][fn] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-              __builtin_bit_cast(bf16x8, fa[cur][fm]), __builtin_bit_cast(bf16x8, fb[cur][fn]),
-              acc[fm][fn], 0, 0, 0);
+          acc[fm][fn] = mfma32<TR>(fa[cur][fm], fb[cur][fn], acc[fm][fn]);
       // Interleave: one MFMA, then (while any remain) one refill load and one
       // LDS read.
       constexpr int NDS_I = NDS < NMF ? NDS : NMF;
@@ -489,9 +494,7 @@ __global__ void __launch_bounds__(TR::NT) gemm2_persistent_kernel(Gemm2Params g,
       for (int fm = 0; fm < TR::FM; ++fm)
 #pragma unroll
         for (int fn = 0; fn < TR::FN; ++fn)
-          acc[fm][fn] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-              __builtin_bit_cast(bf16x8, fa[cur][fm]), __builtin_bit_cast(bf16x8, fb[cur][fn]),
-              acc[fm][fn], 0, 0, 0);
+          acc[fm][fn] = mfma32<TR>(fa[cur][fm], fb[cur][fn], acc[fm][fn]);
       constexpr int NDS_I = NDS < NMF ? NDS : NMF;
       if (last && STEADY) {
 #pragma unroll

@@ -32,7 +32,7 @@ constexpr int64_t kF64WaveM = 64;
 
 // How one lce_forward / lce_backward call is laid out for a shape.
 struct CEPlan {
-  int32_t dtype = 0;          // LCE_BF16 or LCE_F64
+  int32_t dtype = 0;          // LCE_BF16, LCE_F16 or LCE_F64
   int64_t n = 0, D = 0, V = 0, chunk = 0;
   size_t elem = 0;            // bytes per input element
   size_t acc = 0;             // bytes per accumulator element

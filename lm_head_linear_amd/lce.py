@@ -19,13 +19,13 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "liblce.so")
 
 OK = 580
-BF16, F32, F64, I64, U8 = 1, 2, 3, 4, 6
+BF16, F32, F64, I64, F16, U8 = 1, 2, 3, 4, 5, 6
 STATUS = {580: "ok", 581: "empty_dimension", 582: "length_mismatch", 583: "dimension_too_large",
           584: "work_budget_exceeded", 585: "non_finite_scalar", 586: "target_id_out_of_range",
           587: "chunk_exceeds_logit_budget", 588: "unknown_objective", 589: "device_error",
           590: "dtype_mismatch"}
-_DT = {torch.bfloat16: BF16, torch.float32: F32, torch.float64: F64, torch.int64: I64,
-       torch.uint8: U8, torch.bool: U8}
+_DT = {torch.bfloat16: BF16, torch.float16: F16, torch.float32: F32, torch.float64: F64,
+       torch.int64: I64, torch.uint8: U8, torch.bool: U8}
 
 
 class LceError(RuntimeError):

@@ -9,8 +9,9 @@ Recipe (one numpy Generator per workload, draws in this order):
   targets ~ uniform ids in [0, vocab), or Zipf(s) ids by inverse CDF
   mask    : exactly round(frac * n_tok) tokens masked, chosen by a seeded
             permutation; 1 = counted
-bf16 workloads draw in fp32 and round to bf16 (round to nearest even, done by
-torch); the oracle reads exactly those bf16 values widened to fp64.
+bf16 and fp16 workloads draw in fp32 and round to the 16-bit type (round to
+nearest even, done by torch); the oracle reads exactly those values widened to
+fp64.
 Distillation: student ~ N(0, 4^2), teacher = student + N(0, 1), both rounded
 to the workload dtype after the sum.
 Label cross-entropy from logits: logits ~ N(0, 4^2) rounded to the dtype,
@@ -32,7 +33,7 @@ class CEWorkload:
     d_model: int
     vocab: int
     chunk: int
-    dtype: str            # "f64" or "bf16"
+    dtype: str            # "f64", "bf16" or "f16"
     sigma_w: float
     z_coef: float
     mask_frac: float
@@ -82,7 +83,8 @@ LABEL_BF16 = LabelWorkload("label_ce_bf16_4096x151936", 4096, 151936, "bf16", 1e
 
 
 def torch_dtype(name: str):
-    return {"bf16": torch.bfloat16, "f64": torch.float64, "f32": torch.float32}[name]
+    return {"bf16": torch.bfloat16, "f16": torch.float16, "f64": torch.float64,
+            "f32": torch.float32}[name]
 
 
 def _normal(rng: np.random.Generator, shape, sigma: float, dtype: str) -> torch.Tensor:

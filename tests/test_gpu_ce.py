@@ -130,6 +130,37 @@ def test_small_forward_backward(dt, n, D, V, chunk, mask, z):
         assert not dH[c.m == 0].any()
 
 
+F16 = [
+    # n, D, V, chunk, mask, z: pipelined core (one slab, several slabs) and the
+    # element-wise generic core
+    (300, 192, 3000, 64, 0.05, 1e-4),
+    (512, 256, 5000, 256, 0.05, 1e-4),
+    (130, 128, 500, 1024, None, 1e-3),
+    (96, 100, 777, 16, 0.2, 0.0),
+]
+
+
+@pytest.mark.parametrize("n,D,V,chunk,mask,z", F16)
+def test_f16_forward_backward(n, D, V, chunk, mask, z):
+    """fp16 inputs (fp32 accumulation, the bf16 path's tolerances).  The
+    gradient carries a loss scale in grad_out, as fp16 training does, so the
+    fp16 logit gradients stay clear of the fp16 subnormal range."""
+    import dataclasses
+    w = dataclasses.replace(syn.QWEN_BF16, dtype="f16")
+    _say(f"case f16 n={n} D={D} V={V} chunk={chunk} mask={mask} z={z}")
+    c = Case(w, n, D, V, seed=n + D + 1, mask_frac=mask, z=z)
+    assert c.H.dtype == torch.float16
+    fwd = c.gpu_forward(chunk)
+    ref = c.oracle_forward(chunk)
+    c.w = syn.QWEN_BF16            # same tolerances as the bf16 path
+    check_forward(c, fwd, ref)
+    dH, dW = c.gpu_backward(fwd.lse, chunk, grad_out=1024.0)
+    assert dH.dtype == torch.float16 and dW.dtype == torch.float32
+    rdH, rdW = oracle.backward(c.H64, c.W64, c.x.targets, ref["lse"], mask=c.x.mask,
+                               z_coef=c.z, grad_out=1024.0)
+    check_grads(c, dH, dW, rdH, rdW)
+
+
 def test_bf16_slab_pipeline_accumulates_d_weight():
     """accumulate_d_weight through the slab pipeline adds to the given rows."""
     c = Case(syn.QWEN_BF16, 512, 256, 5000, seed=11, mask_frac=0.05, z=1e-4)

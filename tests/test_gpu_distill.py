@@ -45,6 +45,26 @@ def test_small_distill(dt, obj, n, V):
     assert not g[m == 0].any()
 
 
+@pytest.mark.parametrize("obj", [0, 1, 2])
+def test_f16_distill(obj):
+    """fp16 logits; grad_out carries a loss scale as in fp16 training."""
+    dev = _dev()
+    n, V = 37, 1000
+    d = syn.distill_inputs(syn.DISTILL_BF16, n_tok=n, vocab=V, seed=60 + obj, dtype="f16")
+    S, U = d.student.to(dev), d.teacher.to(dev)
+    assert S.dtype == torch.float16
+    m = torch.from_numpy(d.mask).to(dev)
+    out, g = lce.distill(S, U, m, objective=obj, temperature=2.0, z_coef=1e-3, grad_out=1024.0)
+    r = oracle.distill(d.student.double().numpy(), d.teacher.double().numpy(), mask=d.mask,
+                       objective=obj, temperature=2.0, z_coef=1e-3, grad_out=1024.0)
+    el = abs(out["loss_mean"] - r["loss"]) / abs(r["loss"])
+    ez = abs(out["z_mean"] - r["z_loss"]) / abs(r["z_loss"])
+    eg = normwise(g.double().cpu().numpy(), r["grad"])
+    print(f"  f16 obj {obj}: loss rel {el:.2e} z rel {ez:.2e} grad {eg:.2e}", flush=True)
+    assert g.dtype == torch.float16
+    assert el <= 2e-3 and ez <= 2e-3 and eg <= 1e-2
+
+
 @pytest.mark.parametrize("obj", [1, 2])
 def test_kl_zero_for_identical_logits(obj):
     dev = _dev()

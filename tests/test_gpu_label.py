@@ -54,6 +54,26 @@ def test_small_label_ce(dt, n, V, mask_frac):
     assert out2["loss_sum"] == out["loss_sum"] and out2["z_sum"] == out["z_sum"]
 
 
+@pytest.mark.parametrize("n,V", [(37, 1000), (20, 1003)])
+def test_f16_label_ce(n, V):
+    """fp16 logits; grad_out carries a loss scale as in fp16 training."""
+    dev = _dev()
+    w = syn.LabelWorkload("small_f16", n, V, "f16", 1e-3, 0.2, 80 + n)
+    d = syn.label_inputs(w)
+    Z = d.logits.to(dev)
+    assert Z.dtype == torch.float16
+    y = torch.from_numpy(d.targets).to(dev)
+    m = torch.from_numpy(d.mask).to(dev)
+    out, g = lce.ce_logits(Z, y, m, z_coef=1e-3, grad_out=1024.0)
+    r = oracle.ce_logits(d.logits.double().numpy(), d.targets, mask=d.mask, z_coef=1e-3,
+                         grad_out=1024.0)
+    el = abs(out["loss_mean"] - r["loss"]) / abs(r["loss"])
+    ez = abs(out["z_mean"] - r["z_loss"]) / abs(r["z_loss"])
+    eg = normwise(g.double().cpu().numpy(), r["grad"])
+    print(f"  f16 label: loss rel {el:.2e} z rel {ez:.2e} grad {eg:.2e}", flush=True)
+    assert el <= 2e-3 and ez <= 2e-3 and eg <= 1e-2
+
+
 def test_uniform_logits_give_log_vocab():
     dev = _dev()
     n, V = 5, 151936
