@@ -214,6 +214,49 @@ def shard_measure(lce, torch, np, dev, w, H, W, y, m, steps: int, shards: int):
             "tokens_per_s": round(n / (ms / 1e3), 1), "loss": out.loss_mean}
 
 
+def f16_measure(lce, torch, np, dev, w, steps: int):
+    """The headline step with fp16 inputs (same shapes and draws, rounded to
+    fp16; grad_out 65536 as an fp16 loss scale)."""
+    import dataclasses
+    from tests import synthetic as syn
+    wf = dataclasses.replace(w, dtype="f16")
+    log(f"bench: fp16 inputs for {w.name}: generating inputs")
+    x = syn.ce_inputs(wf)
+    n, D, V, chunk, z = w.n_tok, w.d_model, w.vocab, w.chunk, w.z_coef
+    H, W = x.hidden.to(dev), x.weight.to(dev)
+    y = torch.from_numpy(x.targets).to(dev)
+    m = torch.from_numpy(x.mask).to(dev) if x.mask is not None else None
+    lse = torch.empty(n, dtype=torch.float32, device=dev)
+    dH = torch.empty_like(H)
+    dW = torch.empty(V, D, dtype=torch.float32, device=dev)
+    ws = torch.empty(lce.lce_workspace_bytes(n, D, V, chunk, H.dtype), dtype=torch.uint8,
+                     device=dev)
+
+    def step():
+        st, _ = lce.lce_forward(H, W, y, m, n, D, V, chunk, z, lse, ws, sync=False)
+        if st != lce.OK:
+            raise lce.LceError(st, "lce_forward")
+        st = lce.lce_backward(H, W, y, m, lse, n, D, V, chunk, z, 65536.0, dH, dW, 0, ws)
+        if st != lce.OK:
+            raise lce.LceError(st, "lce_backward")
+
+    for _ in range(3):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        step()
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) / steps * 1e3
+    st, out = lce.lce_loss_fetch(ws)
+    flops = 8.0 * n * D * V
+    return {"workload": w.name.replace("bf16", "f16"), "ms_per_step": round(ms, 4),
+            "tokens_per_s": round(n / (ms / 1e3), 1),
+            "tflops_8ndv": round(flops / (ms / 1e3) / 1e12, 2),
+            "mfma_frac_8ndv": round(flops / (ms / 1e3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+            "loss": out.loss_mean}
+
+
 def cpu_baseline(w, x, tokens: int):
     """The oracle, as it stands, on the first `tokens` tokens of the workload:
     forward (all tokens of the prefix) + backward (d_hidden of the prefix and
@@ -250,8 +293,10 @@ def main():
                          "reference for the FETCH_SIZE / WRITE_SIZE counters)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-kernel-events", action="store_true")
+    ap.add_argument("--no-shards", action="store_true",
+                    help="skip the vocabulary-shard measurement")
     ap.add_argument("--no-distill", action="store_true",
-                    help="skip the side measurements (vocabulary shards; distillation and label CE at 4096 x 151936 bf16)")
+                    help="skip the side measurements (vocabulary shards, distillation and label CE)")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -396,8 +441,12 @@ def main():
                 "frac": round(achieved / peak, 4), "traffic": traffic_from_profiles(w.name, dom),
                 "kernel": dom, "flops_per_launch": per_launch_flops, "avg_launch_ms": kd["avg_ms"]}
 
+    f16 = None
+    if w.dtype == "bf16" and not (args.no_distill or args.no_shards):
+        f16 = f16_measure(lce, torch, np, dev, w, args.steps)
+
     shard = None
-    if w.dtype == "bf16" and not args.no_distill:
+    if w.dtype == "bf16" and not (args.no_distill or args.no_shards):
         log("bench: the same step in 4 vocabulary shards")
         shard = shard_measure(lce, torch, np, dev, w, H, W, y, m, args.steps, 4)
         shard["vs_unsharded"] = round(ms_per_step / shard["ms_per_step"], 4)
@@ -441,6 +490,7 @@ def main():
         "distill": distill,
         "label_ce": label,
         "vocab_shards": shard,
+        "f16_inputs": f16,
         "cpu_baseline": cpu,
     }
     print(json.dumps(res), flush=True)
