@@ -314,7 +314,16 @@ def main():
         for _ in range(2):
             dst.copy_(src)
         torch.cuda.synchronize()
-        print(json.dumps({"copy_calibration_bytes": nbytes, "copies": 2}), flush=True)
+        # the same copy timed: read + write bytes over time, a practical HBM ceiling
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(10):
+            dst.copy_(src)
+        e1.record()
+        torch.cuda.synchronize()
+        gbs = 2 * nbytes * 10 / (e0.elapsed_time(e1) / 1e3) / 1e9
+        print(json.dumps({"copy_calibration_bytes": nbytes, "copies": 2,
+                          "copy_read_write_GBs": round(gbs, 1)}), flush=True)
         return
 
     from lm_head_linear_amd import lce
