@@ -54,6 +54,23 @@ template <> struct IO<uint16_t> {  // bf16 bits
     }
   }
   __device__ static inline float load1(const uint16_t *p) { return __uint_as_float(uint32_t(*p) << 16); }
+  __device__ static inline void unpack8(const u32x4 v, float *o) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      o[2 * i] = __uint_as_float(v[i] << 16);
+      o[2 * i + 1] = __uint_as_float(v[i] & 0xffff0000u);
+    }
+  }
+  __device__ static inline u32x4 pack8(const float *g) {
+    typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+    u32x4 v;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const bf16x2_t h = {static_cast<__bf16>(g[2 * i]), static_cast<__bf16>(g[2 * i + 1])};
+      v[i] = __builtin_bit_cast(uint32_t, h);
+    }
+    return v;
+  }
   // round to nearest even (v_cvt_pk_bf16_f32; NaN stays NaN)
   __device__ static inline uint16_t cvt(float f) {
     return __builtin_bit_cast(uint16_t, static_cast<__bf16>(f));
@@ -79,6 +96,17 @@ template <> struct IO<_Float16> {  // IEEE half; v_cvt_f16_f32 rounds to nearest
     for (int i = 0; i < 8; ++i) o[i] = static_cast<float>(v[i]);
   }
   __device__ static inline float load1(const _Float16 *p) { return static_cast<float>(*p); }
+  __device__ static inline void unpack8(const u32x4 v, float *o) {
+    const h8 h = __builtin_bit_cast(h8, v);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) o[i] = static_cast<float>(h[i]);
+  }
+  __device__ static inline u32x4 pack8(const float *g) {
+    h8 v;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) v[i] = static_cast<_Float16>(g[i]);
+    return __builtin_bit_cast(u32x4, v);
+  }
   __device__ static inline void store8(_Float16 *p, const float *g) {
     h8 v;
 #pragma unroll
@@ -155,8 +183,9 @@ __device__ inline Online<C> shfl_xor_online(const Online<C> &v, int o) {
 constexpr int kBlock = 1024;
 constexpr int64_t kRowGrid = 256;   // workgroups: one per compute unit
 
-// Reduce within the block in a fixed order; thread 0 gets the result.
-template <class C>
+// Reduce within the block (NT threads) in a fixed order; thread 0 gets the
+// result.
+template <class C, int NT = kBlock>
 __device__ inline void block_merge(Online<C> &v, Online<C> *sh) {
   for (int o = 1; o < 64; o <<= 1) {
     Online<C> w = shfl_xor_online(v, o);
@@ -166,7 +195,7 @@ __device__ inline void block_merge(Online<C> &v, Online<C> *sh) {
   if (lane == 0) sh[wave] = v;
   __syncthreads();
   if (threadIdx.x == 0)
-    for (int w = 1; w < kBlock / 64; ++w) v.merge(sh[w]);
+    for (int w = 1; w < NT / 64; ++w) v.merge(sh[w]);
 }
 
 template <class T, int OBJ, bool VEC>
@@ -359,6 +388,102 @@ __device__ __forceinline__ void label_row(const T *Z, const int64_t *y, const ui
   }
 }
 
+// 16-bit logits with the gradient, rows of at most 8 * CPT * kResBlock values:
+// each thread keeps its CPT 16-byte chunks of the row in registers, so the row
+// is read from memory once (pass 2 computes from the registers).  512 threads,
+// one workgroup per CU: 8 waves of up to 256 registers each.
+constexpr int kResBlock = 512;
+template <class T, int CPT>
+__device__ __forceinline__ void label_row_resident(const T *Z, const int64_t *y,
+                                                   const uint8_t *mask, int64_t t, int64_t V,
+                                                   double z_coef, double grad_out,
+                                                   const Control *ctl, T *grad, double *row_out) {
+  const T *z_row = Z + t * V;
+  T *g_row = grad + t * V;
+  const int tid = threadIdx.x;
+  const int64_t nvec = V / 8;
+  // Buffer accesses: one lane offset, the chunk index in the scalar offset;
+  // every access is predicated on its chunk lying inside the row.
+  const uint32_t voff = uint32_t(tid) * 16u;
+  const __amdgpu_buffer_rsrc_t ro =
+      __builtin_amdgcn_make_buffer_rsrc(g_row, 0, int(V * int64_t(sizeof(T))), 0x00020000);
+  if (mask && !mask[t]) {
+    const u32x4 zero = {0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int i = 0; i < CPT; ++i)
+      if (tid + int64_t(i) * kResBlock < nvec)
+        __builtin_amdgcn_raw_buffer_store_b128(zero, ro, voff, i * kResBlock * 16, 2);
+    if (tid == 0) { row_out[2 * t] = 0.0; row_out[2 * t + 1] = 0.0; }
+    return;
+  }
+  __syncthreads();   // the previous row's statistics are no longer read
+  const __amdgpu_buffer_rsrc_t ri = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<T *>(z_row), 0, int(V * int64_t(sizeof(T))), 0x00020000);
+  u32x4 xr[CPT];
+#pragma unroll
+  for (int i = 0; i < CPT; ++i)
+    if (tid + int64_t(i) * kResBlock < nvec)
+      xr[i] = __builtin_amdgcn_raw_buffer_load_b128(ri, voff, i * kResBlock * 16, 0);
+  Online<float> f;
+  f.init();
+#pragma unroll
+  for (int i = 0; i < CPT; ++i) {
+    if (tid + int64_t(i) * kResBlock >= nvec) continue;
+    float xs[8];
+    IO<T>::unpack8(xr[i], xs);
+    float lm = xs[0];
+#pragma unroll
+    for (int j = 1; j < 8; ++j) lm = xs[j] > lm ? xs[j] : lm;
+    const float nm = f.m > lm ? f.m : lm;
+    f.s *= dexp<float>(f.m - nm);
+    f.m = nm;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) f.s += dexp<float>(xs[j] - nm);
+  }
+  __shared__ Online<float> sh_f[kResBlock / 64];
+  __shared__ float sh_lse;
+  block_merge<float, kResBlock>(f, sh_f);
+  const int64_t yt = y[t];
+  if (tid == 0) {
+    const float lse = f.m + dlog<float>(f.s);
+    sh_lse = lse;
+    row_out[2 * t] = double(lse - IO<T>::load1(z_row + yt));
+    row_out[2 * t + 1] = double(lse);
+  }
+  __syncthreads();
+  const float lse = sh_lse;
+  const int64_t cnt = ctl->count;
+  const float g = cnt ? float(grad_out / double(cnt)) : 0.f;
+  const float a = g * (1.f + float(2.0 * z_coef) * lse);
+  // the target element relative to this thread's first chunk
+  const int64_t ty = yt - int64_t(tid) * 8;
+  // Pass 2 unpacks the packed chunks again: holding pass 1's floats (8 per
+  // chunk) across the reduction would not fit the registers.
+#pragma unroll
+  for (int i = 0; i < CPT; ++i) asm volatile("" : "+v"(xr[i]));
+#pragma unroll
+  for (int i = 0; i < CPT; ++i) {
+    if (tid + int64_t(i) * kResBlock >= nvec) continue;
+    float xs[8], gs[8];
+    IO<T>::unpack8(xr[i], xs);
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+      gs[j] = a * dexp<float>(xs[j] - lse) - (ty == int64_t(i) * kResBlock * 8 + j ? g : 0.f);
+    __builtin_amdgcn_raw_buffer_store_b128(IO<T>::pack8(gs), ro, voff, i * kResBlock * 16, 2);
+  }
+}
+
+template <class T, int CPT>
+__global__ void __launch_bounds__(kResBlock)
+label_resident_kernel(const T *Z, const int64_t *y, const uint8_t *mask, int64_t n, int64_t V,
+                      double z_coef, double grad_out, const Control *ctl, T *grad,
+                      double *row_out) {
+  if (ctl->bad) return;
+  for (int64_t t = blockIdx.x; t < n; t += gridDim.x)
+    label_row_resident<T, CPT>(Z, y, mask, t, V, z_coef, grad_out, ctl, grad, row_out);
+}
+constexpr int kResidentChunks = 38;   // rows up to 8 * 38 * 512 = 155648 values
+
 // Rows t = blockIdx.x, + gridDim.x, ...; nothing runs when the guard found
 // an out-of-range target (the outputs stay untouched).
 template <class T, bool VEC, bool GRAD>
@@ -466,7 +591,16 @@ void label_impl(bool vec, bool want_grad, const T *Z, const int64_t *y, const ui
   const unsigned grid = unsigned(n < kRowGrid ? n : kRowGrid);
   {
     TimedLaunch tl(tm, LCE_K_LABEL_CE, st);
-    if (vec && want_grad)
+    bool done = false;
+    if constexpr (sizeof(T) == 2) {   // 16-bit rows that fit the registers: read once
+      if (vec && want_grad && V / 8 <= int64_t(kResidentChunks) * kResBlock) {
+        hipLaunchKernelGGL((label_resident_kernel<T, kResidentChunks>), dim3(grid),
+                           dim3(kResBlock), 0, st, Z, y, mask, n, V, z, go, ctl, grad, rows);
+        done = true;
+      }
+    }
+    if (done) {
+    } else if (vec && want_grad)
       hipLaunchKernelGGL((label_row_kernel<T, true, true>), dim3(grid), dim3(kBlock), 0, st, Z, y,
                          mask, n, V, z, go, ctl, grad, rows);
     else if (vec)

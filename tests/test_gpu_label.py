@@ -27,7 +27,8 @@ def normwise(a, ref):
 
 
 @pytest.mark.parametrize("dt", ["bf16", "f32", "f64"])
-@pytest.mark.parametrize("n,V,mask_frac", [(37, 1000, 0.2), (20, 1003, 0.0), (3, 4096, 0.34)])
+@pytest.mark.parametrize("n,V,mask_frac", [(37, 1000, 0.2), (20, 1003, 0.0), (3, 4096, 0.34),
+                                            (5, 151936, 0.2), (3, 155648, 0.0)])
 def test_small_label_ce(dt, n, V, mask_frac):
     print(f"case label {dt} n={n} V={V} mask {mask_frac}", flush=True)
     dev = _dev()
@@ -48,10 +49,13 @@ def test_small_label_ce(dt, n, V, mask_frac):
     assert el <= lt and ez <= lt and eg <= gt
     if m is not None:
         assert not g[m == 0].any()
-    # loss only: the same scalars without a gradient pass
+    # loss only: the same scalars without a gradient pass (16-bit rows that fit
+    # the registers take another kernel with another summation order)
     out2, g2 = lce.ce_logits(Z, y, m, z_coef=1e-3, grad_out=1.3, want_grad=False)
     assert g2 is None
-    assert out2["loss_sum"] == out["loss_sum"] and out2["z_sum"] == out["z_sum"]
+    rt = 1e-6 if dt == "bf16" else 0.0
+    assert abs(out2["loss_sum"] - out["loss_sum"]) <= rt * abs(out["loss_sum"])
+    assert abs(out2["z_sum"] - out["z_sum"]) <= rt * abs(out["z_sum"])
 
 
 @pytest.mark.parametrize("n,V", [(37, 1000), (20, 1003)])
