@@ -25,7 +25,7 @@ def normwise(a, ref):
 
 @pytest.mark.parametrize("dt", ["bf16", "f32", "f64"])
 @pytest.mark.parametrize("obj", [0, 1, 2])
-@pytest.mark.parametrize("n,V", [(37, 1000), (20, 1003)])
+@pytest.mark.parametrize("n,V", [(37, 1000), (20, 1003), (4, 151936)])
 def test_small_distill(dt, obj, n, V):
     print(f"case distill {dt} obj={obj} n={n} V={V}", flush=True)
     dev = _dev()
