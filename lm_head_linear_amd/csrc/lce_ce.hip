@@ -340,7 +340,7 @@ __global__ void fwd_final_kernel(const double *loss_tok, const Acc *lse, const u
 
 // ----------------------------------------------------- backward epilogues --
 
-// LDS-staged output of one wave's fp32-accumulated tile (bf16 core; the wave
+// LDS-staged output of one wave's fp32-accumulated tile (16-bit core; the wave
 // tile is TR::WTM x TR::WTN, 32x32 MFMA blocks).  Rows of the accumulator
 // layout are spread over lanes in steps of four, so storing straight from
 // registers costs one narrow access per value.  Instead each 32-row block goes
@@ -490,7 +490,7 @@ struct DlogitEpi {
     else body<true>(acc, vw0, tw0, lane, g, gz);
   }
 
-  // bf16 core: the same values through LDS.  Token columns in [n, d_ld) get
+  // 16-bit core: the same values through LDS.  Token columns in [n, d_ld) get
   // zeros (they are the K padding of the d_weight GEMM).
   //   d = coef * exp(z - lse) - g [v == y] = s exp2(z log2(e) + c2) - g [v == y]
   // with c2 = log2|coef| - lse log2(e) and s the sign of coef (coef 0 gives
@@ -627,7 +627,7 @@ struct StoreEpi {
     else body<true>(acc, o, rw0, cw0, lane);
   }
 
-  // bf16 core: through LDS, 16-byte accesses (cols and ldo multiples of 4,
+  // 16-bit core: through LDS, 16-byte accesses (cols and ldo multiples of 4,
   // `out` 16-byte aligned; the host checks).
   static constexpr bool kStaged = true;
   __device__ __forceinline__ void staged(typename TR::AccBlock (&acc)[TR::FM][TR::FN], int64_t m0,

@@ -7,10 +7,10 @@
 //     registers); the buffer descriptor's record count zero-fills every
 //     element past the operand's valid extent, which handles the M/N edges and
 //     the K tail of MN-major operands without branches;
-//   * a ring of 4 LDS stages of BK = 32 (128 KB) keeps 3 k-steps of loads in
-//     flight; each stage ends with one s_barrier after a vmcnt wait that only
-//     covers the stage about to be read;
-//   * K-major tiles keep 64-byte rows and are read with ds_read_b128; MN-major
+//   * a ring of LDS stages (PipeCfg: STAGES x BK; the library runs 2 x 64,
+//     128 KB) keeps the next k-steps' loads in flight; each stage ends with one
+//     s_barrier after a vmcnt wait that only covers the stage about to be read;
+//   * K-major tiles keep BK * 2-byte rows and are read with ds_read_b128; MN-major
 //     tiles keep their global orientation (512-byte k-rows) and are read with
 //     ds_read_b64_tr_b16, which hands each lane four consecutive k of one row.
 //     XOR swizzles of the 16-byte chunks keep the DMA writes and both kinds of
@@ -22,7 +22,8 @@
 //   * an epilogue with kStaged set gets the LDS ring (after a barrier) as
 //     staging space for its output tile (staged()); otherwise operator() runs
 //     straight from the accumulators.  kPrefetchBytes lets it load per-tile
-//     constants into LDS while the first stages are in flight.
+//     constants before the first stages issue and write them to LDS after
+//     the main loop.
 // Requirements (checked by the host): 16-byte aligned bases, leading
 // dimensions multiple of 8, K-major operands zero-padded (or exact) to a
 // multiple of the k-step along K, 256 * ld * 2 bytes below 2^31.
