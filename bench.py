@@ -170,7 +170,7 @@ def shard_measure(lce, torch, np, dev, w, H, W, y, m, steps: int, shards: int):
     n, D = H.shape
     V = W.shape[0]
     bounds = [V * q // shards // 256 * 256 for q in range(shards)] + [V]
-    acc = torch.float32 if H.dtype == torch.bfloat16 else torch.float64
+    acc = torch.float64 if H.dtype == torch.float64 else torch.float32
     stats = torch.empty(shards, 3, n, dtype=acc, device=dev)
     lse = torch.empty(n, dtype=acc, device=dev)
     part = torch.empty(n, D, dtype=acc, device=dev)

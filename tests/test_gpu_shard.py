@@ -35,7 +35,7 @@ def run_shards(H, W, y, m, bounds, chunk, z, grad_out=1.0, backward=True):
     dev = H.device
     n, D = H.shape
     V = W.shape[0]
-    acc = torch.float32 if H.dtype == torch.bfloat16 else torch.float64
+    acc = torch.float64 if H.dtype == torch.float64 else torch.float32
     P = len(bounds) - 1
     stats = torch.empty(P, 3, n, dtype=acc, device=dev)
     wss = []
@@ -112,6 +112,30 @@ def test_shards_match_the_whole_head(dt, n, D, V, bounds, chunk, mask, z):
     ew = normwise(dW.double().cpu().numpy(), rdW)
     _say(f"  dH {eh:.2e} dW {ew:.2e}")
     assert eh <= gt and ew <= gt
+
+
+def test_f16_shards():
+    """fp16 inputs in three shards; grad_out carries an fp16 loss scale."""
+    import dataclasses
+    dev = _dev()
+    w = dataclasses.replace(syn.QWEN_BF16, dtype="f16")
+    n, D, V, chunk, z, go = 300, 128, 3000, 64, 1e-4, 1024.0
+    x = syn.ce_inputs(w, n_tok=n, d_model=D, vocab=V, seed=71)
+    x.mask = syn.exact_mask(np.random.default_rng(71), n, 0.05)
+    H, W = x.hidden.to(dev), x.weight.to(dev)
+    assert H.dtype == torch.float16
+    y = torch.from_numpy(x.targets).to(dev)
+    m = torch.from_numpy(x.mask).to(dev)
+    out, lse, _, dH, dW = run_shards(H, W, y, m, [0, 1024, 2048, 3000], chunk, z, grad_out=go)
+    H64, W64 = x.hidden64(), x.weight64()
+    ref = oracle.fused_forward(H64, W64, x.targets, mask=x.mask, chunk=chunk, z_coef=z)
+    el = abs(out["loss_mean"] - ref["loss_mean"]) / abs(ref["loss_mean"])
+    rdH, rdW = oracle.backward(H64, W64, x.targets, ref["lse"], mask=x.mask, z_coef=z,
+                               grad_out=go)
+    eh = normwise(dH.cpu().numpy(), rdH)
+    ew = normwise(dW.double().cpu().numpy(), rdW)
+    _say(f"  f16 shards: loss rel {el:.2e} dH {eh:.2e} dW {ew:.2e}")
+    assert el <= 2e-3 and eh <= 1e-2 and ew <= 1e-2
 
 
 @pytest.mark.parametrize("dt", ["bf16", "f64"])
