@@ -915,7 +915,8 @@ static void forward_impl(const CEPlan &p, const void *H, const void *W, const in
 
 // 16-bit backward as a slab pipeline: launch k runs d_hidden and d_weight of
 // slab k-1 (from slab buffer (k-1) % 2) together with the logit gradient of
-// slab k (into buffer k % 2), longest products first.  The d_hidden split
+// slab k (into buffer k % 2), longest products first.  Slab 0 may be shorter
+// than the rest (the plan sizes it to one round of CUs).  The d_hidden split
 // accumulators start at zero and every launch adds to them.
 template <class TR, bool ACC_DW>
 static void backward_pipelined(const CEPlan &p, const uint16_t *Hp, const uint16_t *Wp,
@@ -935,13 +936,20 @@ static void backward_pipelined(const CEPlan &p, const uint16_t *Hp, const uint16
     hipLaunchKernelGGL(zero_f32_kernel, dim3(unsigned(blocks)), dim3(256), 0, st, dhacc, count);
   }
   const int64_t tiles_d = cdiv(D, 256), tiles_t = cdiv(n, 256);
+  // first vocabulary row and row count of slab j
+  auto slab_at = [&](int64_t j, int64_t &rows) {
+    const int64_t v0 = j == 0 ? 0 : p.pslab0 + (j - 1) * S;
+    const int64_t cap = j == 0 ? p.pslab0 : S;
+    rows = cap < V - v0 ? cap : V - v0;
+    return v0;
+  };
   for (int64_t k = 0; k <= p.pn_slabs; ++k) {
     JH jh{};
     JW jw{};
     JL jl{};
     if (k >= 1) {  // slab k-1: d_hidden += d W_slab, d_weight rows = d H
-      const int64_t vs0 = (k - 1) * S;
-      const int64_t rows = S < V - vs0 ? S : V - vs0;
+      int64_t rows;
+      const int64_t vs0 = slab_at(k - 1, rows);
       const uint16_t *buf = dbuf + ((k - 1) & 1) * S * p.d_ld;
       GemmParams g;
       g.A = buf; g.lda = p.d_ld;
@@ -969,8 +977,8 @@ static void backward_pipelined(const CEPlan &p, const uint16_t *Hp, const uint16
       jw.nb = round_up8(jw.nreal);
     }
     if (k < p.pn_slabs) {  // slab k: recomputed logits -> logit gradient
-      const int64_t vs0 = k * S;
-      const int64_t rows = S < V - vs0 ? S : V - vs0;
+      int64_t rows;
+      const int64_t vs0 = slab_at(k, rows);
       uint16_t *buf = dbuf + (k & 1) * S * p.d_ld;
       GemmParams g;
       g.A = Wp + vs0 * D; g.lda = D;

@@ -153,8 +153,16 @@ int32_t plan_ce(int64_t n, int64_t D, int64_t V, int64_t chunk, int32_t dtype, C
         }
       }
       q.pslab = S < V ? S : V;
-      q.pn_slabs = ceil_div(V, q.pslab);
       q.pdh_splits = best_sp;
+      // The first launch runs slab 0's logit gradient alone: when a whole slab
+      // would take more than one round of CUs, slab 0 gets the rows that fill
+      // exactly one round (8192 at 2048 tokens) and the later slabs the rest.
+      q.pslab0 = q.pslab;
+      if (tn <= kComputeUnits) {
+        const int64_t r0 = (kComputeUnits / tn) * tile_m;
+        if (r0 < q.pslab && ceil_div(q.pslab, tile_m) * tn > kComputeUnits) q.pslab0 = r0;
+      }
+      q.pn_slabs = V > q.pslab0 ? 1 + ceil_div(V - q.pslab0, q.pslab) : 1;
     }
   }
 

@@ -49,6 +49,7 @@ struct CEPlan {
   // d_weight of slab k with the logit gradient of slab k+1)
   int64_t pslab = 0;          // vocabulary rows per buffer
   int64_t pn_slabs = 0;
+  int64_t pslab0 = 0;         // rows of the first slab (<= pslab; the others pslab)
   int64_t pdh_splits = 0;
   // workspace layout (byte offsets)
   size_t off_partials = 0, off_zy = 0, off_losstok = 0;

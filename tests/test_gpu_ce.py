@@ -111,6 +111,9 @@ SMALL = [
     ("bf16", 320, 128, 700, 512, None, 1e-3),     # 512 + 188 rows
     ("bf16", 256, 64, 300, 512, 0.1, 0.0),        # 256 + 44 rows
     ("bf16", 130, 128, 500, 1024, None, 1e-4),    # one slab of 500 rows, ragged tokens
+    # a whole slab of logit-gradient tiles would take more than one round of
+    # CUs: slab 0 gets the rows of one round, 13056 + 18944 + 8000
+    ("bf16", 1100, 64, 40000, 1100, 0.05, 1e-4),
 ]
 
 
@@ -137,6 +140,7 @@ F16 = [
     (512, 256, 5000, 256, 0.05, 1e-4),
     (130, 128, 500, 1024, None, 1e-3),
     (96, 100, 777, 16, 0.2, 0.0),
+    (1100, 64, 40000, 1100, 0.05, 1e-4),          # shorter first slab
 ]
 
 
