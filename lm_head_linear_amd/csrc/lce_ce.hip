@@ -50,13 +50,13 @@ __global__ void ctl_init_kernel(Control *ctl, int keep_loss) {
 // Target-range guard (lossk table, loss_targets_in_range) and the count of
 // counted tokens (y == nullptr: the count only).  Integer work only, so the
 // atomics are order-free.
-__global__ void guard_kernel(const int64_t *y, const uint8_t *mask, int64_t n, int64_t V,
-                             Control *ctl) {
+// Block `bid` of `nblk` (blockDim 256).
+__device__ __forceinline__ void guard_block(const int64_t *y, const uint8_t *mask, int64_t n,
+                                            int64_t V, Control *ctl, int64_t bid, int64_t nblk) {
   __shared__ unsigned long long s_first[4];
   __shared__ unsigned long long s_count[4];
   unsigned long long first = ULLONG_MAX, count = 0;
-  for (int64_t t = int64_t(blockIdx.x) * blockDim.x + threadIdx.x; t < n;
-       t += int64_t(gridDim.x) * blockDim.x) {
+  for (int64_t t = bid * blockDim.x + threadIdx.x; t < n; t += nblk * blockDim.x) {
     const int64_t v = y ? y[t] : 0;
     if (v < 0 || v >= V) first = first < (unsigned long long)t ? first : (unsigned long long)t;
     count += mask ? (mask[t] != 0) : 1;
@@ -82,15 +82,9 @@ __global__ void guard_kernel(const int64_t *y, const uint8_t *mask, int64_t n, i
   }
 }
 
-// Vocabulary shard of rows [offset, offset + rows): a token's target id
-// relative to the shard, or -1 when another shard holds the target row.
-__global__ void localize_targets_kernel(const int64_t *y, int64_t n, int64_t offset, int64_t rows,
-                                        int64_t *yl) {
-  for (int64_t t = int64_t(blockIdx.x) * blockDim.x + threadIdx.x; t < n;
-       t += int64_t(gridDim.x) * blockDim.x) {
-    const int64_t v = y[t] - offset;
-    yl[t] = (v >= 0 && v < rows) ? v : -1;
-  }
+__global__ void guard_kernel(const int64_t *y, const uint8_t *mask, int64_t n, int64_t V,
+                             Control *ctl) {
+  guard_block(y, mask, n, V, ctl, blockIdx.x, gridDim.x);
 }
 
 template <class T> __device__ inline T fexp(T x);
@@ -151,7 +145,7 @@ template <> __device__ inline double shift_exp<double>(double x, double m) { ret
 
 // Z^T tile: rows = vocabulary ids, columns = tokens of the pass.  For every
 // token column and every wave (WTM consecutive vocabulary rows) write
-// (max, sum exp(z - max)).  (The target logits come from target_logit_kernel.)
+// (max, sum exp(z - max)).  (The target logits come from target_logit_block.)
 template <class TR>
 struct FwdLseEpi {
   typedef typename TR::Acc Acc;
@@ -205,23 +199,27 @@ struct FwdLseEpi {
 };
 
 // zy[t] = <H[t], W[y_t]> for every token: one wave per token, lane-strided
-// partial sums in the accumulator type and a fixed shuffle tree.  A negative
-// id (target in another vocabulary shard) gives 0.
+// partial sums in the accumulator type and a fixed shuffle tree.
+// Block `bid` (blockDim 256, four tokens per block).  W holds head rows
+// [offset, offset + rows); a target outside them (another vocabulary shard's
+// row, or an id the guard refuses) gives 0.
 template <class TR>
-__global__ void target_logit_kernel(const typename TR::E *H, const typename TR::E *W,
-                                    const int64_t *y, int64_t n, int64_t D,
-                                    typename TR::Acc *zy, const int32_t *bad, int vec8) {
+__device__ __forceinline__ void target_logit_block(const typename TR::E *H,
+                                                   const typename TR::E *W, const int64_t *y,
+                                                   int64_t offset, int64_t rows, int64_t n,
+                                                   int64_t D, typename TR::Acc *zy, int vec8,
+                                                   int64_t bid) {
   typedef typename TR::Acc Acc;
-  if (*bad) return;
   const int lane = threadIdx.x & 63;
-  const int64_t t = int64_t(blockIdx.x) * (blockDim.x >> 6) + (threadIdx.x >> 6);
+  const int64_t t = bid * (blockDim.x >> 6) + (threadIdx.x >> 6);
   if (t >= n) return;
-  if (y[t] < 0) {   // target row held by another vocabulary shard
+  const int64_t v = y[t] - offset;
+  if (v < 0 || v >= rows) {
     if (lane == 0) zy[t] = 0;
     return;
   }
   const typename TR::E *h = H + t * D;
-  const typename TR::E *w = W + y[t] * D;
+  const typename TR::E *w = W + v * D;
   Acc s = 0;
   if constexpr (std::is_same<typename TR::E, uint16_t>::value) {
     // 16-byte chunks of 8 elements (rows 16-byte aligned and D % 8 == 0: the
@@ -649,13 +647,14 @@ struct StoreEpi {
   }
 };
 
-// Ht[d][t] = H[t][d] for t < n, 0 for n <= t < ld (bf16 bits).  64x64 tiles
-// through LDS; blockDim 256.
-__global__ void transpose_h_kernel(const uint16_t *H, int64_t n, int64_t D, uint16_t *Ht,
-                                   int64_t ld) {
+// Ht[d][t] = H[t][d] for t < n, 0 for n <= t < ld (16-bit values).  64x64
+// tiles through LDS; blockDim 256; block (bt, bd) of the tile grid.
+__device__ __forceinline__ void transpose_h_block(const uint16_t *H, int64_t n, int64_t D,
+                                                  uint16_t *Ht, int64_t ld, int64_t bt,
+                                                  int64_t bd) {
   __shared__ uint16_t tile[64][66];
   const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;
-  const int64_t t0 = int64_t(blockIdx.x) * 64, d0 = int64_t(blockIdx.y) * 64;
+  const int64_t t0 = bt * 64, d0 = bd * 64;
 #pragma unroll
   for (int j = 0; j < 16; ++j) {
     const int64_t t = t0 + ty + 4 * j, d = d0 + tx;
@@ -669,10 +668,63 @@ __global__ void transpose_h_kernel(const uint16_t *H, int64_t n, int64_t D, uint
   }
 }
 
-__global__ void zero_f32_kernel(float *p, int64_t count) {
-  for (int64_t i = int64_t(blockIdx.x) * blockDim.x + threadIdx.x; i < count;
-       i += int64_t(gridDim.x) * blockDim.x)
-    p[i] = 0.f;
+
+// Per-call preparation in one launch.  Its parts do not read each other's
+// results, so they share a grid: blocks [0, nb_guard) run the target guard
+// and token count (ctl_init has run), then nb_local blocks the shard-local
+// target ids, nb_zy blocks the target logits, nb_tr blocks H^T (the d_weight
+// product's K-major operand) and nb_zero blocks clear the d_hidden split
+// accumulators.  A part with no blocks is absent.  blockDim 256.
+template <class TR>
+struct Prep {
+  const int64_t *y;
+  const uint8_t *mask;
+  int64_t n, v_check;       // guard: ids must lie in [0, v_check)
+  Control *ctl;
+  int64_t offset, rows;     // W holds head rows [offset, offset + rows)
+  int64_t *yl;              // shard-local ids (shard calls): y - offset, or -1
+                            // when another shard holds the target row
+  const typename TR::E *H, *W;
+  int64_t D;
+  typename TR::Acc *zy;
+  int vec8;
+  typename TR::E *Ht;       // [D][ld] (16-bit inputs)
+  int64_t ld, tr_cols;      // tr_cols = ceil(ld / 64) tile columns
+  float *zero;
+  int64_t zero_count;
+  int64_t nb_guard, nb_local, nb_zy, nb_tr, nb_zero;
+  int64_t blocks() const { return nb_guard + nb_local + nb_zy + nb_tr + nb_zero; }
+};
+
+template <class TR>
+__global__ void prep_kernel(Prep<TR> a) {
+  int64_t b = blockIdx.x;
+  if (b < a.nb_guard) {
+    guard_block(a.y, a.mask, a.n, a.v_check, a.ctl, b, a.nb_guard);
+    return;
+  }
+  b -= a.nb_guard;
+  if (b < a.nb_local) {
+    for (int64_t t = b * blockDim.x + threadIdx.x; t < a.n; t += a.nb_local * blockDim.x) {
+      const int64_t v = a.y[t] - a.offset;
+      a.yl[t] = (v >= 0 && v < a.rows) ? v : -1;
+    }
+    return;
+  }
+  b -= a.nb_local;
+  if (b < a.nb_zy) {
+    target_logit_block<TR>(a.H, a.W, a.y, a.offset, a.rows, a.n, a.D, a.zy, a.vec8, b);
+    return;
+  }
+  b -= a.nb_zy;
+  if (b < a.nb_tr) {
+    if constexpr (IsH16<TR>::value)
+      transpose_h_block(a.H, a.n, a.D, a.Ht, a.ld, b % a.tr_cols, b / a.tr_cols);
+    return;
+  }
+  b -= a.nb_tr;
+  for (int64_t i = b * blockDim.x + threadIdx.x; i < a.zero_count; i += a.nb_zero * blockDim.x)
+    a.zero[i] = 0.f;
 }
 
 // d_hidden = sum over splits (ascending) of the split accumulators, in the
@@ -842,19 +894,45 @@ struct Shard {
   Acc *stats = nullptr;   // forward: {m, s, z_target} rows of n tokens
 };
 
-// Guard against the head's rows; for a shard, the targets relative to it.
-template <class Acc>
-static const int64_t *guard_targets(const CEPlan &p, const int64_t *y, const uint8_t *mask,
-                                    const Shard<Acc> &sh, Control *ctl, uint8_t *ws,
-                                    hipStream_t st, lce_timers *tm, int keep_loss) {
-  launch_guard(y, mask, p.n, sh.total ? sh.total : p.V, ctl, st, tm, keep_loss);
-  if (!sh.total) return y;
-  int64_t *yl = reinterpret_cast<int64_t *>(ws + p.off_yloc);
-  int64_t blocks = cdiv(p.n, 256);
-  if (blocks > 1024) blocks = 1024;
-  hipLaunchKernelGGL(localize_targets_kernel, dim3(unsigned(blocks)), dim3(256), 0, st, y, p.n,
-                     sh.offset, p.V, yl);
-  return yl;
+// The per-call preparation: ctl_init, then one prep_kernel with the guard
+// (against the head's rows), the shard-local ids (shard calls), the target
+// logits (zy), H^T (Ht) and the cleared d_hidden accumulators (zero; absent
+// when null).  Returns the target ids the later kernels use.
+template <class TR>
+static const int64_t *prepare(const CEPlan &p, const int64_t *y, const uint8_t *mask,
+                              const Shard<typename TR::Acc> &sh, Control *ctl, uint8_t *ws,
+                              const typename TR::E *H, const typename TR::E *W,
+                              typename TR::Acc *zy, bool vec, typename TR::E *Ht, float *zero,
+                              int64_t zero_count, hipStream_t st, lce_timers *tm, int keep_loss) {
+  TimedLaunch tl(tm, LCE_K_GUARD, st);
+  hipLaunchKernelGGL(ctl_init_kernel, dim3(1), dim3(64), 0, st, ctl, keep_loss);
+  const int64_t row_blocks = cdiv(p.n, 256) < 1024 ? cdiv(p.n, 256) : 1024;
+  Prep<TR> a{};
+  a.y = y;
+  a.mask = mask;
+  a.n = p.n;
+  a.v_check = sh.total ? sh.total : p.V;
+  a.ctl = ctl;
+  a.offset = sh.total ? sh.offset : 0;
+  a.rows = p.V;
+  a.yl = sh.total ? reinterpret_cast<int64_t *>(ws + p.off_yloc) : nullptr;
+  a.H = H;
+  a.W = W;
+  a.D = p.D;
+  a.zy = zy;
+  a.vec8 = vec ? 1 : 0;
+  a.Ht = Ht;
+  a.ld = p.d_ld;
+  a.tr_cols = cdiv(p.d_ld, 64);
+  a.zero = zero;
+  a.zero_count = zero_count;
+  a.nb_guard = row_blocks;
+  a.nb_local = sh.total ? row_blocks : 0;
+  a.nb_zy = zy ? cdiv(p.n, 4) : 0;
+  a.nb_tr = Ht ? a.tr_cols * cdiv(p.D, 64) : 0;
+  a.nb_zero = zero ? (cdiv(zero_count, 256) < 4096 ? cdiv(zero_count, 256) : 4096) : 0;
+  hipLaunchKernelGGL(prep_kernel<TR>, dim3(unsigned(a.blocks())), dim3(256), 0, st, a);
+  return sh.total ? a.yl : y;
 }
 
 template <class TR>
@@ -867,13 +945,9 @@ static void forward_impl(const CEPlan &p, const void *H, const void *W, const in
   Acc *zy = reinterpret_cast<Acc *>(ws + p.off_zy);
   double *loss_tok = reinterpret_cast<double *>(ws + p.off_losstok);
   const typename TR::E *Hp = static_cast<const typename TR::E *>(H);
-  const int64_t *y = guard_targets(p, y_in, mask, sh, ctl, ws, st, tm, 0);
-  {
-    TimedLaunch tl(tm, LCE_K_FWD_MERGE, st);
-    hipLaunchKernelGGL(target_logit_kernel<TR>, dim3(unsigned(cdiv(p.n, 4))), dim3(256), 0, st,
-                       Hp, static_cast<const typename TR::E *>(W), y, p.n, p.D, zy,
-                       (const int32_t *)&ctl->bad, vec ? 1 : 0);
-  }
+  const int64_t *y =
+      prepare<TR>(p, y_in, mask, sh, ctl, ws, Hp, static_cast<const typename TR::E *>(W), zy, vec,
+                  nullptr, nullptr, 0, st, tm, 0);
   for (int64_t tok0 = 0; tok0 < p.n; tok0 += p.tok_per_pass) {
     const int64_t ntok = p.tok_per_pass < p.n - tok0 ? p.tok_per_pass : p.n - tok0;
     GemmParams g;
@@ -917,7 +991,8 @@ static void forward_impl(const CEPlan &p, const void *H, const void *W, const in
 // slab k-1 (from slab buffer (k-1) % 2) together with the logit gradient of
 // slab k (into buffer k % 2), longest products first.  Slab 0 may be shorter
 // than the rest (the plan sizes it to one round of CUs).  The d_hidden split
-// accumulators start at zero and every launch adds to them.
+// accumulators start at zero (prepare clears them) and every launch adds to
+// them.
 template <class TR, bool ACC_DW>
 static void backward_pipelined(const CEPlan &p, const uint16_t *Hp, const uint16_t *Wp,
                                const int64_t *y, const uint8_t *mask, const float *lse,
@@ -929,12 +1004,6 @@ static void backward_pipelined(const CEPlan &p, const uint16_t *Hp, const uint16
   typedef Gemm2Job<PipeKK, true, true, StoreEpi<TRP, ACC_DW>> JW;
   typedef Gemm2Job<PipeKK, true, true, DlogitEpi<TRP>> JL;
   const int64_t n = p.n, D = p.D, V = p.V, S = p.pslab, sp = p.pdh_splits;
-  {
-    const int64_t count = sp * n * D;
-    int64_t blocks = cdiv(count, 256);
-    if (blocks > 4096) blocks = 4096;
-    hipLaunchKernelGGL(zero_f32_kernel, dim3(unsigned(blocks)), dim3(256), 0, st, dhacc, count);
-  }
   const int64_t tiles_d = cdiv(D, 256), tiles_t = cdiv(n, 256);
   // first vocabulary row and row count of slab j
   auto slab_at = [&](int64_t j, int64_t &rows) {
@@ -1029,22 +1098,25 @@ static void backward_impl(const CEPlan &p, const void *H, const void *W, const i
   Acc *dhacc = reinterpret_cast<Acc *>(ws + p.off_dhacc);
   const E *Hp = static_cast<const E *>(H);
   const E *Wp = static_cast<const E *>(W);
-  const int64_t *y = guard_targets(p, y_in, mask, sh, ctl, ws, st, tm, 1);
   const bool pipe = UsePipe<TR>::ok(vec, p.D, p.d_ld);
   E *Ht = nullptr;
   Acc *zyb = nullptr;
+  float *zero = nullptr;
   if constexpr (IsH16<TR>::value) {
     if (pipe) {
       // K-major operands of the d_weight product: H^T and the slab buffer,
-      // both zero in token columns [n, d_ld).
-      // (The staged logit-gradient epilogue writes the slab buffer's zeros.)
+      // both zero in token columns [n, d_ld) (the staged logit-gradient
+      // epilogue writes the slab buffer's zeros); the target logits for that
+      // epilogue; the slab pipeline's d_hidden accumulators.
       Ht = reinterpret_cast<E *>(ws + p.off_ht);
-      const dim3 tg{unsigned(cdiv(p.d_ld, 64)), unsigned(cdiv(p.D, 64)), 1u};
-      hipLaunchKernelGGL(transpose_h_kernel, tg, dim3(256), 0, st, Hp, p.n, p.D, Ht, p.d_ld);
-      // target logits for the staged logit-gradient epilogue
       zyb = reinterpret_cast<Acc *>(ws + p.off_zyb);
-      hipLaunchKernelGGL(target_logit_kernel<TR>, dim3(unsigned(cdiv(p.n, 4))), dim3(256), 0, st,
-                         Hp, Wp, y, p.n, p.D, zyb, (const int32_t *)&ctl->bad, vec ? 1 : 0);
+      if (p.pslab > 0) zero = reinterpret_cast<float *>(dhacc);
+    }
+  }
+  const int64_t *y = prepare<TR>(p, y_in, mask, sh, ctl, ws, Hp, Wp, zyb, vec, Ht, zero,
+                                 p.pdh_splits * p.n * p.D, st, tm, 1);
+  if constexpr (IsH16<TR>::value) {
+    if (pipe) {
       if (p.pslab > 0) {
         if (accumulate)
           backward_pipelined<TR, true>(p, Hp, Wp, y, mask, lse, z_coef, grad_out, dW, dbuf,
