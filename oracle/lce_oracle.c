@@ -25,7 +25,7 @@
  *     count.
  *   - exp/log are the C library's.
  *
- * Readings taken where the pages are silent (each is listed in the design doc):
+ * Readings taken where the pages are silent:
  *   per-dimension ceilings n_tok <= 2^24, d_model <= 2^16, vocab <= 2^24;
  *   equality with a ceiling passes; mask value 1 = token counted, NULL mask =
  *   all counted; mean over counted tokens; all tokens masked -> zeros and ok;
