@@ -257,6 +257,64 @@ def f16_measure(lce, torch, np, dev, w, steps: int):
             "loss": out.loss_mean}
 
 
+def single_call_measure(lce, torch, np, dev, steps: int):
+    """lce_forward_backward (a batch of 512 tokens held in one chunk: the
+    logits are computed once and kept, 6nDV) against lce_forward +
+    lce_backward (8nDV) on the same bf16 inputs, at d_model 1024 and 4096 with
+    the 151936-row vocabulary, z 1e-4, 5% masked."""
+    from tests import synthetic as syn
+    out = []
+    for D in (1024, 4096):
+        n, V, chunk, z = 512, 151936, 512, 1e-4
+        log(f"bench: single call {n} x {D} x {V}: generating inputs")
+        x = syn.ce_inputs(syn.QWEN_BF16, n_tok=n, d_model=D, vocab=V, seed=7)
+        H, W = x.hidden.to(dev), x.weight.to(dev)
+        y = torch.from_numpy(x.targets).to(dev)
+        m = torch.from_numpy(syn.exact_mask(np.random.default_rng(7), n, 0.05)).to(dev)
+        lse = torch.empty(n, dtype=torch.float32, device=dev)
+        dH = torch.empty_like(H)
+        dW = torch.empty(V, D, dtype=torch.float32, device=dev)
+        ws1 = torch.empty(lce.lce_forward_backward_workspace_bytes(n, D, V, chunk, H.dtype),
+                          dtype=torch.uint8, device=dev)
+        ws2 = torch.empty(lce.lce_workspace_bytes(n, D, V, chunk, H.dtype), dtype=torch.uint8,
+                          device=dev)
+
+        def single():
+            st, _ = lce.lce_forward_backward(H, W, y, m, n, D, V, chunk, z, 1.0, lse, dH, dW, 0,
+                                             ws1, sync=False)
+            if st != lce.OK:
+                raise lce.LceError(st, "lce_forward_backward")
+
+        def two():
+            st, _ = lce.lce_forward(H, W, y, m, n, D, V, chunk, z, lse, ws2, sync=False)
+            if st != lce.OK:
+                raise lce.LceError(st, "lce_forward")
+            st = lce.lce_backward(H, W, y, m, lse, n, D, V, chunk, z, 1.0, dH, dW, 0, ws2)
+            if st != lce.OK:
+                raise lce.LceError(st, "lce_backward")
+
+        ms = {}
+        for name, f in (("single", single), ("two_calls", two)):
+            for _ in range(3):
+                f()
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            for _ in range(steps):
+                f()
+            torch.cuda.synchronize()
+            ms[name] = (time.perf_counter() - t0) / steps * 1e3
+        f2 = 2.0 * n * D * V
+        out.append({"n_tok": n, "d_model": D, "vocab": V, "chunk": chunk,
+                    "single_ms": round(ms["single"], 4), "two_calls_ms": round(ms["two_calls"], 4),
+                    "speedup": round(ms["two_calls"] / ms["single"], 4),
+                    "single_tflops_6ndv": round(3 * f2 / (ms["single"] / 1e3) / 1e12, 2),
+                    "two_calls_tflops_8ndv": round(4 * f2 / (ms["two_calls"] / 1e3) / 1e12, 2),
+                    "workspace_bytes": int(ws1.numel())})
+        del H, W, dW, ws1, ws2
+        torch.cuda.empty_cache()
+    return out
+
+
 def cpu_baseline(w, x, tokens: int):
     """The oracle, as it stands, on the first `tokens` tokens of the workload:
     forward (all tokens of the prefix) + backward (d_hidden of the prefix and
@@ -454,6 +512,10 @@ def main():
     if w.dtype == "bf16" and not (args.no_distill or args.no_shards):
         f16 = f16_measure(lce, torch, np, dev, w, args.steps)
 
+    single = None
+    if w.dtype == "bf16" and not (args.no_distill or args.no_shards):
+        single = single_call_measure(lce, torch, np, dev, args.steps)
+
     shard = None
     if w.dtype == "bf16" and not (args.no_distill or args.no_shards):
         log("bench: the same step in 4 vocabulary shards")
@@ -500,6 +562,7 @@ def main():
         "label_ce": label,
         "vocab_shards": shard,
         "f16_inputs": f16,
+        "single_call": single,
         "cpu_baseline": cpu,
     }
     print(json.dumps(res), flush=True)

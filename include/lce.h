@@ -138,6 +138,13 @@ int32_t lce_peak_cells(int64_t n_tok, int64_t vocab, int64_t chunk, lce_peak *ou
 int64_t lce_workspace_bytes(int64_t n_tok, int64_t d_model, int64_t vocab, int64_t chunk,
                             int32_t dtype);
 
+/* Bytes of device workspace lce_forward_backward needs (-status if refused):
+ * lce_workspace_bytes, or more when the call keeps the whole batch's logits
+ * (16-bit inputs and a chunk of at least the batch; still at most
+ * chunk*vocab logit cells). */
+int64_t lce_forward_backward_workspace_bytes(int64_t n_tok, int64_t d_model, int64_t vocab,
+                                             int64_t chunk, int32_t dtype);
+
 /* Bytes of device workspace lce_distill_fwd_bwd needs (-status if refused). */
 int64_t lce_distill_workspace_bytes(int64_t n_tok, int64_t vocab);
 
@@ -192,6 +199,32 @@ int32_t lce_backward(const lce_tensor *hidden, const lce_tensor *weight,
                      int64_t chunk, double z_coef, double grad_out, lce_tensor *d_hidden,
                      lce_tensor *d_weight, int32_t accumulate_d_weight,
                      lce_tensor *workspace, void *stream);
+
+/* Forward and backward in one call (lossk table: the flat forward and
+ * backward pair; Fast-LLM 566 fuses a label loss's forward and backward the
+ * same way): the loss scalars (out), lse_out and the gradients of
+ * grad_out * (loss_mean + z_coef * z_mean), with the arguments of
+ * lce_forward and lce_backward and one stream synchronization at the end.
+ *   workspace  numel >= lce_forward_backward_workspace_bytes(...)
+ *   out        host pointer (may be NULL: the scalars stay in the workspace,
+ *              lce_loss_fetch reads them)
+ * With 16-bit inputs and a chunk that holds the whole batch (chunk >= n_tok
+ * rounded up to 4, and up to 32 for tiny batches) the logits are computed
+ * once: kept in fp32 ([vocab][ld] cells, at most chunk*vocab), reduced to
+ * lse, turned in place into the logit gradient and fed to the d_hidden and
+ * d_weight products (6 n d_model vocab flops instead of 8).  The logit
+ * gradient has the same values as lce_backward's, so lse, the loss scalars
+ * and d_weight equal the two-call results bit for bit and d_hidden agrees to
+ * fp32 summation order.  Otherwise (fp64 inputs or a smaller chunk) the call
+ * runs lce_forward's and lce_backward's algorithm.  Status codes as
+ * lce_forward and lce_backward. */
+int32_t lce_forward_backward(const lce_tensor *hidden, const lce_tensor *weight,
+                             const lce_tensor *targets, const lce_tensor *loss_mask,
+                             int64_t n_tok, int64_t d_model, int64_t vocab, int64_t chunk,
+                             double z_coef, double grad_out, lce_tensor *lse_out,
+                             lce_tensor *d_hidden, lce_tensor *d_weight,
+                             int32_t accumulate_d_weight, lce_tensor *workspace, lce_loss *out,
+                             void *stream);
 
 /* Distillation against a teacher distribution, fused forward + backward,
  * with z-loss over the same student softmax (Fast-LLM 566, "What it does"
@@ -306,7 +339,8 @@ int32_t lce_ce_logits_fwd_bwd(const lce_tensor *logits, const lce_tensor *target
                              /* d_hidden and d_weight of slab k with the logit  */
                              /* gradient of slab k+1                            */
 #define LCE_K_LABEL_CE 10    /* label cross-entropy row kernel (logits in)      */
-#define LCE_NUM_KERNELS 11
+#define LCE_K_DLOGIT_ROWS 11 /* single call: kept logits -> logit gradient      */
+#define LCE_NUM_KERNELS 12
 
 /* One slot per kernel kind.  start/stop hold `capacity` caller-created
  * hipEvent_t handles (as void*); a timed call records start[i]/stop[i] on
@@ -324,7 +358,8 @@ typedef struct lce_timers {
   lce_timer_slot slot[LCE_NUM_KERNELS];
 } lce_timers;
 
-/* Same as lce_forward / lce_backward / lce_distill_fwd_bwd, recording
+/* Same as lce_forward / lce_backward / lce_forward_backward /
+ * lce_distill_fwd_bwd, recording
  * events into *timers (NULL = no timing, identical to the plain call). */
 int32_t lce_forward_timed(const lce_tensor *hidden, const lce_tensor *weight,
                           const lce_tensor *targets, const lce_tensor *loss_mask, int64_t n_tok,
@@ -337,6 +372,13 @@ int32_t lce_backward_timed(const lce_tensor *hidden, const lce_tensor *weight,
                            int64_t chunk, double z_coef, double grad_out, lce_tensor *d_hidden,
                            lce_tensor *d_weight, int32_t accumulate_d_weight,
                            lce_tensor *workspace, void *stream, lce_timers *timers);
+int32_t lce_forward_backward_timed(const lce_tensor *hidden, const lce_tensor *weight,
+                                   const lce_tensor *targets, const lce_tensor *loss_mask,
+                                   int64_t n_tok, int64_t d_model, int64_t vocab, int64_t chunk,
+                                   double z_coef, double grad_out, lce_tensor *lse_out,
+                                   lce_tensor *d_hidden, lce_tensor *d_weight,
+                                   int32_t accumulate_d_weight, lce_tensor *workspace,
+                                   lce_loss *out, void *stream, lce_timers *timers);
 int32_t lce_distill_fwd_bwd_timed(const lce_tensor *student, const lce_tensor *teacher,
                                   const lce_tensor *loss_mask, int64_t n_tok, int64_t vocab,
                                   int32_t objective, double temperature, double z_coef,

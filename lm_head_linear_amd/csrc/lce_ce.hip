@@ -669,6 +669,100 @@ __device__ __forceinline__ void transpose_h_block(const uint16_t *H, int64_t n, 
 }
 
 
+// Forward of the single-call path: the online-LSE partials (FwdLseEpi) and
+// the fp32 tile itself, kept at Z[v][t] (StoreEpi, row stride `ldo`).
+template <class TR>
+struct FwdKeepEpi {
+  FwdLseEpi<TR> lse;
+  StoreEpi<TR, false> keep;
+  static constexpr bool kStaged = true;
+  __device__ __forceinline__ void staged(typename TR::AccBlock (&acc)[TR::FM][TR::FN], int64_t m0,
+                                         int64_t n0, int wm, int wn, int lane, int,
+                                         char *lds, const char *pre) const {
+    lse(acc, m0, n0, wm, wn, lane, 0);
+    keep.staged(acc, m0, n0, wm, wn, lane, 0, lds, pre);
+  }
+};
+
+// Single-call path: row v of the kept logits Z (fp32, row stride ld) becomes
+// row v of the logit gradient, written over the same bytes as 16-bit values
+// with row stride 2 * ld.  Each value is formed as DlogitEpi forms it
+// (d = s * exp2(z log2(e) + c2), the target element from the target logit),
+// so the gradient equals the recomputing backward's; token columns
+// [n, round_up(n, 64)) get zeros (the d_weight product's K padding).  A wave
+// takes kDlogitRows consecutive rows and walks the tokens in ascending
+// segments of 64 * K: it forms the segment's per-token constants once, reads
+// the segment of every row, and only then writes them (the 16-bit values of
+// tokens [t0, t1) land on the fp32 bytes of tokens [t0 / 2, t1 / 2), all read
+// by then).
+constexpr int kDlogitRows = 4;
+template <class TR>
+__global__ void dlogit_rows_kernel(float *Z, int64_t V, int64_t n, int64_t ld,
+                                   const int64_t *y, const uint8_t *mask, const float *lse,
+                                   const float *zy, const Control *ctl, double grad_out,
+                                   double z_coef) {
+  if (ctl->bad) return;
+  constexpr int K = 8;
+  const float L2E = 1.4426950408889634f;
+  const int lane = threadIdx.x & 63;
+  const int64_t v0 = (int64_t(blockIdx.x) * (blockDim.x >> 6) + (threadIdx.x >> 6)) * kDlogitRows;
+  if (v0 >= V) return;
+  const int64_t C = ctl->count;
+  const float g = C ? float(grad_out / double(C)) : 0.f;
+  const float gz = C ? float(z_coef * grad_out / double(C)) : 0.f;
+  const int64_t tpad = (n + 63) / 64 * 64;
+  for (int64_t t0 = 0; t0 < tpad; t0 += 64 * K) {
+    float c2[K], gy[K];
+    uint32_t sb[K];
+    int64_t yt[K];
+#pragma unroll
+    for (int k = 0; k < K; ++k) {
+      const int64_t t = t0 + 64 * k + lane;
+      c2[k] = -INFINITY;   // tokens >= n: exp2(-inf) = 0
+      sb[k] = 0;
+      gy[k] = 0.f;
+      yt[k] = -1;
+      if (t < n) {
+        const float l = lse[t];
+        const bool counted = !mask || mask[t] != 0;
+        const float coef = counted ? g + 2.f * gz * l : 0.f;
+        c2[k] = __builtin_amdgcn_logf(fabsf(coef)) - l * L2E;
+        sb[k] = __float_as_uint(coef) & 0x80000000u;
+        yt[k] = y[t];
+        const float ey = __uint_as_float(
+            __float_as_uint(__builtin_amdgcn_exp2f(fmaf(zy[t], L2E, c2[k]))) ^ sb[k]);
+        gy[k] = ey - (counted ? g : 0.f);
+      }
+    }
+    // every row's segment in flight at once, then written
+    float z[kDlogitRows][K];
+#pragma unroll
+    for (int r = 0; r < kDlogitRows; ++r) {
+      const float *zr = Z + (v0 + r) * ld;
+#pragma unroll
+      for (int k = 0; k < K; ++k) {
+        const int64_t t = t0 + 64 * k + lane;
+        z[r][k] = (t < n && v0 + r < V) ? zr[t] : 0.f;
+      }
+    }
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // the segment of every row is read
+#pragma unroll
+    for (int r = 0; r < kDlogitRows; ++r) {
+      const int64_t v = v0 + r;
+      if (v >= V) break;
+      typename TR::E *dr = reinterpret_cast<typename TR::E *>(Z) + v * 2 * ld;
+#pragma unroll
+      for (int k = 0; k < K; ++k) {
+        const int64_t t = t0 + 64 * k + lane;
+        if (t >= tpad) continue;
+        const float e = __uint_as_float(
+            __float_as_uint(__builtin_amdgcn_exp2f(fmaf(z[r][k], L2E, c2[k]))) ^ sb[k]);
+        dr[t] = to_elem<TR>(yt[k] == v ? gy[k] : e);
+      }
+    }
+  }
+}
+
 // Per-call preparation in one launch.  Its parts do not read each other's
 // results, so they share a grid: blocks [0, nb_guard) run the target guard
 // and token count (ctl_init has run), then nb_local blocks the shard-local
@@ -1191,6 +1285,113 @@ static void backward_impl(const CEPlan &p, const void *H, const void *W, const i
                       st, tm);
 }
 
+
+// Forward and backward in one pass over the logits (16-bit inputs, the whole
+// batch in one chunk): the forward GEMM keeps its fp32 tiles in Z besides the
+// (max, sum) partials; after the merge gives lse, dlogit_rows_kernel turns Z
+// in place into the logit gradient, and one launch runs d_hidden (split over
+// the vocabulary) and d_weight from it.  6 n D V flops instead of 8.
+template <class TR>
+static void forward_backward_single(const CEPlan &p, const void *H, const void *W,
+                                    const int64_t *y, const uint8_t *mask, float *lse_out,
+                                    double z_coef, double grad_out, void *dH, float *dW,
+                                    int accumulate, uint8_t *ws, bool vec, hipStream_t st,
+                                    lce_timers *tm) {
+  typedef typename W8Of<TR>::type TRP;
+  typedef typename TR::E E;
+  const int64_t n = p.n, D = p.D, V = p.V, sp = p.f_sp;
+  Control *ctl = reinterpret_cast<Control *>(ws);
+  float *partials = reinterpret_cast<float *>(ws + p.off_partials);
+  float *zy = reinterpret_cast<float *>(ws + p.off_zy);
+  double *loss_tok = reinterpret_cast<double *>(ws + p.off_losstok);
+  float *Z = reinterpret_cast<float *>(ws + p.off_fz);
+  float *dhacc = reinterpret_cast<float *>(ws + p.off_fdh);
+  E *Ht = reinterpret_cast<E *>(ws + p.off_fht);
+  const E *Hp = static_cast<const E *>(H);
+  const E *Wp = static_cast<const E *>(W);
+  const Shard<float> whole;
+  prepare<TR>(p, y, mask, whole, ctl, ws, Hp, Wp, zy, vec, Ht, dhacc, sp * n * D, st, tm, 0);
+  const int64_t tiles_t = cdiv(n, 256), tiles_d = cdiv(D, 256);
+  {
+    GemmParams g;
+    g.A = Wp; g.lda = D;
+    g.B = Hp; g.ldb = D;
+    g.M = V; g.N = n; g.K = D;
+    g.M_read = V; g.N_read = n;
+    g.k_per_split = cdiv(D, PipeKK::BK) * PipeKK::BK;
+    g.tiles_n = tiles_t;
+    g.bad = &ctl->bad;
+    const FwdKeepEpi<TRP> e{FwdLseEpi<TRP>{n, V, p.n_vparts, partials},
+                            StoreEpi<TRP, false>{Z, p.f_ld, 0, V, n, 0}};
+    TimedLaunch tl(tm, LCE_K_FWD_GEMM, st);
+    hipLaunchKernelGGL((gemm2_kernel<PipeKK, TRP, true, true, FwdKeepEpi<TRP>>),
+                       dim3(unsigned(cdiv(V, 256) * tiles_t)), dim3(TRP::NT), 0, st,
+                       to_gemm2<PipeKK>(g), e);
+  }
+  {
+    TimedLaunch tl(tm, LCE_K_FWD_MERGE, st);
+    hipLaunchKernelGGL(fwd_merge_kernel<float>, dim3(unsigned(cdiv(n, 4))), dim3(256), 0, st,
+                       (const float *)partials, (const float *)zy, p.n_vparts, n, lse_out,
+                       loss_tok, (const int32_t *)&ctl->bad, (float *)nullptr, n);
+  }
+  {
+    TimedLaunch tl(tm, LCE_K_REDUCE, st);
+    hipLaunchKernelGGL(fwd_final_kernel<float>, dim3(1), dim3(1024), 0, st,
+                       (const double *)loss_tok, (const float *)lse_out, mask, n, ctl);
+  }
+  {
+    TimedLaunch tl(tm, LCE_K_DLOGIT_ROWS, st);
+    hipLaunchKernelGGL(dlogit_rows_kernel<TR>, dim3(unsigned(cdiv(V, 4 * kDlogitRows))), dim3(256),
+                       0, st, Z,
+                       V, n, p.f_ld, y, mask, (const float *)lse_out, (const float *)zy,
+                       (const Control *)ctl, grad_out, z_coef);
+  }
+  // d_hidden += d W over the whole vocabulary (split-K), d_weight = d^T H:
+  // the two products of a slab-pipeline launch, with the logit gradient in Z
+  // (16-bit values, row stride 2 * f_ld) as the one slab.
+  const uint16_t *buf = reinterpret_cast<const uint16_t *>(Z);
+  const int64_t ldd = 2 * p.f_ld;
+  auto launch = [&](auto acc_tag) {
+    constexpr bool ACC = decltype(acc_tag)::value;
+    typedef Gemm2Job<PipeMN, false, false, StoreEpi<TRP, true>> JH;
+    typedef Gemm2Job<PipeKK, true, true, StoreEpi<TRP, ACC>> JW;
+    typedef Gemm2Job<PipeKK, true, true, DlogitEpi<TRP>> JL;
+    JH jh{};
+    JW jw{};
+    JL jl{};
+    GemmParams g;
+    g.A = buf; g.lda = ldd;
+    g.B = Wp; g.ldb = D;
+    g.M = n; g.N = D; g.K = V;
+    g.M_read = p.d_ld; g.N_read = D;
+    g.k_per_split = cdiv(cdiv(V, sp), PipeMN::BK) * PipeMN::BK;
+    g.tiles_n = tiles_d;
+    g.bad = &ctl->bad;
+    jh.g = to_gemm2<PipeMN>(g);
+    jh.e = StoreEpi<TRP, true>{dhacc, D, 0, n, D, n * D};
+    jh.nreal = tiles_t * tiles_d * sp;
+    jh.nb = round_up8(jh.nreal);
+    GemmParams h;
+    h.A = buf; h.lda = ldd;
+    h.B = Ht; h.ldb = p.d_ld;
+    h.M = V; h.N = D; h.K = n;
+    h.M_read = V; h.N_read = D;
+    h.k_per_split = cdiv(n, PipeKK::BK) * PipeKK::BK;
+    h.tiles_n = tiles_d;
+    h.bad = &ctl->bad;
+    jw.g = to_gemm2<PipeKK>(h);
+    jw.e = StoreEpi<TRP, ACC>{dW, D, 0, V, D, 0};
+    jw.nreal = cdiv(V, 256) * tiles_d;
+    jw.nb = round_up8(jw.nreal);
+    TimedLaunch tl(tm, LCE_K_BWD_GEMM, st);
+    hipLaunchKernelGGL((gemm2_multi_kernel<TRP, JH, JW, JL>), dim3(unsigned(jh.nb + jw.nb)),
+                       dim3(TRP::NT), 0, st, jh, jw, jl);
+  };
+  if (accumulate) launch(std::true_type{});
+  else launch(std::false_type{});
+  launch_dh_final<TR>(dhacc, sp, n * D, dH, false, (const int32_t *)&ctl->bad, st, tm);
+}
+
 }  // namespace lce
 
 using namespace lce;
@@ -1532,3 +1733,113 @@ int32_t backward_call(const lce_tensor *hidden, const lce_tensor *weight,
 }
 
 }  // namespace
+
+namespace {
+
+int32_t forward_backward_call(const lce_tensor *hidden, const lce_tensor *weight,
+                              const lce_tensor *targets, const lce_tensor *loss_mask,
+                              int64_t n_tok, int64_t d_model, int64_t vocab, int64_t chunk,
+                              double z_coef, double grad_out, lce_tensor *lse_out,
+                              lce_tensor *d_hidden, lce_tensor *d_weight,
+                              int32_t accumulate_d_weight, lce_tensor *workspace, lce_loss *out,
+                              void *stream, lce_timers *timers) {
+  int32_t st = lce_dims_check(n_tok, d_model, vocab);
+  if (st != LCE_OK) return st;
+  st = lce_chunk_check(chunk, vocab);
+  if (st != LCE_OK) return st;
+  if (!finite_scalar(z_coef) || !finite_scalar(grad_out)) return LCE_NON_FINITE_SCALAR;
+  int32_t dt = 0;
+  st = check_ce_tensors(hidden, weight, targets, loss_mask, n_tok, d_model, vocab, &dt);
+  if (st != LCE_OK) return st;
+  if (!lse_out || !d_hidden || !d_weight || !workspace) return LCE_LENGTH_MISMATCH;
+  const int32_t acc_dt = dt == LCE_F64 ? LCE_F64 : LCE_F32;
+  if (lse_out->dtype != acc_dt || d_weight->dtype != acc_dt || d_hidden->dtype != dt)
+    return LCE_DTYPE_MISMATCH;
+  if (workspace->dtype != LCE_U8) return LCE_DTYPE_MISMATCH;
+  CEPlan p;
+  st = plan_ce(n_tok, d_model, vocab, chunk, dt, &p);
+  if (st != LCE_OK) return st;
+  st = check_ce_lengths(hidden, weight, targets, loss_mask, n_tok, d_model, vocab);
+  if (st != LCE_OK) return st;
+  if (!has(lse_out) || lse_out->numel < n_tok) return LCE_LENGTH_MISMATCH;
+  if (!has(d_hidden) || d_hidden->numel < n_tok * d_model) return LCE_LENGTH_MISMATCH;
+  if (!has(d_weight) || d_weight->numel < vocab * d_model) return LCE_LENGTH_MISMATCH;
+  if (!has(workspace) || workspace->numel < int64_t(p.f_total) + 256) return LCE_LENGTH_MISMATCH;
+
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  uint8_t *ws = ws_base(workspace);
+  const uint8_t *mask = has(loss_mask) ? static_cast<const uint8_t *>(loss_mask->data) : nullptr;
+  const int64_t *y = static_cast<const int64_t *>(targets->data);
+  const bool acc = accumulate_d_weight != 0;
+  (void)hipGetLastError();
+  if (dt != LCE_F64) {
+    const bool vec = d_model % 8 == 0 && aligned16(hidden->data) && aligned16(weight->data) &&
+                     aligned16(d_weight->data);
+    float *l = static_cast<float *>(lse_out->data);
+    float *dw = static_cast<float *>(d_weight->data);
+    const Shard<float> whole;
+    // the kept logits' 16-bit rows (stride 2 f_ld) must suit the pipelined core
+    const bool single = p.f_ok && UsePipe<TraitsBF16>::ok(vec, d_model, 2 * p.f_ld) &&
+                        UsePipe<TraitsBF16>::ok(vec, d_model, p.d_ld);
+    if (single) {
+      if (dt == LCE_F16)
+        forward_backward_single<TraitsF16>(p, hidden->data, weight->data, y, mask, l, z_coef,
+                                           grad_out, d_hidden->data, dw, acc, ws, vec, s, timers);
+      else
+        forward_backward_single<TraitsBF16>(p, hidden->data, weight->data, y, mask, l, z_coef,
+                                            grad_out, d_hidden->data, dw, acc, ws, vec, s, timers);
+    } else if (dt == LCE_F16) {
+      forward_impl<TraitsF16>(p, hidden->data, weight->data, y, mask, l, ws, vec, s, timers, whole);
+      backward_impl<TraitsF16>(p, hidden->data, weight->data, y, mask, l, z_coef, grad_out,
+                               d_hidden->data, false, dw, acc, ws, vec, s, timers, whole);
+    } else {
+      forward_impl<TraitsBF16>(p, hidden->data, weight->data, y, mask, l, ws, vec, s, timers,
+                               whole);
+      backward_impl<TraitsBF16>(p, hidden->data, weight->data, y, mask, l, z_coef, grad_out,
+                                d_hidden->data, false, dw, acc, ws, vec, s, timers, whole);
+    }
+  } else {
+    const bool vec = d_model % 2 == 0 && aligned16(hidden->data) && aligned16(weight->data);
+    double *l = static_cast<double *>(lse_out->data);
+    const Shard<double> whole;
+    forward_impl<TraitsF64>(p, hidden->data, weight->data, y, mask, l, ws, vec, s, timers, whole);
+    backward_impl<TraitsF64>(p, hidden->data, weight->data, y, mask, l, z_coef, grad_out,
+                             d_hidden->data, false, static_cast<double *>(d_weight->data), acc,
+                             ws, vec, s, timers, whole);
+  }
+  Control hc;
+  st = finish(s, reinterpret_cast<Control *>(ws), &hc);
+  if (st != LCE_OK) return st;
+  if (out) fill_loss(hc, out);
+  return LCE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t lce_forward_backward(const lce_tensor *hidden, const lce_tensor *weight,
+                             const lce_tensor *targets, const lce_tensor *loss_mask,
+                             int64_t n_tok, int64_t d_model, int64_t vocab, int64_t chunk,
+                             double z_coef, double grad_out, lce_tensor *lse_out,
+                             lce_tensor *d_hidden, lce_tensor *d_weight,
+                             int32_t accumulate_d_weight, lce_tensor *workspace, lce_loss *out,
+                             void *stream) {
+  return forward_backward_call(hidden, weight, targets, loss_mask, n_tok, d_model, vocab, chunk,
+                               z_coef, grad_out, lse_out, d_hidden, d_weight, accumulate_d_weight,
+                               workspace, out, stream, nullptr);
+}
+
+int32_t lce_forward_backward_timed(const lce_tensor *hidden, const lce_tensor *weight,
+                                   const lce_tensor *targets, const lce_tensor *loss_mask,
+                                   int64_t n_tok, int64_t d_model, int64_t vocab, int64_t chunk,
+                                   double z_coef, double grad_out, lce_tensor *lse_out,
+                                   lce_tensor *d_hidden, lce_tensor *d_weight,
+                                   int32_t accumulate_d_weight, lce_tensor *workspace,
+                                   lce_loss *out, void *stream, lce_timers *timers) {
+  return forward_backward_call(hidden, weight, targets, loss_mask, n_tok, d_model, vocab, chunk,
+                               z_coef, grad_out, lse_out, d_hidden, d_weight, accumulate_d_weight,
+                               workspace, out, stream, timers);
+}
+
+}  // extern "C"

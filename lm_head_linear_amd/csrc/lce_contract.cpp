@@ -198,6 +198,34 @@ int32_t plan_ce(int64_t n, int64_t D, int64_t V, int64_t chunk, int32_t dtype, C
   off = off > fwd_end ? off : fwd_end;
   q.off_yloc = off;
   q.total = align256(off + size_t(n) * sizeof(int64_t));
+
+  // Single-call layout: the forward region, then the kept logits, the d_hidden
+  // split accumulators and H^T, all live at once.  The logits take V * f_ld
+  // cells (at most chunk*vocab); f_ld also covers, at two 16-bit values per
+  // cell, the gradient rows zero-padded to a multiple of 64 tokens.
+  q.f_total = q.total;
+  if (bf) {
+    int64_t fld = round_up(n, 4);
+    if (2 * fld < round_up(n, 64)) fld = round_up(n, 64) / 2;
+    if (fld <= chunk && q.tok_per_pass >= n) {
+      q.f_ok = true;
+      q.f_ld = fld;
+      int64_t sp = ceil_div(kComputeUnits, out_tiles);
+      if (sp > V / 512) sp = V / 512;
+      if (sp > 32) sp = 32;
+      q.f_sp = sp < 1 ? 1 : sp;
+      size_t o = fwd_end;
+      q.off_fz = o;
+      o = align256(o + size_t(V) * size_t(fld) * 4);
+      q.off_fdh = o;
+      o = align256(o + size_t(q.f_sp) * size_t(n) * size_t(D) * 4);
+      q.off_fht = o;
+      o = align256(o + size_t(D) * size_t(q.d_ld) * 2);
+      q.off_fyloc = o;
+      o = align256(o + size_t(n) * sizeof(int64_t));
+      if (o > q.f_total) q.f_total = o;
+    }
+  }
   *p = q;
   return LCE_OK;
 }
@@ -275,6 +303,14 @@ int64_t lce_workspace_bytes(int64_t n_tok, int64_t d_model, int64_t vocab, int64
   int32_t st = plan_ce(n_tok, d_model, vocab, chunk, dtype, &p);
   if (st != LCE_OK) return -int64_t(st);
   return int64_t(p.total) + 256;  // slack: the library aligns the base to 256 bytes
+}
+
+int64_t lce_forward_backward_workspace_bytes(int64_t n_tok, int64_t d_model, int64_t vocab,
+                                             int64_t chunk, int32_t dtype) {
+  CEPlan p;
+  int32_t st = plan_ce(n_tok, d_model, vocab, chunk, dtype, &p);
+  if (st != LCE_OK) return -int64_t(st);
+  return int64_t(p.f_total) + 256;
 }
 
 int64_t lce_distill_workspace_bytes(int64_t n_tok, int64_t vocab) {

@@ -58,6 +58,14 @@ struct CEPlan {
   size_t off_zyb = 0;         // bf16: target logits for the backward; 0 bytes for fp64
   size_t off_yloc = 0;        // [n] int64 shard-local target ids (shard calls)
   size_t total = 0;
+  // Single-call forward+backward (16-bit inputs, every token in one chunk):
+  // the logits of the whole batch are kept, [V][f_ld] fp32, and turned in
+  // place into the bf16/fp16 logit gradient with row stride 2 * f_ld.
+  bool f_ok = false;
+  int64_t f_ld = 0;           // fp32 logit row stride (tokens)
+  int64_t f_sp = 0;           // d_hidden split count (the reduction runs over all V)
+  size_t off_fz = 0, off_fdh = 0, off_fht = 0, off_fyloc = 0;
+  size_t f_total = 0;         // workspace of the single call (>= total)
 };
 
 // Fills *p; returns LCE_OK or a refusal status.

@@ -44,10 +44,10 @@ class Peak(ctypes.Structure):
                 ("status", ctypes.c_int32)]
 
 
-NUM_KERNELS = 11
+NUM_KERNELS = 12
 KERNEL_KINDS = {"guard": 0, "fwd_gemm": 1, "fwd_merge": 2, "reduce": 3, "dlogit_gemm": 4,
                 "dw_gemm": 5, "dh_gemm": 6, "dh_final": 7, "distill": 8, "bwd_gemm": 9,
-                "label_ce": 10}
+                "label_ce": 10, "dlogit_rows": 11}
 
 
 class TimerSlot(ctypes.Structure):
@@ -136,6 +136,8 @@ def lib():
         L.lce_workspace_bytes.argtypes = [i64, i64, i64, i64, i32]
         L.lce_distill_workspace_bytes.restype = i64
         L.lce_distill_workspace_bytes.argtypes = [i64, i64]
+        L.lce_forward_backward_workspace_bytes.restype = i64
+        L.lce_forward_backward_workspace_bytes.argtypes = [i64, i64, i64, i64, i32]
         L.lce_forward.restype = i32
         L.lce_forward.argtypes = [PT, PT, PT, PT, i64, i64, i64, i64, dbl, PT, PT,
                                   ctypes.POINTER(Loss), vp]
@@ -158,6 +160,11 @@ def lib():
         L.lce_shard_backward.argtypes = [PT, PT, PT, PT, PT, i64, i64, i64, i64, i64, i64, dbl,
                                          dbl, PT, PT, i32, PT, vp]
         PTM = ctypes.POINTER(Timers)
+        L.lce_forward_backward.restype = i32
+        L.lce_forward_backward.argtypes = [PT, PT, PT, PT, i64, i64, i64, i64, dbl, dbl, PT, PT,
+                                           PT, i32, PT, ctypes.POINTER(Loss), vp]
+        L.lce_forward_backward_timed.restype = i32
+        L.lce_forward_backward_timed.argtypes = L.lce_forward_backward.argtypes + [PTM]
         L.lce_forward_timed.restype = i32
         L.lce_forward_timed.argtypes = L.lce_forward.argtypes + [PTM]
         L.lce_backward_timed.restype = i32
@@ -219,6 +226,12 @@ def lce_workspace_bytes(n_tok: int, d_model: int, vocab: int, chunk: int, dtype)
 
 def lce_distill_workspace_bytes(n_tok: int, vocab: int) -> int:
     return lib().lce_distill_workspace_bytes(n_tok, vocab)
+
+
+def lce_forward_backward_workspace_bytes(n_tok: int, d_model: int, vocab: int, chunk: int,
+                                         dtype) -> int:
+    dt = _DT[dtype] if isinstance(dtype, torch.dtype) else int(dtype)
+    return lib().lce_forward_backward_workspace_bytes(n_tok, d_model, vocab, chunk, dt)
 
 
 # ------------------------------------------------------------ device calls
@@ -342,6 +355,27 @@ def lce_shard_backward(hidden, weight_shard, targets, loss_mask, lse, n_tok, d_m
 
 # ------------------------------------------------- allocating conveniences
 
+def lce_forward_backward(hidden, weight, targets, loss_mask, n_tok, d_model, vocab, chunk,
+                         z_coef, grad_out, lse_out, d_hidden, d_weight, accumulate_d_weight,
+                         workspace, stream: Optional[int] = None,
+                         timer: Optional[KernelTimer] = None, sync: bool = True):
+    """Direct call of the C entry point (lce_forward_backward_timed when a
+    timer is given).  Returns (status, Loss or None when sync is False)."""
+    out = Loss() if sync else None
+    ts = [_t(hidden), _t(weight), _t(targets), _t(loss_mask)]
+    lse_t, dh, dw, ws = _t(lse_out), _t(d_hidden), _t(d_weight), _t(workspace)
+    call = [*[ctypes.byref(a) for a in ts], n_tok, d_model, vocab, chunk, float(z_coef),
+            float(grad_out), ctypes.byref(lse_t), ctypes.byref(dh), ctypes.byref(dw),
+            int(bool(accumulate_d_weight)), ctypes.byref(ws),
+            ctypes.byref(out) if sync else None,
+            stream if stream is not None else _stream(hidden.device)]
+    if timer is None:
+        st = lib().lce_forward_backward(*call)
+    else:
+        st = lib().lce_forward_backward_timed(*call, ctypes.byref(timer.struct))
+    return st, out
+
+
 def _acc_dtype(dt: torch.dtype) -> torch.dtype:
     return torch.float64 if dt == torch.float64 else torch.float32
 
@@ -387,6 +421,28 @@ def backward(hidden, weight, targets, lse, loss_mask=None, chunk=256, z_coef=0.0
     if st != OK:
         raise LceError(st, "lce_backward")
     return dh, dw
+
+
+def forward_backward(hidden, weight, targets, loss_mask=None, chunk=256, z_coef=0.0,
+                     grad_out=1.0, d_weight=None, accumulate=False, workspace=None):
+    """Allocate lse, d_hidden, d_weight (unless given) and the workspace, call
+    lce_forward_backward.  Returns (ForwardResult, d_hidden, d_weight)."""
+    n, D = hidden.shape
+    V = weight.shape[0]
+    acc = _acc_dtype(hidden.dtype)
+    lse = torch.empty(n, dtype=acc, device=hidden.device)
+    dh = torch.empty_like(hidden)
+    dw = d_weight if d_weight is not None else torch.empty(V, D, dtype=acc, device=hidden.device)
+    if workspace is None:
+        nbytes = lce_forward_backward_workspace_bytes(n, D, V, chunk, hidden.dtype)
+        if nbytes < 0:
+            raise LceError(int(-nbytes), "lce_forward_backward_workspace_bytes")
+        workspace = torch.empty(nbytes, dtype=torch.uint8, device=hidden.device)
+    st, out = lce_forward_backward(hidden, weight, targets, loss_mask, n, D, V, chunk, z_coef,
+                                   grad_out, lse, dh, dw, accumulate, workspace)
+    if st != OK:
+        raise LceError(st, "lce_forward_backward")
+    return ForwardResult(out.as_dict(), lse), dh, dw
 
 
 def distill(student, teacher, loss_mask=None, objective=0, temperature=1.0, z_coef=0.0,

@@ -84,6 +84,33 @@ def test_workspace_monotone_and_bounded(n, D, V, chunk):
         assert b > 0
 
 
+def test_single_call_workspace():
+    """lce_forward_backward keeps the batch's logits only when a 16-bit batch
+    fits one chunk; the kept logits take at most chunk*vocab fp32 cells."""
+    f = lce.lce_forward_backward_workspace_bytes
+    # the headline (chunk 256 < 2048 tokens): the two-call workspace
+    for dt in (lce.BF16, lce.F16, lce.F64):
+        assert f(2048, 1024, 151936, 256, dt) == lce.lce_workspace_bytes(2048, 1024, 151936, 256,
+                                                                          dt)
+    # fp64 never keeps logits
+    assert f(512, 1024, 151936, 512, lce.F64) == lce.lce_workspace_bytes(512, 1024, 151936, 512,
+                                                                          lce.F64)
+    for n, D, V, chunk in [(512, 1024, 151936, 512), (300, 192, 3000, 300), (1, 64, 33, 32),
+                           (517, 256, 2100, 600)]:
+        single, two = f(n, D, V, chunk, lce.BF16), lce.lce_workspace_bytes(n, D, V, chunk,
+                                                                           lce.BF16)
+        assert single > two
+        sp = 64
+        extra = 4 * V * chunk + 4 * sp * n * D + 2 * D * (n + 63) // 64 * 64 + 8 * n + 5 * 256
+        assert single <= two + extra
+    # a batch one row larger than the chunk goes the two-call way
+    assert f(301, 192, 3000, 300, lce.BF16) == lce.lce_workspace_bytes(301, 192, 3000, 300,
+                                                                        lce.BF16)
+    assert f(2048, 1024, 151936, 1024, lce.BF16) == -587
+    assert f(0, 1024, 151936, 256, lce.BF16) == -581
+    assert f(64, 64, 1000, 64, lce.F32) == -590
+
+
 def test_loss_fetch_refuses_short_workspace_without_device():
     ws = torch.zeros(100, dtype=torch.uint8)
     assert lce.lce_loss_fetch(ws, stream=0)[0] == 582
