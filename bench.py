@@ -349,6 +349,9 @@ def main():
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only copy MIB MiB device-to-device twice and exit (the known-size "
                          "reference for the FETCH_SIZE / WRITE_SIZE counters)")
+    ap.add_argument("--single-call-only", action="store_true",
+                    help="only time lce_forward_backward against the two calls (512 tokens, "
+                         "d_model 1024 and 4096) and print that record")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-kernel-events", action="store_true")
     ap.add_argument("--no-shards", action="store_true",
@@ -364,6 +367,13 @@ def main():
 
     import numpy as np
     import torch
+
+    if args.single_call_only:
+        from lm_head_linear_amd import lce
+        lce.lib()
+        res = single_call_measure(lce, torch, np, torch.device("cuda:0"), args.steps)
+        print(json.dumps({"single_call": res}), flush=True)
+        return
 
     if args.copy_calibration:
         nbytes = args.copy_calibration << 20
