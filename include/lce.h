@@ -208,9 +208,9 @@ int32_t lce_backward(const lce_tensor *hidden, const lce_tensor *weight,
  *   workspace  numel >= lce_forward_backward_workspace_bytes(...)
  *   out        host pointer (may be NULL: the scalars stay in the workspace,
  *              lce_loss_fetch reads them)
- * With 16-bit inputs and a chunk that holds the whole batch (chunk >= n_tok
- * rounded up to 4, and up to 32 for tiny batches) the logits are computed
- * once: kept in fp32 ([vocab][ld] cells, at most chunk*vocab), reduced to
+ * With 16-bit inputs and a chunk that holds the whole batch (chunk >=
+ * max(n_tok rounded up to 4, n_tok rounded up to 64 / 2)) the logits are
+ * computed once: kept in fp32 ([vocab][ld] cells, at most chunk*vocab), reduced to
  * lse, turned in place into the logit gradient and fed to the d_hidden and
  * d_weight products (6 n d_model vocab flops instead of 8).  The logit
  * gradient has the same values as lce_backward's, so lse, the loss scalars
