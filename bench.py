@@ -3,17 +3,23 @@
 Default workload: the Qwen3-0.6B-shaped LM head, 2048 tokens x d_model 1024 x
 vocab 151936, bf16 inputs with fp32 accumulation, chunk 256, z-loss 1e-4, 5%
 of tokens masked, synthetic seeded inputs already resident in HBM.  One step
-= lce_forward (asynchronous: no host round trip) + lce_backward (target guard,
-its status synchronization included), as a training loop makes them; the loss
-scalars are read back once after the timed steps (lce_loss_fetch).  Prints
-one JSON line.
+= lce_forward + lce_backward as a training loop makes them; neither call waits
+for the device, and the loss scalars and the target guard's verdict are read
+back once after the timed steps (lce_loss_fetch).  Prints one JSON line.
 
 Timing: the K timed steps run with nothing recorded between kernels (value,
-ms_per_step).  A second pass repeats the K steps with HIP events that the
+ms_per_step, from the host clock around the K steps and a final sync); a
+per-step pass records an event between consecutive steps (step_ms_median,
+step_ms_min).  A third pass repeats the K steps with HIP events that the
 library records around every kernel launch on the launch stream
 (lce_forward_timed / lce_backward_timed); those give the per-kind kernel
 durations and roofline.achieved.  Events add idle time between kernels, so
 that pass never feeds the step time.
+
+Side records (default run): fp16 inputs, the single call, vocabulary shards,
+the fp64 chunk sweep (128/256/512, and 1024 refused with 587), the
+8192 x 4096 x 128256 head, distillation and label CE throughput, and a
+practical MFMA ceiling (hipBLASLt on 8192^3 with the sampled clock).
 """
 from __future__ import annotations
 
@@ -257,15 +263,123 @@ def f16_measure(lce, torch, np, dev, w, steps: int):
             "loss": out.loss_mean}
 
 
+def step_runner(lce, w, H, W, y, m, lse, dH, dW, ws, grad_out=1.0):
+    n, D = H.shape
+    V = W.shape[0]
+
+    def step(timer=None):
+        st, _ = lce.lce_forward(H, W, y, m, n, D, V, w.chunk, w.z_coef, lse, ws, timer=timer,
+                                sync=False)
+        if st != lce.OK:
+            raise lce.LceError(st, "lce_forward")
+        st = lce.lce_backward(H, W, y, m, lse, n, D, V, w.chunk, w.z_coef, grad_out, dH, dW, 0,
+                              ws, timer=timer)
+        if st != lce.OK:
+            raise lce.LceError(st, "lce_backward")
+    return step
+
+
+def per_step_ms(torch, step, steps: int):
+    """Device time of each of `steps` steps (events between steps only)."""
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+    ev[0].record()
+    for i in range(steps):
+        step()
+        ev[i + 1].record()
+    torch.cuda.synchronize()
+    return [ev[i].elapsed_time(ev[i + 1]) for i in range(steps)]
+
+
+def f64_sweep_measure(lce, torch, np, dev, steps: int):
+    """The 2048 x 1024 x 151936 head in fp64 at chunk 128, 256 and 512 (step
+    time, loss bit-identical across chunks) and chunk 1024, which the
+    chunk*vocab budget refuses (587) before any work."""
+    import dataclasses
+    from tests import synthetic as syn
+    w0 = syn.QWEN_F64
+    log(f"bench: fp64 chunk sweep {w0.name}: generating inputs")
+    x = syn.ce_inputs(w0)
+    n, D, V = w0.n_tok, w0.d_model, w0.vocab
+    H, W = x.hidden.to(dev), x.weight.to(dev)
+    y = torch.from_numpy(x.targets).to(dev)
+    lse = torch.empty(n, dtype=torch.float64, device=dev)
+    dH = torch.empty_like(H)
+    dW = torch.empty(V, D, dtype=torch.float64, device=dev)
+    flops = 8.0 * n * D * V
+    res = {"workload": w0.name, "peak_tflops": PEAK_F64_TFLOPS, "chunks": {}}
+    losses = []
+    for chunk in (128, 256, 512, 1024):
+        nb = lce.lce_workspace_bytes(n, D, V, chunk, torch.float64)
+        if nb < 0:
+            st, _ = lce.lce_forward(H, W, y, None, n, D, V, chunk, 0.0, lse,
+                                    torch.empty(1024, dtype=torch.uint8, device=dev))
+            res["chunks"][str(chunk)] = {"status": int(-nb), "forward_status": int(st)}
+            continue
+        ws = torch.empty(nb, dtype=torch.uint8, device=dev)
+        step = step_runner(lce, dataclasses.replace(w0, chunk=chunk), H, W, y, None, lse, dH, dW,
+                           ws)
+        step()
+        torch.cuda.synchronize()
+        t = per_step_ms(torch, step, steps)
+        st, out = lce.lce_loss_fetch(ws)
+        losses.append(out.loss_mean)
+        med = float(np.median(t))
+        res["chunks"][str(chunk)] = {
+            "status": int(st), "ms_median": round(med, 3), "ms_min": round(float(np.min(t)), 3),
+            "tflops_8ndv": round(flops / (med / 1e3) / 1e12, 2),
+            "frac_8ndv": round(flops / (med / 1e3) / 1e12 / PEAK_F64_TFLOPS, 4),
+            "loss": out.loss_mean, "workspace_bytes": nb}
+        del ws
+    res["loss_bit_identical_across_chunks"] = len(set(losses)) == 1
+    del H, W, dW, dH
+    torch.cuda.empty_cache()
+    return res
+
+
+def large_head_measure(lce, torch, np, dev, steps: int):
+    """The 8192 x 4096 x 128256 bf16 head (Zipf targets, chunk 512, z
+    1e-4): the same step as the headline, per-step device time."""
+    from tests import synthetic as syn
+    w = syn.LARGE_BF16
+    log(f"bench: {w.name}: generating inputs")
+    x = syn.ce_inputs(w)
+    n, D, V = w.n_tok, w.d_model, w.vocab
+    H, W = x.hidden.to(dev), x.weight.to(dev)
+    y = torch.from_numpy(x.targets).to(dev)
+    lse = torch.empty(n, dtype=torch.float32, device=dev)
+    dH = torch.empty_like(H)
+    dW = torch.empty(V, D, dtype=torch.float32, device=dev)
+    ws = torch.empty(lce.lce_workspace_bytes(n, D, V, w.chunk, H.dtype), dtype=torch.uint8,
+                     device=dev)
+    step = step_runner(lce, w, H, W, y, None, lse, dH, dW, ws)
+    for _ in range(2):
+        step()
+    torch.cuda.synchronize()
+    t = per_step_ms(torch, step, steps)
+    st, out = lce.lce_loss_fetch(ws)
+    med = float(np.median(t))
+    flops = 8.0 * n * D * V
+    res = {"workload": w.name, "status": int(st), "ms_median": round(med, 3),
+           "ms_min": round(float(np.min(t)), 3), "tokens_per_s": round(n / (med / 1e3), 1),
+           "tflops_8ndv": round(flops / (med / 1e3) / 1e12, 2),
+           "mfma_frac_8ndv": round(flops / (med / 1e3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+           "mfma_frac_6ndv": round(0.75 * flops / (med / 1e3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+           "loss": out.loss_mean}
+    del H, W, dW, dH, ws
+    torch.cuda.empty_cache()
+    return res
+
+
 def single_call_measure(lce, torch, np, dev, steps: int):
-    """lce_forward_backward (a batch of 512 tokens held in one chunk: the
-    logits are computed once and kept, 6nDV) against lce_forward +
-    lce_backward (8nDV) on the same bf16 inputs, at d_model 1024 and 4096 with
-    the 151936-row vocabulary, z 1e-4, 5% masked."""
+    """lce_forward_backward (the whole batch in one chunk) against
+    lce_forward + lce_backward (8nDV) on the same bf16 inputs with the
+    151936-row vocabulary, z 1e-4, 5% masked.  Where the call's cost model
+    keeps the logits it does 6nDV; elsewhere it runs the two-call algorithm
+    (keeps_logits 0)."""
     from tests import synthetic as syn
     out = []
-    for D in (1024, 4096):
-        n, V, chunk, z = 512, 151936, 512, 1e-4
+    for n, D in ((256, 1024), (512, 1024), (512, 4096)):
+        V, chunk, z = 151936, n, 1e-4
         log(f"bench: single call {n} x {D} x {V}: generating inputs")
         x = syn.ce_inputs(syn.QWEN_BF16, n_tok=n, d_model=D, vocab=V, seed=7)
         H, W = x.hidden.to(dev), x.weight.to(dev)
@@ -305,6 +419,8 @@ def single_call_measure(lce, torch, np, dev, steps: int):
             ms[name] = (time.perf_counter() - t0) / steps * 1e3
         f2 = 2.0 * n * D * V
         out.append({"n_tok": n, "d_model": D, "vocab": V, "chunk": chunk,
+                    "keeps_logits": lce.lce_forward_backward_keeps_logits(n, D, V, chunk,
+                                                                          H.dtype),
                     "single_ms": round(ms["single"], 4), "two_calls_ms": round(ms["two_calls"], 4),
                     "speedup": round(ms["two_calls"] / ms["single"], 4),
                     "single_tflops_6ndv": round(3 * f2 / (ms["single"] / 1e3) / 1e12, 2),
@@ -312,6 +428,131 @@ def single_call_measure(lce, torch, np, dev, steps: int):
                     "workspace_bytes": int(ws1.numel())})
         del H, W, dW, ws1, ws2
         torch.cuda.empty_cache()
+    return out
+
+
+def cpu_model_name() -> str:
+    """The host CPU's model name from /proc/cpuinfo ("unknown" if absent)."""
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+class ClockSampler:
+    """Samples the GPU's current graphics clock (MHz) and socket power (W)
+    through amdsmi from a background thread while the caller keeps the GPU
+    busy; best effort (no samples when amdsmi cannot be initialised)."""
+
+    def __init__(self, period_s: float = 0.005):
+        import threading
+        self.period = period_s
+        self.clk, self.power = [], []
+        self._stop = threading.Event()
+        self._thread = None
+        self.error = None
+        try:
+            import amdsmi
+            amdsmi.amdsmi_init()
+            self._smi = amdsmi
+            self._h = amdsmi.amdsmi_get_processor_handles()[0]
+        except Exception as e:          # noqa: BLE001 - optional telemetry
+            self._smi = None
+            self.error = f"{type(e).__name__}: {e}"
+
+    def _run(self):
+        smi = self._smi
+        while not self._stop.is_set():
+            try:
+                c = smi.amdsmi_get_clock_info(self._h, smi.AmdSmiClkType.GFX)
+                self.clk.append(float(c.get("clk", c.get("cur_clk", 0))))
+            except Exception as e:      # noqa: BLE001
+                self.error = f"{type(e).__name__}: {e}"
+                return
+            try:
+                p = smi.amdsmi_get_power_info(self._h)
+                v = p.get("current_socket_power", p.get("average_socket_power"))
+                if isinstance(v, (int, float)):
+                    self.power.append(float(v))
+            except Exception:           # noqa: BLE001
+                pass
+            time.sleep(self.period)
+
+    def __enter__(self):
+        import threading
+        if self._smi is not None:
+            self._thread = threading.Thread(target=self._run, daemon=True)
+            self._thread.start()
+        return self
+
+    def __exit__(self, *exc):
+        self._stop.set()
+        if self._thread is not None:
+            self._thread.join()
+        if self._smi is not None:
+            try:
+                self._smi.amdsmi_shut_down()
+            except Exception:           # noqa: BLE001
+                pass
+
+    def summary(self) -> dict:
+        import numpy as np
+        out = {"samples": len(self.clk)}
+        if self.clk:
+            # the first samples may precede the load
+            c = np.array(self.clk[len(self.clk) // 5:])
+            out.update({"gfx_mhz_median": float(np.median(c)), "gfx_mhz_min": float(np.min(c)),
+                        "gfx_mhz_max": float(np.max(c))})
+        if self.power:
+            pw = np.array(self.power[len(self.power) // 5:])
+            out["socket_power_w_median"] = float(np.median(pw))
+        if self.error:
+            out["error"] = self.error
+        return out
+
+
+def mfma_ceiling_measure(torch, np, dev, fwd_tflops=None):
+    """A practical ceiling for bf16 matrix work on this part: torch.matmul
+    (hipBLASLt) on random bf16 8192 x 8192 x 8192 operands, timed with events
+    over a loop of about two seconds, with the graphics clock and socket power
+    sampled meanwhile; the same on constant operands (less switching activity
+    per MFMA) for contrast.  The nominal peak assumes 2400 MHz."""
+    N = 8192
+    out = {"shape": [N, N, N], "dtype": "bf16", "library": "torch.matmul (hipBLASLt)",
+           "nominal_peak_tflops": PEAK_BF16_TFLOPS}
+    for kind in ("random", "constant"):
+        if kind == "random":
+            a = torch.randn(N, N, device=dev, dtype=torch.bfloat16)
+            b = torch.randn(N, N, device=dev, dtype=torch.bfloat16)
+        else:
+            a = torch.full((N, N), 0.5, device=dev, dtype=torch.bfloat16)
+            b = torch.full((N, N), 0.25, device=dev, dtype=torch.bfloat16)
+        c = torch.empty(N, N, device=dev, dtype=torch.bfloat16)
+        for _ in range(3):
+            torch.matmul(a, b, out=c)
+        torch.cuda.synchronize()
+        iters = 40
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        with ClockSampler() as cs:
+            for _ in range(4):           # ~0.7 s per round at ~1.3 PFLOP/s
+                e0.record()
+                for _ in range(iters):
+                    torch.matmul(a, b, out=c)
+                e1.record()
+                torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / iters
+        tf = 2.0 * N ** 3 / (ms / 1e3) / 1e12
+        rec = {"ms": round(ms, 4), "tflops": round(tf, 1),
+               "frac_of_nominal": round(tf / PEAK_BF16_TFLOPS, 4), "clock": cs.summary()}
+        mhz = rec["clock"].get("gfx_mhz_median")
+        if mhz:
+            rec["peak_at_measured_clock_tflops"] = round(PEAK_BF16_TFLOPS * mhz / 2400.0, 1)
+        out[kind] = rec
+        del a, b, c
+    torch.cuda.empty_cache()
     return out
 
 
@@ -332,6 +573,7 @@ def cpu_baseline(w, x, tokens: int):
     oracle.backward(H, W, y, r["lse"], mask=m, z_coef=w.z_coef, nthreads=threads)
     dt = time.perf_counter() - t0
     return {"value": tokens / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "cpu_model": cpu_model_name(),
             "sample": f"first {tokens} tokens of the {w.n_tok}-token batch, full vocab "
                       f"{w.vocab} and d_model {w.d_model}: fp64 forward + backward "
                       f"(d_hidden of the sample, all d_weight rows), {dt:.2f} s",
@@ -416,16 +658,10 @@ def main():
     mem0 = torch.cuda.memory_allocated()
     torch.cuda.reset_peak_memory_stats()
 
-    def step(timer=None):
-        # forward without a host round trip, then the backward (synchronizes
-        # and reports its status); the loss scalars stay in the workspace
-        st, _ = lce.lce_forward(H, W, y, m, n, D, V, chunk, z, lse, ws, timer=timer, sync=False)
-        if st != lce.OK:
-            raise lce.LceError(st, "lce_forward")
-        st = lce.lce_backward(H, W, y, m, lse, n, D, V, chunk, z, 1.0, dH, dW, 0, ws,
-                              timer=timer)
-        if st != lce.OK:
-            raise lce.LceError(st, "lce_backward")
+    # forward and backward without a host round trip (neither call waits for
+    # the device); the loss scalars and the target guard's verdict stay in the
+    # workspace until lce_loss_fetch
+    step = step_runner(lce, w, H, W, y, m, lse, dH, dW, ws)
 
     def fetch():
         st, out = lce.lce_loss_fetch(ws)
@@ -456,6 +692,12 @@ def main():
     peak_extra = torch.cuda.max_memory_allocated() - mem0
     log(f"bench: {ms_per_step:.3f} ms/step wall, {gpu_ms / args.steps:.3f} ms/step events, "
         f"loss {out.loss_mean:.6f}")
+
+    # Per-step pass: the same K steps with an event between consecutive steps
+    # (median and min of the per-step device times).
+    steps_ms = per_step_ms(torch, step, args.steps)
+    fetch()
+    log(f"bench: per-step median {np.median(steps_ms):.4f} ms, min {np.min(steps_ms):.4f} ms")
 
     # Kernel pass: the same K steps again with HIP events around every kernel
     # launch (on the launch stream); the events add idle time between kernels,
@@ -537,6 +779,13 @@ def main():
         distill = distill_measure(lce, torch, np, dev, args.steps)
         label = label_measure(lce, torch, np, dev, args.steps)
 
+    f64_sweep = large = ceiling = None
+    if w.dtype == "bf16" and not args.no_distill:
+        f64_sweep = f64_sweep_measure(lce, torch, np, dev, max(3, args.steps // 5))
+        large = large_head_measure(lce, torch, np, dev, max(5, args.steps // 4))
+        log("bench: practical bf16 MFMA ceiling (torch.matmul 8192^3) with clock sampling")
+        ceiling = mfma_ceiling_measure(torch, np, dev)
+
     cpu = None
     if not args.no_cpu_baseline:
         log(f"bench: CPU oracle baseline on {args.cpu_tokens} tokens")
@@ -551,6 +800,8 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": round(ms_per_step, 4),
+        "step_ms_median": round(float(np.median(steps_ms)), 4),
+        "step_ms_min": round(float(np.min(steps_ms)), 4),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -573,6 +824,9 @@ def main():
         "vocab_shards": shard,
         "f16_inputs": f16,
         "single_call": single,
+        "f64_chunk_sweep": f64_sweep,
+        "large_head": large,
+        "mfma_ceiling": ceiling,
         "cpu_baseline": cpu,
     }
     print(json.dumps(res), flush=True)

@@ -21,13 +21,16 @@
  *   holds no global state, so calls are reentrant given distinct workspaces.
  *   Calls that share one workspace must be ordered (same stream).
  * Streams: device work is enqueued on the caller's stream (a hipStream_t
- *   passed as void*; NULL = the null stream).  lce_forward, lce_backward and
- *   lce_distill_fwd_bwd synchronize that stream once before returning,
- *   because their status (and the forward's scalars) come from the device.
+ *   passed as void*; NULL = the null stream).  Calls that hand back device
+ *   scalars (lce_forward with a non-NULL out, lce_distill_fwd_bwd, ...)
+ *   synchronize that stream once before returning.  lce_backward never
+ *   waits: it returns once its kernels are enqueued, and the verdict of its
+ *   target guard reaches the host through lce_loss_fetch.
  * Validation order: dimensions -> chunk -> scalars -> dtypes -> buffer
  *   lengths and workspace size -> objective id -> device-side target guard
  *   -> compute.  The target guard runs on the device; when it fails, every
- *   compute kernel exits before writing and 586 is returned.
+ *   compute kernel of that call exits before writing, and 586 is returned by
+ *   the call (synchronous calls) or by the next lce_loss_fetch.
  * Precision: bf16 and fp16 inputs are multiplied on the matrix cores with
  *   fp32 accumulation; every softmax statistic is fp32 and every token sum
  *   fp64.  fp64 inputs run end to end in fp64.  16-bit gradients (d_hidden,
@@ -145,6 +148,19 @@ int64_t lce_workspace_bytes(int64_t n_tok, int64_t d_model, int64_t vocab, int64
 int64_t lce_forward_backward_workspace_bytes(int64_t n_tok, int64_t d_model, int64_t vocab,
                                              int64_t chunk, int32_t dtype);
 
+/* Which algorithm lce_forward_backward runs for a shape (host only): 1 when
+ * it keeps the logits, 0 when it runs the two-call algorithm, -status when
+ * the shape, chunk or dtype is refused.  1 needs all of: 16-bit inputs
+ * (LCE_BF16 or LCE_F16); d_model a multiple of 64; a chunk that holds the
+ * whole batch (chunk >= max(n_tok rounded up to 4, n_tok rounded up to 64
+ * divided by 2)); and a launch-cost model of both algorithms that puts the
+ * kept path at least 3% ahead (it saves the recompute but moves about 10
+ * bytes per kept logit; measured on 512 x 151936 heads it loses at d_model
+ * 1024 and wins at 4096).  The call additionally needs hidden, weight and
+ * d_weight 16-byte aligned, which only the pointers can tell. */
+int32_t lce_forward_backward_keeps_logits(int64_t n_tok, int64_t d_model, int64_t vocab,
+                                          int64_t chunk, int32_t dtype);
+
 /* Bytes of device workspace lce_distill_fwd_bwd needs (-status if refused). */
 int64_t lce_distill_workspace_bytes(int64_t n_tok, int64_t vocab);
 
@@ -177,9 +193,11 @@ int32_t lce_forward(const lce_tensor *hidden, const lce_tensor *weight,
 
 /* The scalars of the last lce_forward on this workspace (lce_backward on the
  * same workspace keeps them): synchronizes `stream`, fills *out.  Returns 586
- * when that forward (or a later lce_backward) met a target out of range,
- * 582 for a NULL out or a workspace shorter than its control block, 590 for
- * a workspace that is not LCE_U8. */
+ * when that forward, or any lce_backward enqueued on this workspace since,
+ * met a target out of range (the scalars are then not filled in), 582 for a
+ * NULL out or a workspace shorter than its control block, 590 for a
+ * workspace that is not LCE_U8.  Meaningful only after an lce_forward on
+ * this workspace. */
 int32_t lce_loss_fetch(const lce_tensor *workspace, lce_loss *out, void *stream);
 
 /* Analytic backward of loss_mean + z_coef*z_mean scaled by grad_out
@@ -192,7 +210,12 @@ int32_t lce_loss_fetch(const lce_tensor *workspace, lce_loss *out, void *stream)
  *   d_weight   [vocab*d_model] LCE_F32 for 16-bit inputs, LCE_F64 for fp64;
  *              overwritten, or added to when accumulate_d_weight != 0
  * Logits are recomputed from H and W; the logit-gradient buffer holds at
- * most chunk*vocab cells at once. */
+ * most chunk*vocab cells at once.
+ * Asynchronous: returns 580 once the kernels are enqueued on `stream` (or a
+ * host-side refusal, or 589 when a launch fails) without waiting for the
+ * device.  A target out of range makes every kernel of the call exit before
+ * writing (d_hidden and d_weight keep their contents); lce_loss_fetch on the
+ * same workspace then returns 586. */
 int32_t lce_backward(const lce_tensor *hidden, const lce_tensor *weight,
                      const lce_tensor *targets, const lce_tensor *loss_mask,
                      const lce_tensor *lse, int64_t n_tok, int64_t d_model, int64_t vocab,
@@ -206,18 +229,20 @@ int32_t lce_backward(const lce_tensor *hidden, const lce_tensor *weight,
  * grad_out * (loss_mean + z_coef * z_mean), with the arguments of
  * lce_forward and lce_backward and one stream synchronization at the end.
  *   workspace  numel >= lce_forward_backward_workspace_bytes(...)
- *   out        host pointer (may be NULL: the scalars stay in the workspace,
- *              lce_loss_fetch reads them)
- * With 16-bit inputs and a chunk that holds the whole batch (chunk >=
- * max(n_tok rounded up to 4, n_tok rounded up to 64 / 2)) the logits are
- * computed once: kept in fp32 ([vocab][ld] cells, at most chunk*vocab), reduced to
- * lse, turned in place into the logit gradient and fed to the d_hidden and
- * d_weight products (6 n d_model vocab flops instead of 8).  The logit
- * gradient has the same values as lce_backward's, so lse, the loss scalars
- * and d_weight equal the two-call results bit for bit and d_hidden agrees to
- * fp32 summation order.  Otherwise (fp64 inputs or a smaller chunk) the call
- * runs lce_forward's and lce_backward's algorithm.  Status codes as
- * lce_forward and lce_backward. */
+ *   out        host pointer: the call synchronizes the stream and fills it.
+ *              NULL: asynchronous, as lce_forward with a NULL out; the
+ *              scalars and the target guard's verdict (586) stay in the
+ *              workspace for lce_loss_fetch
+ * The logits are computed once -- kept in fp32 ([vocab][ld] cells, at most
+ * chunk*vocab), reduced to lse, turned in place into the logit gradient and
+ * fed to the d_hidden and d_weight products (6 n d_model vocab flops
+ * instead of 8) -- exactly when lce_forward_backward_keeps_logits(...) is 1
+ * for the shape AND hidden, weight and d_weight are 16-byte aligned.  The
+ * logit gradient then has the same values as lce_backward's, so lse, the
+ * loss scalars and d_weight equal the two-call results bit for bit and
+ * d_hidden agrees to fp32 summation order.  Otherwise the call runs
+ * lce_forward's and lce_backward's algorithm.  Status codes as lce_forward
+ * and lce_backward. */
 int32_t lce_forward_backward(const lce_tensor *hidden, const lce_tensor *weight,
                              const lce_tensor *targets, const lce_tensor *loss_mask,
                              int64_t n_tok, int64_t d_model, int64_t vocab, int64_t chunk,

@@ -32,11 +32,13 @@ namespace lce {
 
 // ---------------------------------------------------------- small kernels --
 
-// keep_loss: leave the forward's loss scalars for lce_loss_fetch.
+// keep_loss (a backward after a forward on this workspace): leave the
+// forward's loss scalars for lce_loss_fetch and carry the guard verdicts met
+// since that forward into seen_bad; otherwise (a forward) start afresh.
 __global__ void ctl_init_kernel(Control *ctl, int keep_loss) {
   if (threadIdx.x == 0) {
+    ctl->seen_bad = keep_loss ? (ctl->seen_bad | ctl->bad) : 0;
     ctl->bad = 0;
-    ctl->pad0 = 0;
     ctl->first_bad = LLONG_MAX;
     ctl->count = 0;
     ctl->pad1 = 0;
@@ -1451,8 +1453,11 @@ int32_t finish(hipStream_t st, Control *dev_ctl, Control *host_ctl) {
   if (hipMemcpyAsync(host_ctl, dev_ctl, sizeof(Control), hipMemcpyDeviceToHost, st) != hipSuccess)
     return LCE_DEVICE_ERROR;
   if (hipStreamSynchronize(st) != hipSuccess) return LCE_DEVICE_ERROR;
-  return host_ctl->bad ? LCE_TARGET_OUT_OF_RANGE : LCE_OK;
+  return (host_ctl->bad || host_ctl->seen_bad) ? LCE_TARGET_OUT_OF_RANGE : LCE_OK;
 }
+
+// An asynchronous call's status: only launch errors are known on return.
+int32_t enqueued() { return hipGetLastError() == hipSuccess ? LCE_OK : LCE_DEVICE_ERROR; }
 
 void fill_loss(const Control &hc, lce_loss *out) {
   out->loss_sum = hc.loss_sum;
@@ -1600,8 +1605,7 @@ int32_t forward_call(const lce_tensor *hidden, const lce_tensor *weight,
                             total ? nullptr : static_cast<double *>(lse_out->data), ws, vec, s,
                             timers, sh);
   }
-  if (!out)  // asynchronous: the scalars stay in the workspace (lce_loss_fetch)
-    return hipGetLastError() == hipSuccess ? LCE_OK : LCE_DEVICE_ERROR;
+  if (!out) return enqueued();   // the scalars stay in the workspace (lce_loss_fetch)
   Control hc;
   st = finish(s, reinterpret_cast<Control *>(ws), &hc);
   if (st != LCE_OK) return st;
@@ -1728,8 +1732,9 @@ int32_t backward_call(const lce_tensor *hidden, const lce_tensor *weight,
                              d_hidden->data, total != 0, static_cast<double *>(d_weight->data),
                              accumulate_d_weight != 0, ws, vec, s, timers, sh);
   }
-  Control hc;
-  return finish(s, reinterpret_cast<Control *>(ws), &hc);
+  // No wait: a failed target guard makes every later kernel of the call exit
+  // before writing, and lce_loss_fetch reports it.
+  return enqueued();
 }
 
 }  // namespace
@@ -1807,10 +1812,11 @@ int32_t forward_backward_call(const lce_tensor *hidden, const lce_tensor *weight
                              d_hidden->data, false, static_cast<double *>(d_weight->data), acc,
                              ws, vec, s, timers, whole);
   }
+  if (!out) return enqueued();   // the scalars and the guard's verdict: lce_loss_fetch
   Control hc;
   st = finish(s, reinterpret_cast<Control *>(ws), &hc);
   if (st != LCE_OK) return st;
-  if (out) fill_loss(hc, out);
+  fill_loss(hc, out);
   return LCE_OK;
 }
 

@@ -154,6 +154,9 @@ int32_t plan_ce(int64_t n, int64_t D, int64_t V, int64_t chunk, int32_t dtype, C
       }
       q.pslab = S < V ? S : V;
       q.pdh_splits = best_sp;
+      // forward (rounds of vocabulary x token tiles, each D deep) + backward
+      q.model_two = ceil_div(ceil_div(V, tile_m) * tn * (D + kEpi), kComputeUnits) + kLaunch +
+                    best_cost;
       // The first launch runs slab 0's logit gradient alone: when a whole slab
       // would take more than one round of CUs, slab 0 gets the rows that fill
       // exactly one round (8192 at 2048 tokens) and the later slabs the rest.
@@ -203,17 +206,40 @@ int32_t plan_ce(int64_t n, int64_t D, int64_t V, int64_t chunk, int32_t dtype, C
   // split accumulators and H^T, all live at once.  The logits take V * f_ld
   // cells (at most chunk*vocab); f_ld also covers, at two 16-bit values per
   // cell, the gradient rows zero-padded to a multiple of 64 tokens.
+  //
+  // Whether keeping pays is decided by the same launch model as the slab
+  // pipeline (times in k-rows of one 256x256 tile on one compute unit,
+  // about 28 ns each): the kept path saves the recompute but writes the
+  // logits in fp32, reads them back and writes the 16-bit gradient (10
+  // bytes per kept cell, about 128 KB per unit at the chip's streaming
+  // rate) and runs d_hidden as one launch over the whole vocabulary.  The
+  // logits are kept only when the model puts that path at least 3% ahead of
+  // the two-call algorithm (measured on 512 x 151936 heads: 0.93x at
+  // d_model 1024, 1.19x at 4096; 1.15x at 256 x 1024).
   q.f_total = q.total;
   if (bf) {
     int64_t fld = round_up(n, 4);
     if (2 * fld < round_up(n, 64)) fld = round_up(n, 64) / 2;
-    if (fld <= chunk && q.tok_per_pass >= n) {
+    int64_t sp = ceil_div(kComputeUnits, out_tiles);
+    if (sp > V / 512) sp = V / 512;
+    if (sp > 32) sp = 32;
+    if (sp < 1) sp = 1;
+    {
+      const int64_t kEpi = 256, kLaunch = 64, kBytesPerUnit = 128000;
+      const int64_t tn = ceil_div(n, tile_m), td = ceil_div(D, tile_n);
+      const int64_t fwd = ceil_div(ceil_div(V, tile_m) * tn * (D + 2 * kEpi), kComputeUnits);
+      const int64_t kept = V * fld * 10 / kBytesPerUnit;
+      const int64_t dh_wg = (ceil_div(V, sp) * 5) / 4 + kEpi;
+      const int64_t work = out_tiles * sp * dh_wg + ceil_div(V, tile_m) * td * (n + kEpi);
+      const int64_t spread = ceil_div(work, kComputeUnits);
+      q.model_single = fwd + kept + (spread > dh_wg ? spread : dh_wg) + 3 * kLaunch;
+    }
+    // (without a slab pipeline to compare with, keeping always pays)
+    const bool pays = q.model_two == 0 || q.model_single * 103 < q.model_two * 100;
+    if (fld <= chunk && q.tok_per_pass >= n && pays) {
       q.f_ok = true;
       q.f_ld = fld;
-      int64_t sp = ceil_div(kComputeUnits, out_tiles);
-      if (sp > V / 512) sp = V / 512;
-      if (sp > 32) sp = 32;
-      q.f_sp = sp < 1 ? 1 : sp;
+      q.f_sp = sp;
       size_t o = fwd_end;
       q.off_fz = o;
       o = align256(o + size_t(V) * size_t(fld) * 4);
@@ -311,6 +337,15 @@ int64_t lce_forward_backward_workspace_bytes(int64_t n_tok, int64_t d_model, int
   int32_t st = plan_ce(n_tok, d_model, vocab, chunk, dtype, &p);
   if (st != LCE_OK) return -int64_t(st);
   return int64_t(p.f_total) + 256;
+}
+
+int32_t lce_forward_backward_keeps_logits(int64_t n_tok, int64_t d_model, int64_t vocab,
+                                          int64_t chunk, int32_t dtype) {
+  CEPlan p;
+  const int32_t st = plan_ce(n_tok, d_model, vocab, chunk, dtype, &p);
+  if (st != LCE_OK) return -st;
+  // the kept path reads every operand with the 16-byte pipelined core
+  return p.f_ok && d_model % 64 == 0 ? 1 : 0;
 }
 
 int64_t lce_distill_workspace_bytes(int64_t n_tok, int64_t vocab) {

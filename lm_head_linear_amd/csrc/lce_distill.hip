@@ -498,6 +498,7 @@ label_row_kernel(const T *Z, const int64_t *y, const uint8_t *mask, int64_t n, i
 __global__ void distill_init_kernel(Control *ctl) {
   if (threadIdx.x == 0) {
     ctl->bad = 0;
+    ctl->seen_bad = 0;
     ctl->first_bad = LLONG_MAX;
     ctl->count = 0;
     ctl->loss_sum = 0.0;

@@ -11,8 +11,9 @@ namespace lce {
 // Device-side control block at offset 0 of every workspace.  The guard
 // kernel fills bad/first_bad/count; the reduction kernels fill the sums.
 struct Control {
-  int32_t bad;          // nonzero when a target id is out of range
-  int32_t pad0;
+  int32_t bad;          // nonzero when this call's target guard failed
+  int32_t seen_bad;     // a guard failed in the last forward on this workspace
+                        // or in a backward since (read by lce_loss_fetch)
   int64_t first_bad;    // smallest offending token index (diagnostic)
   int64_t count;        // counted (unmasked) tokens
   int64_t pad1;
@@ -51,6 +52,10 @@ struct CEPlan {
   int64_t pn_slabs = 0;
   int64_t pslab0 = 0;         // rows of the first slab (<= pslab; the others pslab)
   int64_t pdh_splits = 0;
+  // modelled duration (k-rows of a 256x256 tile on one compute unit) of the
+  // two-call algorithm and of the single call that keeps the logits (16-bit
+  // inputs; 0 when not modelled)
+  int64_t model_two = 0, model_single = 0;
   // workspace layout (byte offsets)
   size_t off_partials = 0, off_zy = 0, off_losstok = 0;
   size_t off_dbuf = 0, off_dhacc = 0;

@@ -138,6 +138,8 @@ def lib():
         L.lce_distill_workspace_bytes.argtypes = [i64, i64]
         L.lce_forward_backward_workspace_bytes.restype = i64
         L.lce_forward_backward_workspace_bytes.argtypes = [i64, i64, i64, i64, i32]
+        L.lce_forward_backward_keeps_logits.restype = i32
+        L.lce_forward_backward_keeps_logits.argtypes = [i64, i64, i64, i64, i32]
         L.lce_forward.restype = i32
         L.lce_forward.argtypes = [PT, PT, PT, PT, i64, i64, i64, i64, dbl, PT, PT,
                                   ctypes.POINTER(Loss), vp]
@@ -234,6 +236,12 @@ def lce_forward_backward_workspace_bytes(n_tok: int, d_model: int, vocab: int, c
     return lib().lce_forward_backward_workspace_bytes(n_tok, d_model, vocab, chunk, dt)
 
 
+def lce_forward_backward_keeps_logits(n_tok: int, d_model: int, vocab: int, chunk: int,
+                                      dtype) -> int:
+    dt = _DT[dtype] if isinstance(dtype, torch.dtype) else int(dtype)
+    return lib().lce_forward_backward_keeps_logits(n_tok, d_model, vocab, chunk, dt)
+
+
 # ------------------------------------------------------------ device calls
 
 def lce_forward(hidden, weight, targets, loss_mask, n_tok, d_model, vocab, chunk, z_coef,
@@ -270,7 +278,8 @@ def lce_backward(hidden, weight, targets, loss_mask, lse, n_tok, d_model, vocab,
                  grad_out, d_hidden, d_weight, accumulate_d_weight, workspace,
                  stream: Optional[int] = None, timer: Optional[KernelTimer] = None) -> int:
     """Direct call of the C entry point (lce_backward_timed when a timer is
-    given).  Returns the status."""
+    given).  Returns the status; the call does not wait for the device, so a
+    target out of range shows in the next lce_loss_fetch (586)."""
     ts = [_t(hidden), _t(weight), _t(targets), _t(loss_mask), _t(lse)]
     dh, dw, ws = _t(d_hidden), _t(d_weight), _t(workspace)
     call = [*[ctypes.byref(a) for a in ts], n_tok, d_model, vocab, chunk, float(z_coef),

@@ -95,8 +95,8 @@ def test_single_call_workspace():
     # fp64 never keeps logits
     assert f(512, 1024, 151936, 512, lce.F64) == lce.lce_workspace_bytes(512, 1024, 151936, 512,
                                                                           lce.F64)
-    for n, D, V, chunk in [(512, 1024, 151936, 512), (300, 192, 3000, 300), (1, 64, 33, 32),
-                           (517, 256, 2100, 600)]:
+    for n, D, V, chunk in [(512, 4096, 151936, 512), (256, 1024, 151936, 256),
+                           (300, 192, 3000, 300), (1, 64, 33, 32), (517, 256, 2100, 600)]:
         single, two = f(n, D, V, chunk, lce.BF16), lce.lce_workspace_bytes(n, D, V, chunk,
                                                                            lce.BF16)
         assert single > two
@@ -109,6 +109,30 @@ def test_single_call_workspace():
     assert f(2048, 1024, 151936, 1024, lce.BF16) == -587
     assert f(0, 1024, 151936, 256, lce.BF16) == -581
     assert f(64, 64, 1000, 64, lce.F32) == -590
+
+
+def test_single_call_dispatch():
+    """lce_forward_backward_keeps_logits: the launch-cost model keeps the
+    logits where that measured faster (512 x 4096 and 256 x 1024 heads of
+    151936 rows) and takes the two-call algorithm where it measured slower
+    (512 x 1024); the workspace follows the choice."""
+    k = lce.lce_forward_backward_keeps_logits
+    f = lce.lce_forward_backward_workspace_bytes
+    w = lce.lce_workspace_bytes
+    assert k(512, 4096, 151936, 512, lce.BF16) == 1
+    assert k(256, 1024, 151936, 256, lce.BF16) == 1
+    assert k(512, 1024, 151936, 512, lce.BF16) == 0
+    assert f(512, 1024, 151936, 512, lce.BF16) == w(512, 1024, 151936, 512, lce.BF16)
+    assert k(512, 4096, 151936, 512, lce.F16) == 1
+    assert k(512, 4096, 151936, 512, lce.F64) == 0        # fp64 never keeps
+    assert k(2048, 1024, 151936, 256, lce.BF16) == 0      # the batch exceeds the chunk
+    assert k(96, 100, 777, 96, lce.BF16) == 0             # d_model not a multiple of 64
+    assert k(2048, 1024, 151936, 1024, lce.BF16) == -587
+    assert k(0, 1024, 151936, 256, lce.BF16) == -581
+    assert k(64, 64, 1000, 64, lce.F32) == -590
+    for n, D, V, chunk in [(300, 192, 3000, 300), (200, 128, 3000, 256), (130, 128, 2000, 132)]:
+        assert k(n, D, V, chunk, lce.BF16) == 1, (n, D, V)
+        assert f(n, D, V, chunk, lce.BF16) > w(n, D, V, chunk, lce.BF16)
 
 
 def test_loss_fetch_refuses_short_workspace_without_device():

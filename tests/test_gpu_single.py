@@ -139,21 +139,23 @@ def test_refusals_leave_outputs_untouched():
 
 
 def test_kept_logits_full_vocab():
-    """512 tokens x 1024 x 151936 bf16 in one chunk of 512, 5% masked, z 1e-4:
-    sampled rows against the oracle, everything against the two-call path."""
+    """256 tokens x 1024 x 151936 bf16 in one chunk of 256, 5% masked, z 1e-4
+    (a shape where the call keeps the logits): sampled rows against the
+    oracle, everything against the two-call path."""
     w = syn.QWEN_BF16
-    _say("case 512 x 1024 x 151936 bf16, chunk 512: generating inputs")
-    c = Case(w, 512, 1024, 151936, seed=41, mask_frac=0.05)
-    fwd, dH, dW = _single(c, 512)
-    f2 = c.gpu_forward(512)
-    dH2, dW2 = c.gpu_backward(f2.lse, 512)
+    _say("case 256 x 1024 x 151936 bf16, chunk 256: generating inputs")
+    c = Case(w, 256, 1024, 151936, seed=41, mask_frac=0.05)
+    assert lce.lce_forward_backward_keeps_logits(256, 1024, 151936, 256, c.H.dtype) == 1
+    fwd, dH, dW = _single(c, 256)
+    f2 = c.gpu_forward(256)
+    dH2, dW2 = c.gpu_backward(f2.lse, 256)
     torch.cuda.synchronize()
     assert fwd.loss == f2.loss and torch.equal(fwd.lse, f2.lse) and torch.equal(dW, dW2)
     e = normwise(dH.double().cpu().numpy(), dH2.double().cpu().numpy())
     _say(f"  single vs two calls: d_hidden {e:.2e}")
     assert e <= 1e-2
     _say("  oracle forward (all tokens)")
-    ref = c.oracle_forward(512)
+    ref = c.oracle_forward(256)
     check_forward(c, fwd, ref)
     rng = np.random.default_rng(7)
     th = _sample(rng, c.n, 4)
