@@ -271,6 +271,24 @@ int32_t lce_distill_fwd_bwd(const lce_tensor *student, const lce_tensor *teacher
                             double grad_out, lce_tensor *grad_logits, lce_tensor *workspace,
                             lce_loss *out, void *stream);
 
+/* lce_distill_fwd_bwd for callers that cannot allocate device memory (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc): the same computation, arguments and statuses without the
+ * workspace argument.  Its scratch (control block and per-row results) is a
+ * static device array of this library, 256 + 16 * 65536 bytes per GPU, held
+ * by every GPU the library runs on until the process ends; the call itself
+ * allocates nothing.
+ *   n_tok     at most 65536 (else 582: the static scratch is too short)
+ * The call clears what must start at zero.  Every call on one GPU shares
+ * that GPU's scratch, so calls that overlap on one GPU (different streams or
+ * host threads) race; order them.  Returns 589 if the scratch's device
+ * address cannot be obtained. */
+int32_t lce_distill_fwd_bwd_noalloc(const lce_tensor *student, const lce_tensor *teacher,
+                                    const lce_tensor *loss_mask, int64_t n_tok, int64_t vocab,
+                                    int32_t objective, double temperature, double z_coef,
+                                    double grad_out, lce_tensor *grad_logits, lce_loss *out,
+                                    void *stream);
+
 /* ---- vocabulary shards: one GPU's rows of a vocabulary-parallel head ---- */
 
 /* The lossk reduction (per token lse and target logit, "Loss functions and

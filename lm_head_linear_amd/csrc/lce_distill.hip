@@ -31,6 +31,8 @@
 // row is read once.
 #include <hip/hip_runtime.h>
 
+#include <mutex>
+
 #include <climits>
 #include <cmath>
 
@@ -637,37 +639,49 @@ extern "C" int32_t lce_distill_fwd_bwd(const lce_tensor *student, const lce_tens
                                    stream, nullptr);
 }
 
-extern "C" int32_t lce_distill_fwd_bwd_timed(const lce_tensor *student, const lce_tensor *teacher,
-                                             const lce_tensor *loss_mask, int64_t n_tok,
-                                             int64_t vocab, int32_t objective, double temperature,
-                                             double z_coef, double grad_out,
-                                             lce_tensor *grad_logits, lce_tensor *workspace,
-                                             lce_loss *out, void *stream, lce_timers *timers) {
+namespace lce {
+namespace {
+
+// The distillation call on a resolved scratch region: `ws` (256-byte aligned)
+// holds at least `ws_bytes` bytes of device memory for the control block and
+// the per-row results (DistillPlan).  ws == nullptr: the caller's workspace
+// descriptor `workspace` supplies it.
+int32_t distill_call(const lce_tensor *student, const lce_tensor *teacher,
+                     const lce_tensor *loss_mask, int64_t n_tok, int64_t vocab,
+                     int32_t objective, double temperature, double z_coef, double grad_out,
+                     lce_tensor *grad_logits, const lce_tensor *workspace, uint8_t *ws,
+                     int64_t ws_bytes, lce_loss *out, void *stream, lce_timers *timers) {
   DistillPlan p;
   int32_t st = plan_distill(n_tok, vocab, &p);
   if (st != LCE_OK) return st;
   if (!finite_scalar(z_coef) || !finite_scalar(grad_out) || !finite_scalar(temperature) ||
       !(temperature > 0.0))
     return LCE_NON_FINITE_SCALAR;
-  if (!student || !teacher || !grad_logits || !workspace) return LCE_LENGTH_MISMATCH;
+  if (!student || !teacher || !grad_logits || (!ws && !workspace)) return LCE_LENGTH_MISMATCH;
   const int32_t dt = student->dtype;
   if (dt != LCE_BF16 && dt != LCE_F16 && dt != LCE_F32 && dt != LCE_F64)
     return LCE_DTYPE_MISMATCH;
   if (teacher->dtype != dt || grad_logits->dtype != dt) return LCE_DTYPE_MISMATCH;
   if (has(loss_mask) && loss_mask->dtype != LCE_U8) return LCE_DTYPE_MISMATCH;
-  if (workspace->dtype != LCE_U8) return LCE_DTYPE_MISMATCH;
+  if (!ws && workspace->dtype != LCE_U8) return LCE_DTYPE_MISMATCH;
   const int64_t cells = n_tok * vocab;
   if (!has(student) || student->numel < cells || !has(teacher) || teacher->numel < cells ||
       !has(grad_logits) || grad_logits->numel < cells)
     return LCE_LENGTH_MISMATCH;
   if (has(loss_mask) && loss_mask->numel < n_tok) return LCE_LENGTH_MISMATCH;
-  if (!has(workspace) || workspace->numel < int64_t(p.total) + 256) return LCE_LENGTH_MISMATCH;
+  if (ws) {
+    if (ws_bytes < int64_t(p.total)) return LCE_LENGTH_MISMATCH;
+  } else if (!has(workspace) || workspace->numel < int64_t(p.total) + 256) {
+    return LCE_LENGTH_MISMATCH;
+  }
   if (objective < 0 || objective > 2) return LCE_UNKNOWN_OBJECTIVE;
   if (!out) return LCE_LENGTH_MISMATCH;
 
   hipStream_t s = static_cast<hipStream_t>(stream);
-  uintptr_t base = (reinterpret_cast<uintptr_t>(workspace->data) + 255) & ~uintptr_t(255);
-  uint8_t *ws = reinterpret_cast<uint8_t *>(base);
+  if (!ws) {
+    const uintptr_t base = (reinterpret_cast<uintptr_t>(workspace->data) + 255) & ~uintptr_t(255);
+    ws = reinterpret_cast<uint8_t *>(base);
+  }
   Control *ctl = reinterpret_cast<Control *>(ws);
   double *rows = reinterpret_cast<double *>(ws + p.off_rows);
   const uint8_t *mask = has(loss_mask) ? static_cast<const uint8_t *>(loss_mask->data) : nullptr;
@@ -706,6 +720,59 @@ extern "C" int32_t lce_distill_fwd_bwd_timed(const lce_tensor *student, const lc
   out->loss_mean = hc.count ? hc.loss_sum / double(hc.count) : 0.0;
   out->z_mean = hc.count ? hc.z_sum / double(hc.count) : 0.0;
   return LCE_OK;
+}
+
+// Scratch of the allocation-free distillation call: one control block and
+// the per-row results of up to kNoAllocMaxTok tokens.  Each device holds its
+// own copy for the life of the process; host code reaches it only through
+// the per-device address hipGetSymbolAddress returns.
+constexpr int64_t kNoAllocMaxTok = 65536;
+constexpr size_t kNoAllocScratchBytes = kControlBytes + size_t(kNoAllocMaxTok) * 2 * sizeof(double);
+__device__ __attribute__((aligned(256))) uint8_t scratch[kNoAllocScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[kMaxDevices];
+
+// The current device's address of `scratch`, looked up once per device.
+uint8_t *scratch_for_current_device() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void *ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) return nullptr;
+    g_scratch_ptr[dev] = ptr;
+  }
+  return static_cast<uint8_t *>(g_scratch_ptr[dev]);
+}
+
+}  // namespace
+}  // namespace lce
+
+extern "C" int32_t lce_distill_fwd_bwd_timed(const lce_tensor *student, const lce_tensor *teacher,
+                                             const lce_tensor *loss_mask, int64_t n_tok,
+                                             int64_t vocab, int32_t objective, double temperature,
+                                             double z_coef, double grad_out,
+                                             lce_tensor *grad_logits, lce_tensor *workspace,
+                                             lce_loss *out, void *stream, lce_timers *timers) {
+  return distill_call(student, teacher, loss_mask, n_tok, vocab, objective, temperature, z_coef,
+                      grad_out, grad_logits, workspace, nullptr, 0, out, stream, timers);
+}
+
+extern "C" int32_t lce_distill_fwd_bwd_noalloc(const lce_tensor *student,
+                                               const lce_tensor *teacher,
+                                               const lce_tensor *loss_mask, int64_t n_tok,
+                                               int64_t vocab, int32_t objective,
+                                               double temperature, double z_coef, double grad_out,
+                                               lce_tensor *grad_logits, lce_loss *out,
+                                               void *stream) {
+  // more than kNoAllocMaxTok tokens: the scratch-length check refuses (582)
+  uint8_t *ws = scratch_for_current_device();
+  if (!ws) return LCE_DEVICE_ERROR;
+  return distill_call(student, teacher, loss_mask, n_tok, vocab, objective, temperature, z_coef,
+                      grad_out, grad_logits, nullptr, ws, int64_t(kNoAllocScratchBytes), out,
+                      stream, nullptr);
 }
 
 extern "C" int32_t lce_ce_logits_fwd_bwd(const lce_tensor *logits, const lce_tensor *targets,

@@ -151,6 +151,9 @@ def lib():
         L.lce_distill_fwd_bwd.restype = i32
         L.lce_distill_fwd_bwd.argtypes = [PT, PT, PT, i64, i64, i32, dbl, dbl, dbl, PT, PT,
                                           ctypes.POINTER(Loss), vp]
+        L.lce_distill_fwd_bwd_noalloc.restype = i32
+        L.lce_distill_fwd_bwd_noalloc.argtypes = [PT, PT, PT, i64, i64, i32, dbl, dbl, dbl, PT,
+                                                  ctypes.POINTER(Loss), vp]
         L.lce_ce_logits_fwd_bwd.restype = i32
         L.lce_ce_logits_fwd_bwd.argtypes = [PT, PT, PT, i64, i64, dbl, dbl, PT, PT,
                                             ctypes.POINTER(Loss), vp]
@@ -305,6 +308,21 @@ def lce_distill_fwd_bwd(student, teacher, loss_mask, n_tok, vocab, objective, te
         st = lib().lce_distill_fwd_bwd(*call)
     else:
         st = lib().lce_distill_fwd_bwd_timed(*call, ctypes.byref(timer.struct))
+    return st, out
+
+
+def lce_distill_fwd_bwd_noalloc(student, teacher, loss_mask, n_tok, vocab, objective,
+                                temperature, z_coef, grad_out, grad_logits,
+                                stream: Optional[int] = None):
+    """Direct call of the allocation-free C entry point (its scratch is the
+    library's static device array).  Returns (status, Loss)."""
+    out = Loss()
+    ts = [_t(student), _t(teacher), _t(loss_mask)]
+    g = _t(grad_logits)
+    st = lib().lce_distill_fwd_bwd_noalloc(
+        *[ctypes.byref(a) for a in ts], n_tok, vocab, int(objective), float(temperature),
+        float(z_coef), float(grad_out), ctypes.byref(g), ctypes.byref(out),
+        stream if stream is not None else _stream(student.device))
     return st, out
 
 
