@@ -1108,6 +1108,14 @@ static void backward_pipelined(const CEPlan &p, const uint16_t *Hp, const uint16
     rows = cap < V - v0 ? cap : V - v0;
     return v0;
   };
+  struct Packed {
+    int64_t key[3];
+    double d0;
+    bool ok;
+    PackCounts pc;
+    int slots;
+  } packs[4];
+  int n_packs = 0;
   for (int64_t k = 0; k <= p.pn_slabs; ++k) {
     JH jh{};
     JW jw{};
@@ -1159,9 +1167,35 @@ static void backward_pipelined(const CEPlan &p, const uint16_t *Hp, const uint16
       jl.nb = round_up8(jl.nreal);
     }
     TimedLaunch tl(tm, LCE_K_BWD_GEMM, st);
-    const int64_t total = jh.nb + jw.nb + jl.nb;
-    hipLaunchKernelGGL((gemm2_multi_kernel<TRP, JH, JW, JL>), dim3(unsigned(total)),
-                       dim3(TRP::NT), 0, st, jh, jw, jl);
+    // Packed onto the compute units by the host with the tile-duration model
+    // the planner chose the slabs with; hardware dispatch in product order
+    // when the packing does not apply.
+    const int64_t nt[3] = {jh.nreal, jw.nreal, jl.nreal};
+    const double dur[3] = {tile_us_dhidden(jh.g.k_per_split), tile_us_dweight(n),
+                           tile_us_dlogit(D)};
+    // launches with the same tile counts and durations share one packing
+    int m = -1;
+    for (int i = 0; i < n_packs; ++i)
+      if (packs[i].key[0] == nt[0] && packs[i].key[1] == nt[1] && packs[i].key[2] == nt[2] &&
+          packs[i].d0 == dur[0])
+        m = i;
+    if (m < 0 && n_packs < 4 && p.ppacked) {
+      m = n_packs++;
+      packs[m].key[0] = nt[0]; packs[m].key[1] = nt[1]; packs[m].key[2] = nt[2];
+      packs[m].d0 = dur[0];
+      packs[m].ok = pack_tiles(nt, dur, &packs[m].pc, &packs[m].slots);
+    }
+    if (m >= 0 && packs[m].ok) {
+      const PackCounts &pack = packs[m].pc;
+      const int pack_slots = packs[m].slots;
+      hipLaunchKernelGGL((gemm2_packed_kernel<TRP, JH, JW, JL>),
+                         dim3(unsigned(kPackXcds * pack_slots)), dim3(TRP::NT), 0, st, jh, jw,
+                         jl, pack);
+    } else {
+      const int64_t total = jh.nb + jw.nb + jl.nb;
+      hipLaunchKernelGGL((gemm2_multi_kernel<TRP, JH, JW, JL>), dim3(unsigned(total)),
+                         dim3(TRP::NT), 0, st, jh, jw, jl);
+    }
   }
 }
 

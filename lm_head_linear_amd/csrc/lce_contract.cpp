@@ -6,6 +6,7 @@
 // lossk function table, "Status codes" and "The two budgets are genuinely
 // different questions".
 #include <cmath>
+#include <mutex>
 
 #include "lce_internal.h"
 
@@ -28,6 +29,106 @@ size_t dtype_size(int32_t dtype) {
 static int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 static int64_t round_up(int64_t a, int64_t b) { return ceil_div(a, b) * b; }
 static size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+namespace {
+
+struct SlabChoice {
+  int64_t slab = 0, slab0 = 0, splits = 1;
+  double us = 0.0;   // modelled backward time
+};
+
+// Modelled time of one slab-pipeline launch: d_hidden (split `sp` ways) and
+// d_weight of `prev` rows with the logit gradient of `next` rows, packed.
+double launch_us(int64_t n, int64_t D, int64_t prev, int64_t next, int64_t sp, int64_t td,
+                 int64_t tn, int64_t out_tiles) {
+  const int64_t nt[3] = {prev > 0 ? out_tiles * sp : 0, prev > 0 ? ceil_div(prev, 256) * td : 0,
+                         next > 0 ? ceil_div(next, 256) * tn : 0};
+  const double dur[3] = {tile_us_dhidden(round_up(ceil_div(prev > 0 ? prev : 1, sp), 64)),
+                         tile_us_dweight(n), tile_us_dlogit(D)};
+  PackCounts pc;
+  int slots = 0;
+  double ms = 0.0;
+  if (!pack_tiles(nt, dur, &pc, &slots, &ms)) {
+    // hardware dispatch in product order: work spread over the compute
+    // units, plus a tail of about one tile
+    double work = 0.0, longest = 0.0;
+    for (int j = 0; j < 3; ++j) {
+      work += double(nt[j]) * (dur[j] + 1.0);
+      if (nt[j] > 0 && dur[j] > longest) longest = dur[j];
+    }
+    ms = work / kComputeUnits + longest;
+  }
+  return ms + kLaunchUs;
+}
+
+// The slab (a multiple of 256 rows, at most s_max), the first slab and the
+// d_hidden split count with the least modelled backward time, among the
+// choices whose launches hold at most three tiles per compute unit (coarser
+// work is where in-order dispatch leaves a long tail and packing pays); slab
+// 0 when there is none.  The search is memoized per shape.
+SlabChoice choose_slabs(int64_t n, int64_t D, int64_t V, int64_t s_max, int64_t tn, int64_t td,
+                        int64_t out_tiles) {
+  struct Entry {
+    int64_t key[4];
+    SlabChoice c;
+  };
+  static std::mutex mu;
+  static Entry memo[32];
+  static int n_memo = 0, next_slot = 0;
+  {
+    std::lock_guard<std::mutex> lock(mu);
+    for (int i = 0; i < n_memo; ++i)
+      if (memo[i].key[0] == n && memo[i].key[1] == D && memo[i].key[2] == V &&
+          memo[i].key[3] == s_max)
+        return memo[i].c;
+  }
+  SlabChoice best;
+  const int64_t s_min = s_max - 8 * 256 > 256 ? s_max - 8 * 256 : 256;
+  for (int64_t S = s_max; S >= s_min; S -= 256) {
+    // slab 0: the rows of one round of compute units, or a whole slab
+    int64_t firsts[2] = {S, S};
+    if (tn <= kComputeUnits) {
+      const int64_t r0 = (kComputeUnits / tn) * 256;
+      if (r0 < S) firsts[1] = r0;
+    }
+    for (int f = 0; f < 2; ++f) {
+      if (f == 1 && firsts[1] == firsts[0]) continue;
+      const int64_t s0 = firsts[f] < V ? firsts[f] : V;
+      // slab rows: s0, then S ..., then the remainder
+      const int64_t ns = V > s0 ? 1 + ceil_div(V - s0, S) : 1;
+      const int64_t last = ns > 1 ? V - s0 - (ns - 2) * S : s0;
+      for (int64_t sp = 1; sp <= 16; sp *= 2) {
+        if (sp > 1 && S / sp < 512) break;
+        const int64_t busiest = out_tiles * sp + ceil_div(S, 256) * (td + tn);
+        if (busiest > 3 * kComputeUnits) continue;
+        double t = launch_us(n, D, 0, s0, sp, td, tn, out_tiles);
+        if (ns == 1) {
+          t += launch_us(n, D, s0, 0, sp, td, tn, out_tiles);
+        } else {
+          t += launch_us(n, D, s0, ns > 2 ? S : last, sp, td, tn, out_tiles);
+          if (ns > 3) t += double(ns - 3) * launch_us(n, D, S, S, sp, td, tn, out_tiles);
+          if (ns > 2) t += launch_us(n, D, S, last, sp, td, tn, out_tiles);
+          t += launch_us(n, D, last, 0, sp, td, tn, out_tiles);
+        }
+        if (best.slab == 0 || t < best.us) {
+          best.slab = S;
+          best.slab0 = s0;
+          best.splits = sp;
+          best.us = t;
+        }
+      }
+    }
+  }
+  std::lock_guard<std::mutex> lock(mu);
+  Entry &e = memo[next_slot];
+  next_slot = (next_slot + 1) % 32;
+  if (n_memo < 32) ++n_memo;
+  e.key[0] = n; e.key[1] = D; e.key[2] = V; e.key[3] = s_max;
+  e.c = best;
+  return best;
+}
+
+}  // namespace
 
 int32_t plan_ce(int64_t n, int64_t D, int64_t V, int64_t chunk, int32_t dtype, CEPlan *p) {
   int32_t st = lce_dims_check(n, D, V);
@@ -152,18 +253,32 @@ int32_t plan_ce(int64_t n, int64_t D, int64_t V, int64_t chunk, int32_t dtype, C
           best_cost = c;
         }
       }
-      q.pslab = S < V ? S : V;
-      q.pdh_splits = best_sp;
-      // forward (rounds of vocabulary x token tiles, each D deep) + backward
+      // forward (rounds of vocabulary x token tiles, each D deep) + backward,
+      // for the single call's choice below
       q.model_two = ceil_div(ceil_div(V, tile_m) * tn * (D + kEpi), kComputeUnits) + kLaunch +
                     best_cost;
-      // The first launch runs slab 0's logit gradient alone: when a whole slab
-      // would take more than one round of CUs, slab 0 gets the rows that fill
-      // exactly one round (8192 at 2048 tokens) and the later slabs the rest.
-      q.pslab0 = q.pslab;
-      if (tn <= kComputeUnits) {
-        const int64_t r0 = (kComputeUnits / tn) * tile_m;
-        if (r0 < q.pslab && ceil_div(q.pslab, tile_m) * tn > kComputeUnits) q.pslab0 = r0;
+      // The launches themselves are packed onto the compute units
+      // (pack_tiles), so the slab, its d_hidden split count and the first
+      // slab are chosen by the packed makespans of all launches of the
+      // backward (choose_slabs).
+      const SlabChoice c = choose_slabs(n, D, V, S, tn, td, out_tiles);
+      if (c.slab > 0) {
+        q.pslab = c.slab;
+        q.pslab0 = c.slab0;
+        q.pdh_splits = c.splits;
+        q.ppacked = true;
+        q.model_bwd_us = c.us;
+      } else {
+        // Finer-grained launches (more than three tiles per compute unit):
+        // hardware dispatch balances them; the largest slab, the split count
+        // of the launch model above and a first slab of one round.
+        q.pslab = S < V ? S : V;
+        q.pdh_splits = best_sp;
+        q.pslab0 = q.pslab;
+        if (tn <= kComputeUnits) {
+          const int64_t r0 = (kComputeUnits / tn) * tile_m;
+          if (r0 < q.pslab && ceil_div(q.pslab, tile_m) * tn > kComputeUnits) q.pslab0 = r0;
+        }
       }
       q.pn_slabs = V > q.pslab0 ? 1 + ceil_div(V - q.pslab0, q.pslab) : 1;
     }
@@ -254,6 +369,133 @@ int32_t plan_ce(int64_t n, int64_t D, int64_t V, int64_t chunk, int32_t dtype, C
   }
   *p = q;
   return LCE_OK;
+}
+
+namespace {
+
+constexpr int kSlotsPerXcd = kPackSlots / kPackXcds;
+
+// Best-fit decreasing under makespan T: every tile goes to the slot whose
+// load it leaves closest to T (a new slot only when none has room).  Tiles
+// of one product are identical, so placing them one by one fills the
+// fullest slot that still has room as far as it goes, then the next fullest:
+// done here in bulk.  gap is the per-tile cost of starting another tile on a
+// slot.
+bool pack_under(const int64_t k[3], const double dur[3], const int order[3], double T,
+                double gap, uint8_t c[kSlotsPerXcd][3], int *used) {
+  double load[kSlotsPerXcd] = {};
+  int open = 0;
+  for (int s = 0; s < kSlotsPerXcd; ++s) c[s][0] = c[s][1] = c[s][2] = 0;
+  for (int oi = 0; oi < 3; ++oi) {
+    const int j = order[oi];
+    const double d = dur[j] + gap;
+    int64_t left = k[j];
+    if (left > 0 && d > T) return false;
+    while (left > 0) {
+      // the fullest open slot with room for one more tile of this product
+      int best = -1;
+      for (int s = 0; s < open; ++s)
+        if (load[s] + d <= T && c[s][j] < 255 && (best < 0 || load[s] > load[best])) best = s;
+      if (best < 0) {
+        if (open == kSlotsPerXcd) return false;
+        best = open++;
+      }
+      int64_t fit = int64_t((T - load[best]) / d);
+      if (fit > 255 - c[best][j]) fit = 255 - c[best][j];
+      if (fit > left) fit = left;
+      if (fit < 1) return false;
+      load[best] += double(fit) * d;
+      c[best][j] = uint8_t(c[best][j] + fit);
+      left -= fit;
+    }
+  }
+  *used = open;
+  return true;
+}
+
+// One XCD's share: the smallest makespan (to 0.5%) best-fit decreasing
+// reaches; false when no makespan fits (a slot would need more than 255
+// tiles of one product).
+bool pack_xcd(const int64_t k[3], const double dur[3], uint8_t c[kSlotsPerXcd][3], int *used) {
+  const double gap = 1.0;
+  int order[3] = {0, 1, 2};
+  for (int a = 0; a < 3; ++a)   // longest tiles first
+    for (int b = a + 1; b < 3; ++b)
+      if (dur[order[b]] > dur[order[a]]) {
+        const int t = order[a];
+        order[a] = order[b];
+        order[b] = t;
+      }
+  double total = 0.0, longest = 0.0;
+  for (int j = 0; j < 3; ++j) {
+    total += double(k[j]) * (dur[j] + gap);
+    if (k[j] > 0 && dur[j] + gap > longest) longest = dur[j] + gap;
+  }
+  if (total == 0.0) {
+    *used = 0;
+    for (int s = 0; s < kSlotsPerXcd; ++s) c[s][0] = c[s][1] = c[s][2] = 0;
+    return true;
+  }
+  double lo = total / kSlotsPerXcd > longest ? total / kSlotsPerXcd : longest;
+  double hi = lo;
+  uint8_t tmp[kSlotsPerXcd][3];
+  int u = 0;
+  while (!pack_under(k, dur, order, hi, gap, tmp, &u)) {
+    hi *= 1.125;
+    if (hi > 2.0 * total + longest) return false;   // counts beyond 255 per slot
+  }
+  for (int s = 0; s < kSlotsPerXcd; ++s)
+    for (int j = 0; j < 3; ++j) c[s][j] = tmp[s][j];
+  *used = u;
+  for (int it = 0; it < 10 && hi - lo > 0.005 * lo; ++it) {
+    const double mid = 0.5 * (lo + hi);
+    if (pack_under(k, dur, order, mid, gap, tmp, &u)) {
+      hi = mid;
+      for (int s = 0; s < kSlotsPerXcd; ++s)
+        for (int j = 0; j < 3; ++j) c[s][j] = tmp[s][j];
+      *used = u;
+    } else {
+      lo = mid;
+    }
+  }
+  return true;
+}
+
+}  // namespace
+
+bool pack_tiles(const int64_t n[3], const double dur[3], PackCounts *out, int *slots,
+                double *makespan) {
+  // XCDs with the same tile counts get the same packing
+  int64_t seen[kPackXcds][3];
+  uint8_t packed[kPackXcds][kSlotsPerXcd][3];
+  int used[kPackXcds];
+  int n_seen = 0, most = 0;
+  for (int x = 0; x < kPackXcds; ++x) {
+    int64_t k[3];
+    for (int j = 0; j < 3; ++j) k[j] = n[j] / kPackXcds + (x < n[j] % kPackXcds ? 1 : 0);
+    int m = -1;
+    for (int i = 0; i < n_seen; ++i)
+      if (seen[i][0] == k[0] && seen[i][1] == k[1] && seen[i][2] == k[2]) m = i;
+    if (m < 0) {
+      m = n_seen++;
+      for (int j = 0; j < 3; ++j) seen[m][j] = k[j];
+      if (!pack_xcd(k, dur, packed[m], &used[m])) return false;
+    }
+    for (int s = 0; s < kSlotsPerXcd; ++s)
+      for (int j = 0; j < 3; ++j) out->c[kPackXcds * s + x][j] = packed[m][s][j];
+    if (used[m] > most) most = used[m];
+  }
+  *slots = most;
+  if (makespan) {
+    double worst = 0.0;
+    for (int b = 0; b < kPackSlots; ++b) {
+      double load = 0.0;
+      for (int j = 0; j < 3; ++j) load += double(out->c[b][j]) * (dur[j] + 1.0);
+      if (load > worst) worst = load;
+    }
+    *makespan = worst;
+  }
+  return true;
 }
 
 int32_t plan_distill(int64_t n, int64_t V, DistillPlan *p) {

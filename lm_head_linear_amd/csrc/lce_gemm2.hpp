@@ -32,10 +32,12 @@
 #include <type_traits>
 
 #include "lce_gemm.hpp"
+#include "lce_internal.h"
 
 namespace lce {
 
 typedef short shortx4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef __attribute__((address_space(3))) void lds_void_t;
 typedef __attribute__((address_space(3))) shortx4 lds_shortx4_t;
 
@@ -155,6 +157,31 @@ struct PipeOperand {
     }
   }
 
+  // MN-major reads issued by hand (mn_frag_addr / mn_frag_issue): the LDS
+  // address of the fragment of tile rows base..base+31 at k-substep 0 of the
+  // stage at `src`; substep kk adds kk * 16 k-rows of 512 bytes, the second
+  // half of the fragment 4 k-rows more (both fit the instruction's offset).
+  __device__ inline uint32_t mn_frag_addr(const char *src, int base, int lane) const {
+    static_assert(!KMAJOR, "MN-major operands only");
+    const int g = lane >> 4, i = lane & 15;
+    const int mn = base + 16 * (g & 1) + 4 * (i & 3);
+    const int krow = 8 * (g >> 1) + (i >> 2);
+    const char *a = src + krow * 512 + (((mn >> 3) ^ mswz2(krow)) << 4) + (mn & 7) * 2;
+    // generic -> LDS address space: the 32-bit LDS byte address
+    return uint32_t(reinterpret_cast<uintptr_t>((const __attribute__((address_space(3))) char *)a));
+  }
+  // Two ds_read_b64_tr_b16 of substep KK at `addr`.  The caller waits
+  // (lgkmcnt) before using the result: the compiler does not track these
+  // reads, and so does not make them wait for the stage loads in flight.
+  template <int KK>
+  __device__ __forceinline__ static void mn_frag_issue(u32x4 &out, uint32_t addr) {
+    u32x2 lo, hi;
+    asm volatile("ds_read_b64_tr_b16 %0, %1 offset:%2" : "=v"(lo) : "v"(addr), "n"(KK * 8192));
+    asm volatile("ds_read_b64_tr_b16 %0, %1 offset:%2"
+                 : "=v"(hi) : "v"(addr), "n"(KK * 8192 + 2048));
+    out = u32x4{lo[0], lo[1], hi[0], hi[1]};
+  }
+
   // The 32x32x16 MFMA operand of tile rows base..base+31 for k-substep kk.
   __device__ inline u32x4 frag(const char *src, int base, int kk, int lane) const {
     if (KMAJOR) {
@@ -191,6 +218,24 @@ struct Gemm2Params {
   int64_t tiles_n;
   const int32_t *bad;
 };
+
+// f(std::integral_constant<int, I>) for I = B .. E-1, in order.
+template <int B, int E, class F>
+__device__ __forceinline__ void static_for(F &&f) {
+  if constexpr (B < E) {
+    f(std::integral_constant<int, B>{});
+    static_for<B + 1, E>(f);
+  }
+}
+
+// Waits for every LDS read in flight and ties the fragments to the wait, so
+// that no MFMA reading them is scheduled above it.
+template <int FM, int FN>
+__device__ __forceinline__ void wait_frags(u32x4 (&a)[FM], u32x4 (&b)[FN]) {
+  static_assert(FM == 4 && FN == 2, "8-wave 128 x 64 wave tile");
+  asm volatile("s_waitcnt lgkmcnt(0)"
+               : "+v"(a[0]), "+v"(a[1]), "+v"(a[2]), "+v"(a[3]), "+v"(b[0]), "+v"(b[1]));
+}
 
 // s_waitcnt lgkmcnt(0) vmcnt(N) followed by a bare s_barrier: unlike
 // __syncthreads this leaves the N most recent loads in flight.
@@ -230,13 +275,11 @@ template <class CFG, class Epi> constexpr int gemm2_lds_bytes() {
   return CFG::STAGES * CFG::STAGE_BYTES + EpiPrefetch<Epi>::bytes;
 }
 
-// One workgroup of a product: `bid` of `nb` workgroups of this product, of
-// which the first `nreal` logical ones carry work (nb may be padded to a
-// multiple of the XCD count so that a following product keeps its XCD
-// mapping); `smem` at least gemm2_lds_bytes<CFG, Epi>() bytes (1 KB aligned).
+// One tile of a product: logical index LS (split-major over (split, tile));
+// `smem` at least gemm2_lds_bytes<CFG, Epi>() bytes (1 KB aligned).
 template <class CFG, class TR, bool AK, bool BKM, class Epi>
-__device__ __forceinline__ void gemm2_block(const Gemm2Params &g, const Epi &epi, int64_t bid,
-                                            int64_t nb, int64_t nreal, char *smem) {
+__device__ __forceinline__ void gemm2_tile(const Gemm2Params &g, const Epi &epi, int64_t LS,
+                                           char *smem) {
   constexpr int BK = CFG::BK, STAGES = CFG::STAGES, KSUB = CFG::KSUB;
   constexpr int NWAVES = TR::NT / 64;
   typedef PipeOperand<CFG, NWAVES, AK> OpA;
@@ -255,12 +298,7 @@ __device__ __forceinline__ void gemm2_block(const Gemm2Params &g, const Epi &epi
   const int wave = tid >> 6;
   const int wm = wave / TR::WAVES_N, wn = wave % TR::WAVES_N;
 
-  // One flat grid over (split, tile), split-major, dealt to the XCDs in
-  // contiguous ranges: an XCD's workgroups share whole K-splits, so each
-  // split's operand rows are fetched into one L2 only.
   const int64_t tiles = (g.M + CFG::BM - 1) / CFG::BM * g.tiles_n;
-  const int64_t LS = xcd_remap(bid, nb);
-  if (LS >= nreal) return;   // padding
   const int split = int(LS / tiles);
   const int64_t L = LS % tiles;
   const int64_t m0 = (L / g.tiles_n) * CFG::BM;
@@ -302,13 +340,74 @@ __device__ __forceinline__ void gemm2_block(const Gemm2Params &g, const Epi &epi
   }
   wait_vm_barrier_stages<LPS, STAGES - 1>(n_k - 1);
   u32x4 fa[2][TR::FM], fb[2][TR::FN];
-  if (n_k > 0) {
+  // Both operands MN-major: fragments come from hand-issued transposing reads
+  // (see mn_step); their lane addresses within a stage are fixed.
+  constexpr bool MNMN = !AK && !BKM;
+  uint32_t a_off[TR::FM], b_off[TR::FN];
+  if constexpr (MNMN) {
 #pragma unroll
-    for (int f = 0; f < TR::FM; ++f) fa[0][f] = pa.frag(smem, wm * TR::WTM + f * 32, 0, lane);
+    for (int f = 0; f < TR::FM; ++f) a_off[f] = pa.mn_frag_addr(smem, wm * TR::WTM + f * 32, lane);
 #pragma unroll
     for (int f = 0; f < TR::FN; ++f)
-      fb[0][f] = pb.frag(smem + CFG::OP_BYTES, wn * TR::WTN + f * 32, 0, lane);
+      b_off[f] = pb.mn_frag_addr(smem + CFG::OP_BYTES, wn * TR::WTN + f * 32, lane);
   }
+  if (n_k > 0) {
+    if constexpr (MNMN) {
+#pragma unroll
+      for (int f = 0; f < TR::FM; ++f) OpA::template mn_frag_issue<0>(fa[0][f], a_off[f]);
+#pragma unroll
+      for (int f = 0; f < TR::FN; ++f) OpB::template mn_frag_issue<0>(fb[0][f], b_off[f]);
+    } else {
+#pragma unroll
+      for (int f = 0; f < TR::FM; ++f) fa[0][f] = pa.frag(smem, wm * TR::WTM + f * 32, 0, lane);
+#pragma unroll
+      for (int f = 0; f < TR::FN; ++f)
+        fb[0][f] = pb.frag(smem + CFG::OP_BYTES, wn * TR::WTN + f * 32, 0, lane);
+    }
+  }
+
+  // One k-step of an MN-major x MN-major product.  Same dataflow as `step`
+  // below, in a fixed instruction order: at each substep, wait for the
+  // fragments read during the previous one, then alternate one MFMA with one
+  // fragment (two transposing reads) of the next substep.  The compiler does
+  // not see these reads, so it does not hold them until the next stage's
+  // loads have landed (which would expose the whole load latency each step).
+  auto mn_step = [&](const int it, auto steady_tag) {
+    constexpr bool STEADY = decltype(steady_tag)::value;
+    constexpr int NFR = TR::FM + TR::FN;   // fragments read per substep
+    const uint32_t sa = uint32_t((it % CFG::STAGES) * CFG::STAGE_BYTES);
+    const uint32_t sn = uint32_t(((it + 1) % CFG::STAGES) * CFG::STAGE_BYTES);
+    char *sa_p = smem + sa;
+    static_for<0, CFG::KSUB>([&](auto kkc) {
+      constexpr int kk = decltype(kkc)::value;
+      constexpr int cur = kk & 1, nxt = cur ^ 1;
+      constexpr bool last = kk == CFG::KSUB - 1;
+      constexpr int ks = last ? 0 : kk + 1;
+      const uint32_t so = last ? sn : sa;
+      const bool reads = !last || STEADY || it + 1 < n_k;
+      wait_frags<TR::FM, TR::FN>(fa[cur], fb[cur]);
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int i = 0; i < TR::FM * TR::FN; ++i) {
+        const int fm = i / TR::FN, fn = i % TR::FN;
+        acc[fm][fn] = mfma32<TR>(fa[cur][fm], fb[cur][fn], acc[fm][fn]);
+        if (i < NFR && reads) {
+          if (i < TR::FM) OpA::template mn_frag_issue<ks>(fa[nxt][i], a_off[i] + so);
+          else OpB::template mn_frag_issue<ks>(fb[nxt][i - TR::FM], b_off[i - TR::FM] + so);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      if constexpr (kk == CFG::KSUB - 2) {
+        if (STEADY) wait_vm_barrier<LPS * (CFG::STAGES - 2)>();
+        else wait_vm_barrier_stages<LPS, CFG::STAGES - 2>(n_k - 2 - it);
+        if (STEADY || it + CFG::STAGES < n_k) {
+          pa.issue(k_begin + int64_t(it + CFG::STAGES) * CFG::BK, sa_p, wave);
+          pb.issue(k_begin + int64_t(it + CFG::STAGES) * CFG::BK, sa_p + CFG::OP_BYTES, wave);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    });
+  };
 
   // One k-step of BK = KSUB MFMA k-substeps.  Substep kk computes on the
   // fragments read during substep kk-1 while reading those of kk+1 (of the
@@ -366,8 +465,13 @@ __device__ __forceinline__ void gemm2_block(const Gemm2Params &g, const Epi &epi
     }
   };
   int it = 0;
-  for (; it + STAGES < n_k; ++it) step(it, std::true_type{});
-  for (; it < n_k; ++it) step(it, std::false_type{});
+  if constexpr (MNMN) {
+    for (; it + STAGES < n_k; ++it) mn_step(it, std::true_type{});
+    for (; it < n_k; ++it) mn_step(it, std::false_type{});
+  } else {
+    for (; it + STAGES < n_k; ++it) step(it, std::true_type{});
+    for (; it < n_k; ++it) step(it, std::false_type{});
+  }
 
   int lane_e = lane, wm_e = wm, wn_e = wn;
   int64_t m0_e = m0, n0_e = n0;
@@ -384,6 +488,20 @@ __device__ __forceinline__ void gemm2_block(const Gemm2Params &g, const Epi &epi
   } else {
     epi(acc, m0_e, n0_e, wm_e, wn_e, lane_e, split);
   }
+}
+
+// One workgroup of a product: `bid` of `nb` workgroups of this product, of
+// which the first `nreal` logical ones carry work (nb may be padded to a
+// multiple of the XCD count so that a following product keeps its XCD
+// mapping).  One flat grid over (split, tile), split-major, dealt to the XCDs
+// in contiguous ranges: an XCD's workgroups share whole K-splits, so each
+// split's operand rows are fetched into one L2 only.
+template <class CFG, class TR, bool AK, bool BKM, class Epi>
+__device__ __forceinline__ void gemm2_block(const Gemm2Params &g, const Epi &epi, int64_t bid,
+                                            int64_t nb, int64_t nreal, char *smem) {
+  const int64_t LS = xcd_remap(bid, nb);
+  if (LS >= nreal) return;   // padding
+  gemm2_tile<CFG, TR, AK, BKM, Epi>(g, epi, LS, smem);
 }
 
 template <class CFG, class TR, bool AK, bool BKM, class Epi>
@@ -574,6 +692,56 @@ __global__ void __launch_bounds__(TR::NT) gemm2_multi_kernel(J0 j0, J1 j1, J2 j2
   b -= j1.nb;
   gemm2_block<typename J2::CFG, TR, J2::AK, J2::BKM>(j2.g, j2.e, b, j2.nb, j2.nreal,
                                                                      smem);
+}
+
+// A packed launch (PackCounts): slot b = 8 s + x (slot s of XCD x) runs
+// c[b][j] tiles of product j, taken in order from the XCD's contiguous range
+// of that product's logical tiles, after the tiles of the same product that
+// the XCD's earlier slots run.
+// First logical tile of XCD x's range when n tiles are dealt to 8 XCDs in
+// contiguous ranges (the larger ranges first).
+__device__ inline int64_t xcd_range_lo(int64_t n, int x) {
+  const int64_t q = n / 8, r = n % 8;
+  return x < r ? x * (q + 1) : r * (q + 1) + (x - r) * q;
+}
+
+// Three independent products, packed: each workgroup (one per compute unit)
+// runs the list of tiles its slot holds, so that long and short tiles share
+// compute units as a host-side bin packing decided instead of in dispatch
+// order.  Every logical tile of every product is run exactly once when the
+// counts of each XCD sum to that XCD's range; indices past a range are
+// skipped.
+template <class TR, class J0, class J1, class J2>
+__global__ void __launch_bounds__(TR::NT) gemm2_packed_kernel(J0 j0, J1 j1, J2 j2,
+                                                              PackCounts pc) {
+  constexpr int B0 = gemm2_lds_bytes<typename J0::CFG, typename J0::Epi>();
+  constexpr int B1 = gemm2_lds_bytes<typename J1::CFG, typename J1::Epi>();
+  constexpr int B2 = gemm2_lds_bytes<typename J2::CFG, typename J2::Epi>();
+  constexpr int B01 = B0 > B1 ? B0 : B1;
+  __shared__ __attribute__((aligned(1024))) char smem[B01 > B2 ? B01 : B2];
+  const int b = blockIdx.x, x = b % 8, s = b / 8;
+  int off0 = 0, off1 = 0, off2 = 0;
+  for (int t = 0; t < s; ++t) {
+    off0 += pc.c[8 * t + x][0];
+    off1 += pc.c[8 * t + x][1];
+    off2 += pc.c[8 * t + x][2];
+  }
+  bool first = true;
+  auto run = [&](const auto &job, int n_here, int off) {
+    typedef typename std::remove_reference<decltype(job)>::type J;
+    const int64_t n = job.nreal;
+    const int64_t lo = xcd_range_lo(n, x), hi = xcd_range_lo(n, x + 1);
+    for (int i = 0; i < n_here; ++i) {
+      const int64_t LS = lo + off + i;
+      if (LS >= hi) break;
+      if (!first) __syncthreads();   // the previous tile's epilogue is done with the LDS
+      first = false;
+      gemm2_tile<typename J::CFG, TR, J::AK, J::BKM>(job.g, job.e, LS, smem);
+    }
+  };
+  run(j0, pc.c[b][0], off0);
+  run(j1, pc.c[b][1], off1);
+  run(j2, pc.c[b][2], off2);
 }
 
 }  // namespace lce

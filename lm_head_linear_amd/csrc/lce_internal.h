@@ -52,10 +52,12 @@ struct CEPlan {
   int64_t pn_slabs = 0;
   int64_t pslab0 = 0;         // rows of the first slab (<= pslab; the others pslab)
   int64_t pdh_splits = 0;
+  bool ppacked = false;       // launches packed onto the compute units (pack_tiles)
   // modelled duration (k-rows of a 256x256 tile on one compute unit) of the
   // two-call algorithm and of the single call that keeps the logits (16-bit
   // inputs; 0 when not modelled)
   int64_t model_two = 0, model_single = 0;
+  double model_bwd_us = 0.0;  // packed-launch model of the 16-bit backward (us)
   // workspace layout (byte offsets)
   size_t off_partials = 0, off_zy = 0, off_losstok = 0;
   size_t off_dbuf = 0, off_dhacc = 0;
@@ -72,6 +74,34 @@ struct CEPlan {
   size_t off_fz = 0, off_fdh = 0, off_fht = 0, off_fyloc = 0;
   size_t f_total = 0;         // workspace of the single call (>= total)
 };
+
+// Tile counts per workgroup slot of a packed multi-product launch: slot
+// b = 8 s + x is slot s of XCD x (the hardware deals workgroup b to XCD
+// b % 8); it runs c[b][j] tiles of product j.
+constexpr int kPackSlots = 256;
+constexpr int kPackXcds = 8;
+struct PackCounts {
+  uint8_t c[kPackSlots][3];
+};
+
+// Packs the tiles of three independent products -- n[j] tiles of modelled
+// duration dur[j] each (any unit), dealt to the XCDs in contiguous ranges --
+// onto the 32 slots of every XCD so that the longest slot is as short as a
+// best-fit-decreasing packing under a bisected makespan target gets it.
+// *slots = slots used on the busiest XCD.  Returns false (and the caller
+// keeps hardware dispatch) when a slot would hold more than 255 tiles of one
+// product.
+bool pack_tiles(const int64_t n[3], const double dur[3], PackCounts *out, int *slots,
+                double *makespan = nullptr);
+
+// Modelled duration (microseconds) of one 256 x 256 tile of each backward
+// product on the 16-bit pipelined core: 1.43 us per 64-deep k-step of a
+// K-major product and 1.71 for the MN-major d_hidden product, plus the
+// epilogue and the pipeline fill (measured per tile at 2048 x 1024 x 151936).
+inline double tile_us_dhidden(int64_t k_per_split) { return 11.8 + 1.71 * double((k_per_split + 63) / 64); }
+inline double tile_us_dweight(int64_t n_tok) { return 5.2 + 1.43 * double((n_tok + 63) / 64); }
+inline double tile_us_dlogit(int64_t d_model) { return 11.8 + 1.43 * double((d_model + 63) / 64); }
+constexpr double kLaunchUs = 5.0;
 
 // Fills *p; returns LCE_OK or a refusal status.
 int32_t plan_ce(int64_t n, int64_t D, int64_t V, int64_t chunk, int32_t dtype, CEPlan *p);
