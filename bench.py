@@ -502,12 +502,12 @@ class ClockSampler:
         import numpy as np
         out = {"samples": len(self.clk)}
         if self.clk:
-            # the first samples may precede the load
-            c = np.array(self.clk[len(self.clk) // 5:])
+            # the telemetry lags the load: keep the second half of the samples
+            c = np.array(self.clk[len(self.clk) // 2:])
             out.update({"gfx_mhz_median": float(np.median(c)), "gfx_mhz_min": float(np.min(c)),
                         "gfx_mhz_max": float(np.max(c))})
         if self.power:
-            pw = np.array(self.power[len(self.power) // 5:])
+            pw = np.array(self.power[len(self.power) // 2:])
             out["socket_power_w_median"] = float(np.median(pw))
         if self.error:
             out["error"] = self.error
@@ -536,8 +536,12 @@ def mfma_ceiling_measure(torch, np, dev, fwd_tflops=None):
         torch.cuda.synchronize()
         iters = 40
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        # about 1.5 s of back-to-back products; the telemetry lags, so the
+        # sampler's summary keeps the later samples, and the time is that of
+        # the last round
         with ClockSampler() as cs:
-            for _ in range(4):           # ~0.7 s per round at ~1.3 PFLOP/s
+            t_end = time.perf_counter() + 1.5
+            while time.perf_counter() < t_end:
                 e0.record()
                 for _ in range(iters):
                     torch.matmul(a, b, out=c)

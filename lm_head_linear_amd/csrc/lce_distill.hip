@@ -206,6 +206,35 @@ __device__ __forceinline__ void distill_row(const T *S, const T *U, const uint8_
                                             double grad_out, const Control *ctl, T *grad,
                                             double *row_out);
 
+// The 16-byte chunks i = tid, tid + kBlock, ... (below nvec) of one row (b ==
+// nullptr) or of two rows at once, with kStreamBatch chunks per row and
+// thread in flight before any is consumed (a load per thread and row at a
+// time leaves the memory system too few bytes in flight to reach its
+// bandwidth); f(i, chunk of a, chunk of b) runs for ascending i.
+constexpr int kStreamBatch = 4;
+template <class T, class F>
+__device__ __forceinline__ void stream_chunks(const T *a, const T *b, int64_t nvec, int tid,
+                                              F &&f) {
+  constexpr int B = kStreamBatch;
+  for (int64_t i0 = tid; i0 < nvec; i0 += int64_t(B) * kBlock) {
+    u32x4 va[B], vb[B];
+#pragma unroll
+    for (int k = 0; k < B; ++k) {
+      const int64_t i = i0 + int64_t(k) * kBlock;
+      va[k] = vb[k] = u32x4{0u, 0u, 0u, 0u};
+      if (i < nvec) {
+        va[k] = *reinterpret_cast<const u32x4 *>(a + i * 8);
+        if (b) vb[k] = *reinterpret_cast<const u32x4 *>(b + i * 8);
+      }
+    }
+#pragma unroll
+    for (int k = 0; k < B; ++k) {
+      const int64_t i = i0 + int64_t(k) * kBlock;
+      if (i < nvec) f(i, va[k], vb[k]);
+    }
+  }
+}
+
 template <class T, int OBJ, bool VEC>
 __global__ void __launch_bounds__(kBlock)
 distill_row_kernel(const T *S, const T *U, const uint8_t *mask, int64_t n, int64_t V,
@@ -263,13 +292,24 @@ __device__ __forceinline__ void distill_row(const T *S, const T *U, const uint8_
       else fx.a += ex * (xs[i] - ys[i]);
     }
   };
-  for (int64_t i = tid; i < nvec; i += kBlock) {
-    C xs[8], ys[8];
-    IO<T>::load8(s_row + i * 8, xs);
-    IO<T>::load8(u_row + i * 8, ys);
+  if constexpr (sizeof(T) == 2) {
+    stream_chunks(s_row, u_row, nvec, tid, [&](int64_t, u32x4 cs, u32x4 cu) {
+      C xs[8], ys[8];
+      IO<T>::unpack8(cs, xs);
+      IO<T>::unpack8(cu, ys);
 #pragma unroll
-    for (int j = 0; j < 8; ++j) { xs[j] *= iT; ys[j] *= iT; }
-    consume(xs, ys, 8);
+      for (int j = 0; j < 8; ++j) { xs[j] *= iT; ys[j] *= iT; }
+      consume(xs, ys, 8);
+    });
+  } else {
+    for (int64_t i = tid; i < nvec; i += kBlock) {
+      C xs[8], ys[8];
+      IO<T>::load8(s_row + i * 8, xs);
+      IO<T>::load8(u_row + i * 8, ys);
+#pragma unroll
+      for (int j = 0; j < 8; ++j) { xs[j] *= iT; ys[j] *= iT; }
+      consume(xs, ys, 8);
+    }
   }
   for (int64_t v = tail0 + tid; v < V; v += kBlock) {
     C xs[1] = {IO<T>::load1(s_row + v) * iT}, ys[1] = {IO<T>::load1(u_row + v) * iT};
@@ -308,13 +348,24 @@ __device__ __forceinline__ void distill_row(const T *S, const T *U, const uint8_
     else d = p - dexp<C>(y - lse_y);
     return scale * (d + zc * p);
   };
-  for (int64_t i = tid; i < nvec; i += kBlock) {
-    C xs[8], ys[8], gs[8];
-    IO<T>::load8(s_row + i * 8, xs);
-    IO<T>::load8(u_row + i * 8, ys);
+  if constexpr (sizeof(T) == 2) {
+    stream_chunks(s_row, u_row, nvec, tid, [&](int64_t i, u32x4 cs, u32x4 cu) {
+      C xs[8], ys[8], gs[8];
+      IO<T>::unpack8(cs, xs);
+      IO<T>::unpack8(cu, ys);
 #pragma unroll
-    for (int j = 0; j < 8; ++j) gs[j] = grad_of(xs[j] * iT, ys[j] * iT);
-    IO<T>::store8(g_row + i * 8, gs);
+      for (int j = 0; j < 8; ++j) gs[j] = grad_of(xs[j] * iT, ys[j] * iT);
+      IO<T>::store8(g_row + i * 8, gs);
+    });
+  } else {
+    for (int64_t i = tid; i < nvec; i += kBlock) {
+      C xs[8], ys[8], gs[8];
+      IO<T>::load8(s_row + i * 8, xs);
+      IO<T>::load8(u_row + i * 8, ys);
+#pragma unroll
+      for (int j = 0; j < 8; ++j) gs[j] = grad_of(xs[j] * iT, ys[j] * iT);
+      IO<T>::store8(g_row + i * 8, gs);
+    }
   }
   for (int64_t v = tail0 + tid; v < V; v += kBlock)
     IO<T>::store1(g_row + v, grad_of(IO<T>::load1(s_row + v) * iT, IO<T>::load1(u_row + v) * iT));
@@ -352,10 +403,19 @@ __device__ __forceinline__ void label_row(const T *Z, const int64_t *y, const ui
     f.m = nm;
     for (int i = 0; i < cnt; ++i) f.s += dexp<C>(xs[i] - nm);
   };
-  for (int64_t i = tid; i < nvec; i += kBlock) {
-    C xs[8];
-    IO<T>::load8(z_row + i * 8, xs);
-    consume(xs, 8);
+  if constexpr (sizeof(T) == 2) {
+    stream_chunks(z_row, static_cast<const T *>(nullptr), nvec, tid,
+                  [&](int64_t, u32x4 cz, u32x4) {
+                    C xs[8];
+                    IO<T>::unpack8(cz, xs);
+                    consume(xs, 8);
+                  });
+  } else {
+    for (int64_t i = tid; i < nvec; i += kBlock) {
+      C xs[8];
+      IO<T>::load8(z_row + i * 8, xs);
+      consume(xs, 8);
+    }
   }
   for (int64_t v = tail0 + tid; v < V; v += kBlock) {
     const C xs[1] = {IO<T>::load1(z_row + v)};
@@ -378,12 +438,25 @@ __device__ __forceinline__ void label_row(const T *Z, const int64_t *y, const ui
     const int64_t cnt = ctl->count;
     const C g = cnt ? C(grad_out / double(cnt)) : C(0);
     const C a = g * (C(1) + C(2.0 * z_coef) * lse);
-    for (int64_t i = tid; i < nvec; i += kBlock) {
-      C xs[8], gs[8];
-      IO<T>::load8(z_row + i * 8, xs);
+    auto grad8 = [&](int64_t i, const C *xs) {
+      C gs[8];
 #pragma unroll
       for (int j = 0; j < 8; ++j) gs[j] = a * dexp<C>(xs[j] - lse) - (i * 8 + j == yt ? g : C(0));
       IO<T>::store8(g_row + i * 8, gs);
+    };
+    if constexpr (sizeof(T) == 2) {
+      stream_chunks(z_row, static_cast<const T *>(nullptr), nvec, tid,
+                    [&](int64_t i, u32x4 cz, u32x4) {
+                      C xs[8];
+                      IO<T>::unpack8(cz, xs);
+                      grad8(i, xs);
+                    });
+    } else {
+      for (int64_t i = tid; i < nvec; i += kBlock) {
+        C xs[8];
+        IO<T>::load8(z_row + i * 8, xs);
+        grad8(i, xs);
+      }
     }
     for (int64_t v = tail0 + tid; v < V; v += kBlock)
       IO<T>::store1(g_row + v, a * dexp<C>(IO<T>::load1(z_row + v) - lse) - (v == yt ? g : C(0)));

@@ -293,7 +293,10 @@ __device__ __forceinline__ void gemm2_tile(const Gemm2Params &g, const Epi &epi,
   constexpr int PRE = EpiPrefetch<Epi>::bytes;
   char *const pre_lds = smem + STAGES * CFG::STAGE_BYTES;
 
-  const int tid = threadIdx.x;
+  // (opaque: a workgroup running several tiles recomputes its per-lane set-up
+  // per tile instead of holding every product's across the whole loop)
+  int tid = threadIdx.x;
+  asm volatile("" : "+v"(tid));
   const int lane = tid & 63;
   const int wave = tid >> 6;
   const int wm = wave / TR::WAVES_N, wn = wave % TR::WAVES_N;
