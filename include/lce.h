@@ -17,9 +17,13 @@
  *   590 are this library's extensions inside that range.  Nothing throws or
  *   aborts.  On any refusal no output is modified.
  * Ownership: the caller owns every buffer, including the workspace.  The
- *   library allocates no device memory, keeps no pointer after returning and
- *   holds no global state, so calls are reentrant given distinct workspaces.
- *   Calls that share one workspace must be ordered (same stream).
+ *   library allocates no device memory and keeps no pointer after returning.
+ *   Its only state between calls: the backward's launch plan, memoized per
+ *   shape (the first call on a new shape spends a few milliseconds of host
+ *   time choosing it), and the static scratch of
+ *   lce_distill_fwd_bwd_noalloc.  Neither changes a result; calls are
+ *   reentrant given distinct workspaces.  Calls that share one workspace must
+ *   be ordered (same stream).
  * Streams: device work is enqueued on the caller's stream (a hipStream_t
  *   passed as void*; NULL = the null stream).  Calls that hand back device
  *   scalars (lce_forward with a non-NULL out, lce_distill_fwd_bwd, ...)
