@@ -32,6 +32,7 @@
 #include <hip/hip_runtime.h>
 
 #include <mutex>
+#include <type_traits>
 
 #include <climits>
 #include <cmath>
@@ -206,21 +207,24 @@ __device__ __forceinline__ void distill_row(const T *S, const T *U, const uint8_
                                             double grad_out, const Control *ctl, T *grad,
                                             double *row_out);
 
-// The 16-byte chunks i = tid, tid + kBlock, ... (below nvec) of one row (b ==
+// The 16-byte chunks i = tid, tid + NT, ... (below nvec) of one row (b ==
 // nullptr) or of two rows at once, with kStreamBatch chunks per row and
 // thread in flight before any is consumed (a load per thread and row at a
 // time leaves the memory system too few bytes in flight to reach its
 // bandwidth); f(i, chunk of a, chunk of b) runs for ascending i.
 constexpr int kStreamBatch = 4;
-template <class T, class F>
+template <int NT = kBlock, class T, class F>
 __device__ __forceinline__ void stream_chunks(const T *a, const T *b, int64_t nvec, int tid,
                                               F &&f) {
   constexpr int B = kStreamBatch;
-  for (int64_t i0 = tid; i0 < nvec; i0 += int64_t(B) * kBlock) {
+  const int64_t step = int64_t(B) * NT;
+  const int64_t n_batches = nvec > tid ? (nvec - tid + step - 1) / step : 0;
+  for (int64_t bi = 0; bi < n_batches; ++bi) {
+    const int64_t i0 = tid + bi * step;
     u32x4 va[B], vb[B];
 #pragma unroll
     for (int k = 0; k < B; ++k) {
-      const int64_t i = i0 + int64_t(k) * kBlock;
+      const int64_t i = i0 + int64_t(k) * NT;
       va[k] = vb[k] = u32x4{0u, 0u, 0u, 0u};
       if (i < nvec) {
         va[k] = *reinterpret_cast<const u32x4 *>(a + i * 8);
@@ -229,19 +233,212 @@ __device__ __forceinline__ void stream_chunks(const T *a, const T *b, int64_t nv
     }
 #pragma unroll
     for (int k = 0; k < B; ++k) {
-      const int64_t i = i0 + int64_t(k) * kBlock;
+      const int64_t i = i0 + int64_t(k) * NT;
       if (i < nvec) f(i, va[k], vb[k]);
     }
   }
 }
+
+template <class T, int OBJ>
+__device__ __forceinline__ void distill_row16(const T *S, const T *U, const uint8_t *mask,
+                                              int64_t t, int64_t V, double inv_T, double z_coef,
+                                              double grad_out, const Control *ctl, T *grad,
+                                              double *row_out);
 
 template <class T, int OBJ, bool VEC>
 __global__ void __launch_bounds__(kBlock)
 distill_row_kernel(const T *S, const T *U, const uint8_t *mask, int64_t n, int64_t V,
                    double inv_T, double z_coef, double grad_out, const Control *ctl, T *grad,
                    double *row_out) {
-  for (int64_t t = blockIdx.x; t < n; t += gridDim.x)
-    distill_row<T, OBJ, VEC>(S, U, mask, t, V, inv_T, z_coef, grad_out, ctl, grad, row_out);
+  for (int64_t t = blockIdx.x; t < n; t += gridDim.x) {
+    if constexpr (sizeof(T) == 2 && VEC)
+      distill_row16<T, OBJ>(S, U, mask, t, V, inv_T, z_coef, grad_out, ctl, grad, row_out);
+    else
+      distill_row<T, OBJ, VEC>(S, U, mask, t, V, inv_T, z_coef, grad_out, ctl, grad, row_out);
+  }
+}
+
+// 16-bit rows, vocabulary a multiple of 8 and 16-byte aligned rows: the same
+// statistics, objective and gradient as distill_row with the arithmetic
+// arranged to issue fewer vector instructions (the row is streamed twice, so
+// the work per element bounds the kernel as much as the memory does):
+//   * running maxima are kept in raw input units (T > 0 preserves the order),
+//     so each exponential is one fma and one exp2 with c = log2(e) / T folded
+//     in: e^(x - m_x) = 2^(s c - m_s c);
+//   * the maximum is updated, and the sums rescaled, once per batch of
+//     kStreamBatch chunks rather than once per chunk;
+//   * the gradient's scale, sign and z term fold into the exponent:
+//     objectives 0 and 1: g = kA 2^(s c + A) - kB 2^(u c + B) with
+//     A = log2|scale (1 + zc)| - lse_x log2(e), B = log2|scale| - lse_y log2(e);
+//     objective 2: g = kB 2^(s c + B') ((s - u) / T + K), B' = log2|scale| -
+//     lse_x log2(e), K = lse_y - lse_x - L + zc.
+struct OnlineRaw {
+  float m, s, a;   // raw-unit max, sum of 2^((v - m) c), weighted sum on the same max
+};
+
+// max(a, b, c) in one instruction.  (fmaxf on values loaded from memory costs
+// an extra canonicalizing instruction per value; these are finite logits, and
+// a NaN among them makes the row's statistics NaN either way.)
+__device__ __forceinline__ float max3_raw(float a, float b, float c) {
+  float r;
+  asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+  return r;
+}
+
+__device__ inline void raw_merge(OnlineRaw &v, const OnlineRaw &o, float c) {
+  const float M = fmaxf(v.m, o.m);
+  if (M == -INFINITY) return;
+  const float f1 = __builtin_amdgcn_exp2f((v.m - M) * c), f2 = __builtin_amdgcn_exp2f((o.m - M) * c);
+  v.s = v.s * f1 + o.s * f2;
+  v.a = v.a * f1 + o.a * f2;
+  v.m = M;
+}
+
+// Fixed-order block reduction of raw-unit statistics; thread 0 gets the result.
+__device__ inline void block_merge_raw(OnlineRaw &v, OnlineRaw *sh, float c) {
+  for (int o = 1; o < 64; o <<= 1) {
+    OnlineRaw w;
+    w.m = __shfl_xor(v.m, o);
+    w.s = __shfl_xor(v.s, o);
+    w.a = __shfl_xor(v.a, o);
+    raw_merge(v, w, c);
+  }
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  if (lane == 0) sh[wave] = v;
+  __syncthreads();
+  if (threadIdx.x == 0)
+    for (int w = 1; w < kBlock / 64; ++w) raw_merge(v, sh[w], c);
+}
+
+template <class T, int OBJ>
+__device__ __forceinline__ void distill_row16(const T *S, const T *U, const uint8_t *mask,
+                                              int64_t t, int64_t V, double inv_T, double z_coef,
+                                              double grad_out, const Control *ctl, T *grad,
+                                              double *row_out) {
+  constexpr int B = kStreamBatch;
+  const float L2E = 1.4426950408889634f, LN2 = 0.6931471805599453f;
+  const T *s_row = S + t * V;
+  const T *u_row = U + t * V;
+  T *g_row = grad + t * V;
+  const int tid = threadIdx.x;
+  const int64_t nvec = V / 8;
+  const float iT = float(inv_T);
+  const float c = float(inv_T * 1.4426950408889634);
+
+  if (mask && !mask[t]) {
+    const float z[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+    for (int64_t i = tid; i < nvec; i += kBlock) IO<T>::store8(g_row + i * 8, z);
+    if (tid == 0) { row_out[2 * t] = 0.0; row_out[2 * t + 1] = 0.0; }
+    return;
+  }
+  __syncthreads();   // the previous row's statistics are no longer read
+
+  // Pass 1: batches of B chunks per thread, loads first.
+  OnlineRaw fx{-INFINITY, 0.f, 0.f}, fy{-INFINITY, 0.f, 0.f};
+  for (int64_t i0 = tid; i0 < nvec; i0 += int64_t(B) * kBlock) {
+    u32x4 vs[B], vu[B];
+#pragma unroll
+    for (int k = 0; k < B; ++k) {
+      const int64_t i = i0 + int64_t(k) * kBlock;
+      vs[k] = vu[k] = u32x4{0u, 0u, 0u, 0u};
+      if (i < nvec) {
+        vs[k] = *reinterpret_cast<const u32x4 *>(s_row + i * 8);
+        vu[k] = *reinterpret_cast<const u32x4 *>(u_row + i * 8);
+      }
+    }
+    float xs[B][8], ys[B][8];
+    float bmx = fx.m, bmy = fy.m;   // running max, then this batch's values
+#pragma unroll
+    for (int k = 0; k < B; ++k) {
+      IO<T>::unpack8(vs[k], xs[k]);
+      IO<T>::unpack8(vu[k], ys[k]);
+      if (i0 + int64_t(k) * kBlock < nvec) {
+#pragma unroll
+        for (int j = 0; j < 8; j += 2) {
+          bmx = max3_raw(bmx, xs[k][j], xs[k][j + 1]);
+          bmy = max3_raw(bmy, ys[k][j], ys[k][j + 1]);
+        }
+      }
+    }
+    const float nmx = bmx, nmy = bmy;
+    const float rx = __builtin_amdgcn_exp2f((fx.m - nmx) * c);
+    const float ry = __builtin_amdgcn_exp2f((fy.m - nmy) * c);
+    fx.s *= rx; fx.a *= rx; fx.m = nmx;
+    fy.s *= ry; fy.a *= ry; fy.m = nmy;
+    const float bx = -nmx * c, by = -nmy * c;
+#pragma unroll
+    for (int k = 0; k < B; ++k) {
+      if (i0 + int64_t(k) * kBlock >= nvec) continue;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const float ex = __builtin_amdgcn_exp2f(fmaf(xs[k][j], c, bx));
+        const float ey = __builtin_amdgcn_exp2f(fmaf(ys[k][j], c, by));
+        fx.s += ex;
+        fy.s += ey;
+        if constexpr (OBJ == 0) fy.a = fmaf(ey, xs[k][j], fy.a);
+        else if constexpr (OBJ == 1) fy.a = fmaf(ey, ys[k][j] - xs[k][j], fy.a);
+        else fx.a = fmaf(ex, xs[k][j] - ys[k][j], fx.a);
+      }
+    }
+  }
+
+  __shared__ OnlineRaw sh_x[kBlock / 64], sh_y[kBlock / 64];
+  __shared__ float sh_stats[4];
+  block_merge_raw(fx, sh_x, c);
+  block_merge_raw(fy, sh_y, c);
+  if (tid == 0) {
+    // natural-log statistics of x = s / T and y = u / T
+    const float lse_x = (fx.m * c + __builtin_amdgcn_logf(fx.s)) * LN2;
+    const float lse_y = (fy.m * c + __builtin_amdgcn_logf(fy.s)) * LN2;
+    float L;
+    if constexpr (OBJ == 0) L = lse_x - iT * fy.a / fy.s;
+    else if constexpr (OBJ == 1) L = iT * fy.a / fy.s + lse_x - lse_y;
+    else L = iT * fx.a / fx.s + lse_y - lse_x;
+    sh_stats[0] = lse_x;
+    sh_stats[1] = lse_y;
+    sh_stats[2] = L;
+    row_out[2 * t] = double(L);
+    row_out[2 * t + 1] = double(lse_x);
+  }
+  __syncthreads();
+  const float lse_x = sh_stats[0], lse_y = sh_stats[1], L = sh_stats[2];
+  const int64_t cnt = ctl->count;
+  const float scale = cnt ? float(grad_out / double(cnt) * inv_T) : 0.f;
+  const float zc = float(2.0 * z_coef) * lse_x;
+  // exponent offsets and signs of the gradient's terms (log2 of 0 is -inf,
+  // which makes the term 0)
+  const float aA = scale * (1.f + zc);
+  const float offA = __builtin_amdgcn_logf(fabsf(aA)) - lse_x * L2E;
+  const float kA = aA < 0.f ? -1.f : 1.f;
+  const float offB = __builtin_amdgcn_logf(fabsf(scale)) - (OBJ == 2 ? lse_x : lse_y) * L2E;
+  const float kB = scale < 0.f ? -1.f : 1.f;
+  const float K = lse_y - lse_x - L + zc;
+
+  // Pass 2: gradient.  With a positive scale and 1 + zc > 0 (the usual case)
+  // the two terms combine with one subtraction.
+  auto pass2 = [&](auto plain_tag) {
+    constexpr bool PLAIN = decltype(plain_tag)::value;
+    stream_chunks(s_row, u_row, nvec, tid, [&](int64_t i, u32x4 cs, u32x4 cu) {
+      float xs[8], ys[8], gs[8];
+      IO<T>::unpack8(cs, xs);
+      IO<T>::unpack8(cu, ys);
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        if constexpr (OBJ == 2) {
+          const float p = __builtin_amdgcn_exp2f(fmaf(xs[j], c, offB));
+          const float f = fmaf(xs[j] - ys[j], iT, K);
+          gs[j] = PLAIN ? p * f : kB * p * f;
+        } else {
+          const float pa = __builtin_amdgcn_exp2f(fmaf(xs[j], c, offA));
+          const float qb = __builtin_amdgcn_exp2f(fmaf(ys[j], c, offB));
+          gs[j] = PLAIN ? pa - qb : fmaf(kA, pa, -kB * qb);
+        }
+      }
+      IO<T>::store8(g_row + i * 8, gs);
+    });
+  };
+  if (kB > 0.f && (OBJ == 2 || kA > 0.f)) pass2(std::true_type{});
+  else pass2(std::false_type{});
 }
 
 template <class T, int OBJ, bool VEC>
@@ -371,7 +568,7 @@ __device__ __forceinline__ void distill_row(const T *S, const T *U, const uint8_
     IO<T>::store1(g_row + v, grad_of(IO<T>::load1(s_row + v) * iT, IO<T>::load1(u_row + v) * iT));
 }
 
-template <class T, bool VEC, bool GRAD>
+template <class T, bool VEC, bool GRAD, int NT>
 __device__ __forceinline__ void label_row(const T *Z, const int64_t *y, const uint8_t *mask,
                                           int64_t t, int64_t V, double z_coef, double grad_out,
                                           const Control *ctl, T *grad, double *row_out) {
@@ -385,8 +582,8 @@ __device__ __forceinline__ void label_row(const T *Z, const int64_t *y, const ui
     if constexpr (GRAD) {
       T *g_row = grad + t * V;
       const C z[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-      for (int64_t i = tid; i < nvec; i += kBlock) IO<T>::store8(g_row + i * 8, z);
-      for (int64_t v = tail0 + tid; v < V; v += kBlock) IO<T>::store1(g_row + v, C(0));
+      for (int64_t i = tid; i < nvec; i += NT) IO<T>::store8(g_row + i * 8, z);
+      for (int64_t v = tail0 + tid; v < V; v += NT) IO<T>::store1(g_row + v, C(0));
     }
     if (tid == 0) { row_out[2 * t] = 0.0; row_out[2 * t + 1] = 0.0; }
     return;
@@ -404,26 +601,26 @@ __device__ __forceinline__ void label_row(const T *Z, const int64_t *y, const ui
     for (int i = 0; i < cnt; ++i) f.s += dexp<C>(xs[i] - nm);
   };
   if constexpr (sizeof(T) == 2) {
-    stream_chunks(z_row, static_cast<const T *>(nullptr), nvec, tid,
+    stream_chunks<NT>(z_row, static_cast<const T *>(nullptr), nvec, tid,
                   [&](int64_t, u32x4 cz, u32x4) {
                     C xs[8];
                     IO<T>::unpack8(cz, xs);
                     consume(xs, 8);
                   });
   } else {
-    for (int64_t i = tid; i < nvec; i += kBlock) {
+    for (int64_t i = tid; i < nvec; i += NT) {
       C xs[8];
       IO<T>::load8(z_row + i * 8, xs);
       consume(xs, 8);
     }
   }
-  for (int64_t v = tail0 + tid; v < V; v += kBlock) {
+  for (int64_t v = tail0 + tid; v < V; v += NT) {
     const C xs[1] = {IO<T>::load1(z_row + v)};
     consume(xs, 1);
   }
-  __shared__ Online<C> sh_f[kBlock / 64];
+  __shared__ Online<C> sh_f[NT / 64];
   __shared__ C sh_lse;
-  block_merge(f, sh_f);
+  block_merge<C, NT>(f, sh_f);
   const int64_t yt = y[t];
   if (tid == 0) {
     const C lse = f.m + dlog<C>(f.s);
@@ -445,20 +642,20 @@ __device__ __forceinline__ void label_row(const T *Z, const int64_t *y, const ui
       IO<T>::store8(g_row + i * 8, gs);
     };
     if constexpr (sizeof(T) == 2) {
-      stream_chunks(z_row, static_cast<const T *>(nullptr), nvec, tid,
-                    [&](int64_t i, u32x4 cz, u32x4) {
-                      C xs[8];
-                      IO<T>::unpack8(cz, xs);
-                      grad8(i, xs);
-                    });
+      stream_chunks<NT>(z_row, static_cast<const T *>(nullptr), nvec, tid,
+                          [&](int64_t i, u32x4 cz, u32x4) {
+                            C xs[8];
+                            IO<T>::unpack8(cz, xs);
+                            grad8(i, xs);
+                          });
     } else {
-      for (int64_t i = tid; i < nvec; i += kBlock) {
+      for (int64_t i = tid; i < nvec; i += NT) {
         C xs[8];
         IO<T>::load8(z_row + i * 8, xs);
         grad8(i, xs);
       }
     }
-    for (int64_t v = tail0 + tid; v < V; v += kBlock)
+    for (int64_t v = tail0 + tid; v < V; v += NT)
       IO<T>::store1(g_row + v, a * dexp<C>(IO<T>::load1(z_row + v) - lse) - (v == yt ? g : C(0)));
   }
 }
@@ -561,13 +758,16 @@ constexpr int kResidentChunks = 38;   // rows up to 8 * 38 * 512 = 155648 values
 
 // Rows t = blockIdx.x, + gridDim.x, ...; nothing runs when the guard found
 // an out-of-range target (the outputs stay untouched).
-template <class T, bool VEC, bool GRAD>
-__global__ void __launch_bounds__(kBlock)
+// NT threads per workgroup: 1024 (one per CU) when the row is read twice,
+// so the second read finds it in the Infinity Cache; 512 (two per CU, their
+// rows' phases interleaving) for the single read of the loss alone.
+template <class T, bool VEC, bool GRAD, int NT = kBlock>
+__global__ void __launch_bounds__(NT)
 label_row_kernel(const T *Z, const int64_t *y, const uint8_t *mask, int64_t n, int64_t V,
                  double z_coef, double grad_out, const Control *ctl, T *grad, double *row_out) {
   if (ctl->bad) return;
   for (int64_t t = blockIdx.x; t < n; t += gridDim.x)
-    label_row<T, VEC, GRAD>(Z, y, mask, t, V, z_coef, grad_out, ctl, grad, row_out);
+    label_row<T, VEC, GRAD, NT>(Z, y, mask, t, V, z_coef, grad_out, ctl, grad, row_out);
 }
 
 __global__ void distill_init_kernel(Control *ctl) {
@@ -680,8 +880,9 @@ void label_impl(bool vec, bool want_grad, const T *Z, const int64_t *y, const ui
       hipLaunchKernelGGL((label_row_kernel<T, true, true>), dim3(grid), dim3(kBlock), 0, st, Z, y,
                          mask, n, V, z, go, ctl, grad, rows);
     else if (vec)
-      hipLaunchKernelGGL((label_row_kernel<T, true, false>), dim3(grid), dim3(kBlock), 0, st, Z,
-                         y, mask, n, V, z, go, ctl, grad, rows);
+      hipLaunchKernelGGL((label_row_kernel<T, true, false, kBlock / 2>),
+                         dim3(unsigned(n < 2 * kRowGrid ? n : 2 * kRowGrid)), dim3(kBlock / 2), 0,
+                         st, Z, y, mask, n, V, z, go, ctl, grad, rows);
     else if (want_grad)
       hipLaunchKernelGGL((label_row_kernel<T, false, true>), dim3(grid), dim3(kBlock), 0, st, Z,
                          y, mask, n, V, z, go, ctl, grad, rows);
