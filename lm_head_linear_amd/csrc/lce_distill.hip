@@ -696,22 +696,43 @@ __device__ __forceinline__ void label_row_resident(const T *Z, const int64_t *y,
   for (int i = 0; i < CPT; ++i)
     if (tid + int64_t(i) * kResBlock < nvec)
       xr[i] = __builtin_amdgcn_raw_buffer_load_b128(ri, voff, i * kResBlock * 16, 0);
-  Online<float> f;
-  f.init();
+  // Pass 1 from the registers, in batches of four chunks: the raw running
+  // maximum is updated and the sums rescaled once per batch, each chunk of a
+  // batch adds into its own partial sum (independent add chains), and every
+  // exponential is one fma and one exp2 with log2(e) folded in.
+  const float L2E = 1.4426950408889634f;
+  constexpr int BB = 4;
+  float m = -INFINITY, ps[BB] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-  for (int i = 0; i < CPT; ++i) {
-    if (tid + int64_t(i) * kResBlock >= nvec) continue;
-    float xs[8];
-    IO<T>::unpack8(xr[i], xs);
-    float lm = xs[0];
+  for (int i0 = 0; i0 < CPT; i0 += BB) {
+    float xs[BB][8];
+    float bm = m;
 #pragma unroll
-    for (int j = 1; j < 8; ++j) lm = xs[j] > lm ? xs[j] : lm;
-    const float nm = f.m > lm ? f.m : lm;
-    f.s *= dexp<float>(f.m - nm);
-    f.m = nm;
+    for (int k = 0; k < BB; ++k) {
+      if (i0 + k >= CPT) continue;
+      IO<T>::unpack8(xr[i0 + k], xs[k]);
+      if (tid + int64_t(i0 + k) * kResBlock < nvec) {
 #pragma unroll
-    for (int j = 0; j < 8; ++j) f.s += dexp<float>(xs[j] - nm);
+        for (int j = 0; j < 8; j += 2) bm = max3_raw(bm, xs[k][j], xs[k][j + 1]);
+      }
+    }
+    if (bm == -INFINITY) continue;   // nothing but -inf so far
+    const float r = __builtin_amdgcn_exp2f((m - bm) * L2E);
+#pragma unroll
+    for (int k = 0; k < BB; ++k) ps[k] *= r;
+    m = bm;
+    const float b = -bm * L2E;
+#pragma unroll
+    for (int k = 0; k < BB; ++k) {
+      if (i0 + k >= CPT || tid + int64_t(i0 + k) * kResBlock >= nvec) continue;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) ps[k] += __builtin_amdgcn_exp2f(fmaf(xs[k][j], L2E, b));
+    }
   }
+  Online<float> f;
+  f.m = m;
+  f.s = (ps[0] + ps[1]) + (ps[2] + ps[3]);
+  f.a = 0.f;
   __shared__ Online<float> sh_f[kResBlock / 64];
   __shared__ float sh_lse;
   block_merge<float, kResBlock>(f, sh_f);
@@ -727,22 +748,43 @@ __device__ __forceinline__ void label_row_resident(const T *Z, const int64_t *y,
   const int64_t cnt = ctl->count;
   const float g = cnt ? float(grad_out / double(cnt)) : 0.f;
   const float a = g * (1.f + float(2.0 * z_coef) * lse);
-  // the target element relative to this thread's first chunk
+  // a exp(x - lse) = sign(a) 2^(x log2(e) + c2), c2 = log2|a| - lse log2(e)
+  // (a = 0 gives exp2(-inf) = 0)
+  const float c2 = __builtin_amdgcn_logf(fabsf(a)) - lse * L2E;
+  const bool neg = a < 0.f;
+  // the target element: chunk it of this thread (-1: another thread's), and
+  // g at its place within the chunk
   const int64_t ty = yt - int64_t(tid) * 8;
+  const int64_t span = int64_t(kResBlock) * 8;
+  const int it = (ty >= 0 && ty % span < 8) ? int(ty / span) : -1;
+  float gp[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) gp[j] = (it >= 0 && ty % span == j) ? g : 0.f;
   // Pass 2 unpacks the packed chunks again: holding pass 1's floats (8 per
   // chunk) across the reduction would not fit the registers.
 #pragma unroll
   for (int i = 0; i < CPT; ++i) asm volatile("" : "+v"(xr[i]));
+  auto pass2 = [&](auto neg_tag) {
+    constexpr bool NEG = decltype(neg_tag)::value;
 #pragma unroll
-  for (int i = 0; i < CPT; ++i) {
-    if (tid + int64_t(i) * kResBlock >= nvec) continue;
-    float xs[8], gs[8];
-    IO<T>::unpack8(xr[i], xs);
+    for (int i = 0; i < CPT; ++i) {
+      if (tid + int64_t(i) * kResBlock >= nvec) continue;
+      float xs[8], gs[8];
+      IO<T>::unpack8(xr[i], xs);
 #pragma unroll
-    for (int j = 0; j < 8; ++j)
-      gs[j] = a * dexp<float>(xs[j] - lse) - (ty == int64_t(i) * kResBlock * 8 + j ? g : 0.f);
-    __builtin_amdgcn_raw_buffer_store_b128(IO<T>::pack8(gs), ro, voff, i * kResBlock * 16, 2);
-  }
+      for (int j = 0; j < 8; ++j) {
+        const float e = __builtin_amdgcn_exp2f(fmaf(xs[j], L2E, c2));
+        gs[j] = NEG ? -e : e;
+      }
+      if (i == it) {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) gs[j] -= gp[j];
+      }
+      __builtin_amdgcn_raw_buffer_store_b128(IO<T>::pack8(gs), ro, voff, i * kResBlock * 16, 2);
+    }
+  };
+  if (neg) pass2(std::true_type{});
+  else pass2(std::false_type{});
 }
 
 template <class T, int CPT>
