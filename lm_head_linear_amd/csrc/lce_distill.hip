@@ -185,6 +185,19 @@ __device__ inline Online<C> shfl_xor_online(const Online<C> &v, int o) {
 
 constexpr int kBlock = 1024;
 constexpr int64_t kRowGrid = 256;   // workgroups: one per compute unit
+// Row-resident kernels: 512 threads (8 waves of up to 256 registers) keep
+// kResidentChunks 16-byte chunks each, rows up to 8 * 38 * 512 = 155648 values.
+constexpr int kResBlock = 512;
+constexpr int kResidentChunks = 38;
+
+// f(std::integral_constant<int, I>) for I = B .. E-1, in order.
+template <int B, int E, class F>
+__device__ __forceinline__ void static_for(F &&f) {
+  if constexpr (B < E) {
+    f(std::integral_constant<int, B>{});
+    static_for<B + 1, E>(f);
+  }
+}
 
 // Reduce within the block (NT threads) in a fixed order; thread 0 gets the
 // result.
@@ -294,7 +307,9 @@ __device__ inline void raw_merge(OnlineRaw &v, const OnlineRaw &o, float c) {
   v.m = M;
 }
 
-// Fixed-order block reduction of raw-unit statistics; thread 0 gets the result.
+// Fixed-order block reduction of raw-unit statistics (NT threads); thread 0
+// gets the result.
+template <int NT = kBlock>
 __device__ inline void block_merge_raw(OnlineRaw &v, OnlineRaw *sh, float c) {
   for (int o = 1; o < 64; o <<= 1) {
     OnlineRaw w;
@@ -307,7 +322,7 @@ __device__ inline void block_merge_raw(OnlineRaw &v, OnlineRaw *sh, float c) {
   if (lane == 0) sh[wave] = v;
   __syncthreads();
   if (threadIdx.x == 0)
-    for (int w = 1; w < kBlock / 64; ++w) raw_merge(v, sh[w], c);
+    for (int w = 1; w < NT / 64; ++w) raw_merge(v, sh[w], c);
 }
 
 template <class T, int OBJ>
@@ -439,6 +454,218 @@ __device__ __forceinline__ void distill_row16(const T *S, const T *U, const uint
   };
   if (kB > 0.f && (OBJ == 2 || kA > 0.f)) pass2(std::true_type{});
   else pass2(std::false_type{});
+}
+
+// 16-bit rows of at most 8 * CPT * kResBlock values, vocabulary a multiple
+// of 8, 16-byte aligned rows: the same statistics, objective and gradient as
+// distill_row16, with the student row read from memory once.  Each thread
+// keeps its CPT 16-byte chunks of the student row in registers; the teacher
+// row streams through a ring of kDRing chunk-steps in LDS that direct
+// buffer-to-LDS loads keep full (no registers held by loads in flight), once
+// for the statistics and once more for the gradient.  512 threads, one
+// workgroup per CU.  Every load and store is issued for every chunk index,
+// with indices past the row dropped by the buffer's range check, so that
+// each wave's count of memory operations in flight is known at compile time
+// and the ring's waits can name it.
+typedef __attribute__((address_space(3))) void lds_void_t;
+constexpr int kDRing = 16;   // chunk-steps in flight (16 x 8 KB of LDS)
+
+// Vector memory operations issued after the ring load of step q and before
+// the wait at the start of step q (steps [0, 2 CPT): the statistics pass,
+// then the gradient pass, which stores one chunk per step).  The ring loads
+// of steps [0, kDRing) go first; step s then waits, reads its chunk, loads
+// step s + kDRing (if any) and, in the gradient pass, stores its chunk.
+template <int CPT>
+constexpr int ring_ops_after(int q) {
+  int n = 0;
+  bool seen = false;
+  for (int r = 0; r < kDRing && r < 2 * CPT; ++r) {
+    if (seen) ++n;
+    if (r == q) seen = true;
+  }
+  for (int st = 0; st < q; ++st) {
+    if (st + kDRing < 2 * CPT) {
+      if (seen) ++n;
+      if (st + kDRing == q) seen = true;
+    }
+    if (st >= CPT && seen) ++n;
+  }
+  return n;
+}
+
+template <class T, int OBJ, int CPT>
+__device__ __forceinline__ void distill_row_resident(const T *S, const T *U, const uint8_t *mask,
+                                                     int64_t t, int64_t V, double inv_T,
+                                                     double z_coef, double grad_out,
+                                                     const Control *ctl, T *grad,
+                                                     double *row_out, char *ring) {
+  const float L2E = 1.4426950408889634f, LN2 = 0.6931471805599453f;
+  const T *s_row = S + t * V;
+  const T *u_row = U + t * V;
+  T *g_row = grad + t * V;
+  const int tid = threadIdx.x;
+  const int64_t nvec = V / 8;
+  const float iT = float(inv_T);
+  const float c = float(inv_T * 1.4426950408889634);
+  const uint32_t voff = uint32_t(tid) * 16u;
+  const int rbytes = int(V * int64_t(sizeof(T)));
+  const __amdgpu_buffer_rsrc_t ro = __builtin_amdgcn_make_buffer_rsrc(g_row, 0, rbytes, 0x00020000);
+  if (mask && !mask[t]) {
+    const u32x4 zero = {0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int i = 0; i < CPT; ++i)
+      __builtin_amdgcn_raw_buffer_store_b128(zero, ro, voff, i * kResBlock * 16, 2);
+    if (tid == 0) { row_out[2 * t] = 0.0; row_out[2 * t + 1] = 0.0; }
+    return;
+  }
+  __syncthreads();   // the previous row's statistics are no longer read
+  const __amdgpu_buffer_rsrc_t rs =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<T *>(s_row), 0, rbytes, 0x00020000);
+  const __amdgpu_buffer_rsrc_t ru =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<T *>(u_row), 0, rbytes, 0x00020000);
+  u32x4 xr[CPT];
+#pragma unroll
+  for (int i = 0; i < CPT; ++i)
+    xr[i] = __builtin_amdgcn_raw_buffer_load_b128(rs, voff, i * kResBlock * 16, 0);
+  // this wave's 1 KB of every ring slot; lane l's chunk lands at + 16 l
+  char *const wring = ring + (tid >> 6) * 1024;
+  auto ring_load = [&](int q) {   // step q: teacher chunk q mod CPT
+    const int i = q % CPT;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(ru, (lds_void_t *)(wring + (q % kDRing) * (kResBlock * 16)),
+                                             16, voff + uint32_t(i * kResBlock * 16), 0, 0, 0);
+  };
+#pragma unroll
+  for (int q = 0; q < kDRing && q < 2 * CPT; ++q) ring_load(q);
+  auto ring_wait_read = [&](auto q_tag) {
+    constexpr int q = decltype(q_tag)::value;
+    constexpr int N = ring_ops_after<CPT>(q);
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+    u32x4 u = *reinterpret_cast<const u32x4 *>(wring + (q % kDRing) * (kResBlock * 16) +
+                                               (tid & 63) * 16);
+    asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(u) : : "memory");
+    if constexpr (q + kDRing < 2 * CPT) ring_load(q + kDRing);
+    // no later memory operation (this step's store) moves above this load:
+    // the counts of ring_ops_after rely on the issue order
+    asm volatile("" ::: "memory");
+    return u;
+  };
+
+  // Statistics pass: the raw running maxima are updated, and the sums
+  // rescaled, once per chunk; even and odd chunks add into separate partial
+  // sums (independent add chains).
+  float mx = -INFINITY, my = -INFINITY;
+  float sx[2] = {0.f, 0.f}, sy[2] = {0.f, 0.f}, sa[2] = {0.f, 0.f};
+  static_for<0, CPT>([&](auto q_tag) {
+    constexpr int i = decltype(q_tag)::value;
+    constexpr int k = i & 1;
+    const u32x4 uu = ring_wait_read(q_tag);
+    do {
+      if (tid + int64_t(i) * kResBlock >= nvec) break;
+      float xs[8], ys[8];
+      IO<T>::unpack8(xr[i], xs);
+      IO<T>::unpack8(uu, ys);
+      float bmx = mx, bmy = my;
+#pragma unroll
+      for (int j = 0; j < 8; j += 2) {
+        bmx = max3_raw(bmx, xs[j], xs[j + 1]);
+        bmy = max3_raw(bmy, ys[j], ys[j + 1]);
+      }
+      if (bmx == -INFINITY || bmy == -INFINITY) break;
+      const float rx = __builtin_amdgcn_exp2f((mx - bmx) * c);
+      const float ry = __builtin_amdgcn_exp2f((my - bmy) * c);
+      const float ra = OBJ == 2 ? rx : ry;
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        sx[h] *= rx;
+        sy[h] *= ry;
+        sa[h] *= ra;
+      }
+      mx = bmx;
+      my = bmy;
+      const float bx = -bmx * c, by = -bmy * c;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const float ex = __builtin_amdgcn_exp2f(fmaf(xs[j], c, bx));
+        const float ey = __builtin_amdgcn_exp2f(fmaf(ys[j], c, by));
+        sx[k] += ex;
+        sy[k] += ey;
+        if constexpr (OBJ == 0) sa[k] = fmaf(ey, xs[j], sa[k]);
+        else if constexpr (OBJ == 1) sa[k] = fmaf(ey, ys[j] - xs[j], sa[k]);
+        else sa[k] = fmaf(ex, xs[j] - ys[j], sa[k]);
+      }
+    } while (false);
+  });
+  OnlineRaw fx{mx, sx[0] + sx[1], 0.f}, fy{my, sy[0] + sy[1], 0.f};
+  (OBJ == 2 ? fx : fy).a = sa[0] + sa[1];
+  __shared__ OnlineRaw sh_x[kResBlock / 64], sh_y[kResBlock / 64];
+  __shared__ float sh_stats[3];
+  block_merge_raw<kResBlock>(fx, sh_x, c);
+  block_merge_raw<kResBlock>(fy, sh_y, c);
+  if (tid == 0) {
+    const float lse_x = (fx.m * c + __builtin_amdgcn_logf(fx.s)) * LN2;
+    const float lse_y = (fy.m * c + __builtin_amdgcn_logf(fy.s)) * LN2;
+    float L;
+    if constexpr (OBJ == 0) L = lse_x - iT * fy.a / fy.s;
+    else if constexpr (OBJ == 1) L = iT * fy.a / fy.s + lse_x - lse_y;
+    else L = iT * fx.a / fx.s + lse_y - lse_x;
+    sh_stats[0] = lse_x;
+    sh_stats[1] = lse_y;
+    sh_stats[2] = L;
+    row_out[2 * t] = double(L);
+    row_out[2 * t + 1] = double(lse_x);
+  }
+  __syncthreads();
+  const float lse_x = sh_stats[0], lse_y = sh_stats[1], L = sh_stats[2];
+  const int64_t cnt = ctl->count;
+  const float scale = cnt ? float(grad_out / double(cnt) * inv_T) : 0.f;
+  const float zc = float(2.0 * z_coef) * lse_x;
+  const float aA = scale * (1.f + zc);
+  const float offA = __builtin_amdgcn_logf(fabsf(aA)) - lse_x * L2E;
+  const float kA = aA < 0.f ? -1.f : 1.f;
+  const float offB = __builtin_amdgcn_logf(fabsf(scale)) - (OBJ == 2 ? lse_x : lse_y) * L2E;
+  const float kB = scale < 0.f ? -1.f : 1.f;
+  const float K = lse_y - lse_x - L + zc;
+#pragma unroll
+  for (int i = 0; i < CPT; ++i) asm volatile("" : "+v"(xr[i]));
+
+  // Gradient pass (the same exponent folds as distill_row16).
+  auto pass2 = [&](auto plain_tag) {
+    constexpr bool PLAIN = decltype(plain_tag)::value;
+    static_for<CPT, 2 * CPT>([&](auto q_tag) {
+      constexpr int i = decltype(q_tag)::value - CPT;
+      const u32x4 uu = ring_wait_read(q_tag);
+      float xs[8], ys[8], gs[8];
+      IO<T>::unpack8(xr[i], xs);
+      IO<T>::unpack8(uu, ys);
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        if constexpr (OBJ == 2) {
+          const float p = __builtin_amdgcn_exp2f(fmaf(xs[j], c, offB));
+          const float f = fmaf(xs[j] - ys[j], iT, K);
+          gs[j] = PLAIN ? p * f : kB * p * f;
+        } else {
+          const float pa = __builtin_amdgcn_exp2f(fmaf(xs[j], c, offA));
+          const float qb = __builtin_amdgcn_exp2f(fmaf(ys[j], c, offB));
+          gs[j] = PLAIN ? pa - qb : fmaf(kA, pa, -kB * qb);
+        }
+      }
+      __builtin_amdgcn_raw_buffer_store_b128(IO<T>::pack8(gs), ro, voff, i * kResBlock * 16, 2);
+    });
+  };
+  if (kB > 0.f && (OBJ == 2 || kA > 0.f)) pass2(std::true_type{});
+  else pass2(std::false_type{});
+}
+
+template <class T, int OBJ, int CPT>
+__global__ void __launch_bounds__(kResBlock)
+distill_resident_kernel(const T *S, const T *U, const uint8_t *mask, int64_t n, int64_t V,
+                        double inv_T, double z_coef, double grad_out, const Control *ctl, T *grad,
+                        double *row_out) {
+  __shared__ __attribute__((aligned(1024))) char ring[kDRing * kResBlock * 16];
+  for (int64_t t = blockIdx.x; t < n; t += gridDim.x)
+    distill_row_resident<T, OBJ, CPT>(S, U, mask, t, V, inv_T, z_coef, grad_out, ctl, grad,
+                                      row_out, ring);
 }
 
 template <class T, int OBJ, bool VEC>
@@ -664,7 +891,6 @@ __device__ __forceinline__ void label_row(const T *Z, const int64_t *y, const ui
 // each thread keeps its CPT 16-byte chunks of the row in registers, so the row
 // is read from memory once (pass 2 computes from the registers).  512 threads,
 // one workgroup per CU: 8 waves of up to 256 registers each.
-constexpr int kResBlock = 512;
 template <class T, int CPT>
 __device__ __forceinline__ void label_row_resident(const T *Z, const int64_t *y,
                                                    const uint8_t *mask, int64_t t, int64_t V,
@@ -796,7 +1022,6 @@ label_resident_kernel(const T *Z, const int64_t *y, const uint8_t *mask, int64_t
   for (int64_t t = blockIdx.x; t < n; t += gridDim.x)
     label_row_resident<T, CPT>(Z, y, mask, t, V, z_coef, grad_out, ctl, grad, row_out);
 }
-constexpr int kResidentChunks = 38;   // rows up to 8 * 38 * 512 = 155648 values
 
 // Rows t = blockIdx.x, + gridDim.x, ...; nothing runs when the guard found
 // an out-of-range target (the outputs stay untouched).
@@ -869,6 +1094,13 @@ void launch_rows(bool vec, const T *S, const T *U, const uint8_t *mask, int64_t 
                  double inv_T, double z, double go, const Control *ctl, T *grad, double *rows,
                  hipStream_t st) {
   const unsigned grid = unsigned(n < kRowGrid ? n : kRowGrid);
+  if constexpr (sizeof(T) == 2) {   // student rows that fit the registers: read once
+    if (vec && V / 8 <= int64_t(kResidentChunks) * kResBlock) {
+      hipLaunchKernelGGL((distill_resident_kernel<T, OBJ, kResidentChunks>), dim3(grid),
+                         dim3(kResBlock), 0, st, S, U, mask, n, V, inv_T, z, go, ctl, grad, rows);
+      return;
+    }
+  }
   if (vec)
     hipLaunchKernelGGL((distill_row_kernel<T, OBJ, true>), dim3(grid), dim3(kBlock), 0, st, S, U,
                        mask, n, V, inv_T, z, go, ctl, grad, rows);
