@@ -25,7 +25,10 @@ def normwise(a, ref):
 
 @pytest.mark.parametrize("dt", ["bf16", "f32", "f64"])
 @pytest.mark.parametrize("obj", [0, 1, 2])
-@pytest.mark.parametrize("n,V", [(37, 1000), (20, 1003), (4, 151936)])
+@pytest.mark.parametrize("n,V", [(37, 1000), (20, 1003), (4, 151936),
+                                 # the largest vocabulary whose student rows fit the
+                                 # registers, and the next multiple of 8 (streamed rows)
+                                 (2, 155648), (3, 155656)])
 def test_small_distill(dt, obj, n, V):
     print(f"case distill {dt} obj={obj} n={n} V={V}", flush=True)
     dev = _dev()
@@ -43,6 +46,30 @@ def test_small_distill(dt, obj, n, V):
     print(f"  loss rel {el:.2e} z rel {ez:.2e} grad {eg:.2e}", flush=True)
     assert el <= lt and ez <= lt and eg <= gt
     assert not g[m == 0].any()
+
+
+@pytest.mark.parametrize("obj", [0, 1, 2])
+@pytest.mark.parametrize("n,V", [(37, 1000), (3, 155656)])
+@pytest.mark.parametrize("grad_out,z,shift", [(-0.7, 1e-3, 0.0), (1.3, 0.5, -40.0)])
+def test_negative_gradient_scale(obj, n, V, grad_out, z, shift):
+    """The gradient's terms with negative coefficients: grad_out < 0 (every
+    term), and 1 + 2 z lse_student < 0 (student logits shifted down by 40 with
+    z 0.5; objectives 0 and 1), bf16 rows resident (V 1000) and streamed."""
+    print(f"case distill sign obj={obj} n={n} V={V} g={grad_out} z={z} shift={shift}", flush=True)
+    dev = _dev()
+    d = syn.distill_inputs(syn.DISTILL_BF16, n_tok=n, vocab=V, seed=70 + obj + n, dtype="bf16")
+    S = (d.student.float() + shift).to(torch.bfloat16)
+    U = d.teacher
+    m = torch.from_numpy(d.mask)
+    out, g = lce.distill(S.to(dev), U.to(dev), m.to(dev), objective=obj, temperature=2.0,
+                         z_coef=z, grad_out=grad_out)
+    r = oracle.distill(S.double().numpy(), U.double().numpy(), mask=d.mask, objective=obj,
+                       temperature=2.0, z_coef=z, grad_out=grad_out)
+    el = abs(out["loss_mean"] - r["loss"]) / abs(r["loss"])
+    ez = abs(out["z_mean"] - r["z_loss"]) / abs(r["z_loss"])
+    eg = normwise(g.double().cpu().numpy(), r["grad"])
+    print(f"  loss rel {el:.2e} z rel {ez:.2e} grad {eg:.2e}", flush=True)
+    assert el <= 2e-3 and ez <= 2e-3 and eg <= 1e-2
 
 
 @pytest.mark.parametrize("obj", [0, 1, 2])

@@ -28,7 +28,8 @@ def normwise(a, ref):
 
 @pytest.mark.parametrize("dt", ["bf16", "f32", "f64"])
 @pytest.mark.parametrize("n,V,mask_frac", [(37, 1000, 0.2), (20, 1003, 0.0), (3, 4096, 0.34),
-                                            (5, 151936, 0.2), (3, 155648, 0.0)])
+                                            (5, 151936, 0.2), (3, 155648, 0.0),
+                                            (3, 155656, 0.0)])   # rows past the registers
 def test_small_label_ce(dt, n, V, mask_frac):
     print(f"case label {dt} n={n} V={V} mask {mask_frac}", flush=True)
     dev = _dev()
@@ -56,6 +57,27 @@ def test_small_label_ce(dt, n, V, mask_frac):
     rt = 1e-6 if dt == "bf16" else 0.0
     assert abs(out2["loss_sum"] - out["loss_sum"]) <= rt * abs(out["loss_sum"])
     assert abs(out2["z_sum"] - out["z_sum"]) <= rt * abs(out["z_sum"])
+
+
+@pytest.mark.parametrize("n,V", [(37, 1000), (3, 155656)])
+@pytest.mark.parametrize("grad_out,z,shift", [(-0.7, 1e-3, 0.0), (1.3, 0.5, -20.0)])
+def test_negative_gradient_scale(n, V, grad_out, z, shift):
+    """g (1 + 2 z lse) < 0: grad_out < 0, and lse < -1/(2 z) (logits shifted
+    down by 20 with z 0.5), bf16 rows in registers (V 1000) and streamed."""
+    print(f"case label sign n={n} V={V} g={grad_out} z={z} shift={shift}", flush=True)
+    dev = _dev()
+    w = syn.LabelWorkload("sign", n, V, "bf16", z, 0.2, 80 + n)
+    d = syn.label_inputs(w)
+    Z = (d.logits.float() + shift).to(torch.bfloat16)
+    m = torch.from_numpy(d.mask) if d.mask is not None else None
+    out, g = lce.ce_logits(Z.to(dev), torch.from_numpy(d.targets).to(dev),
+                           m.to(dev) if m is not None else None, z_coef=z, grad_out=grad_out)
+    r = oracle.ce_logits(Z.double().numpy(), d.targets, mask=d.mask, z_coef=z, grad_out=grad_out)
+    el = abs(out["loss_mean"] - r["loss"]) / abs(r["loss"])
+    ez = abs(out["z_mean"] - r["z_loss"]) / abs(r["z_loss"])
+    eg = normwise(g.double().cpu().numpy(), r["grad"])
+    print(f"  loss rel {el:.2e} z rel {ez:.2e} grad {eg:.2e}", flush=True)
+    assert el <= 2e-3 and ez <= 2e-3 and eg <= 1e-2
 
 
 @pytest.mark.parametrize("n,V", [(37, 1000), (20, 1003)])
