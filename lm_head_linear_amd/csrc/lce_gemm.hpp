@@ -48,6 +48,7 @@ struct TraitsH16 {
   static constexpr int MF = 32;                 // MFMA output block edge
   static constexpr int FM = WTM / MF, FN = WTN / MF;
   static constexpr int R = 16;                  // accumulators per lane per block
+  static constexpr int MIN_BLOCKS = 1;          // workgroups per CU the registers allow
   static constexpr int CE = 8;                  // elements per 16-byte chunk
   // Row of accumulator r of `lane` inside a 32x32 block; its column is lane & 31.
   __device__ static inline int row_of(int r, int lane) {
@@ -85,6 +86,9 @@ struct TraitsF64 {
   static constexpr int FM = WTM / MF, FN = WTN / MF;
   static constexpr int R = 4;
   static constexpr int CE = 2;
+  // Two workgroups per CU (at most 256 registers per lane): with one, every
+  // k-step's two barriers and LDS stores leave the matrix cores idle.
+  static constexpr int MIN_BLOCKS = 2;
   // Row of accumulator r of `lane` inside a 16x16 block (v_mfma_f64_16x16x4_f64
   // interleaves the four lane groups row by row); its column is lane & 15.
   __device__ static inline int row_of(int r, int lane) { return (lane >> 4) + 4 * r; }
@@ -426,7 +430,7 @@ struct GemmParams {
 // Grid: x = tiles_m * tiles_n (logical order n fastest, XCD-remapped),
 //       y = number of K splits.
 template <class TR, bool AK, bool BKM, bool VEC, class Epi>
-__global__ void __launch_bounds__(TR::NT) gemm_kernel(GemmParams g, Epi epi) {
+__global__ void __launch_bounds__(TR::NT, TR::MIN_BLOCKS) gemm_kernel(GemmParams g, Epi epi) {
   if (g.bad && *g.bad) return;
   __shared__ u32x4 smem[(TR::BM + TR::BN) * 8];
   u32x4 *As = smem;
