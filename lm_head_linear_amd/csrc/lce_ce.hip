@@ -84,6 +84,46 @@ __device__ __forceinline__ void guard_block(const int64_t *y, const uint8_t *mas
   }
 }
 
+// The same check by one workgroup that also starts the control block afresh
+// (what ctl_init_kernel does before a multi-workgroup guard): it writes the
+// verdict and the count instead of accumulating them, so no separate clearing
+// launch has to run first.
+__device__ __forceinline__ void guard_init_block(const int64_t *y, const uint8_t *mask, int64_t n,
+                                                 int64_t V, Control *ctl, int keep_loss) {
+  __shared__ unsigned long long s_first[16];
+  __shared__ unsigned long long s_count[16];
+  unsigned long long first = ULLONG_MAX, count = 0;
+  for (int64_t t = threadIdx.x; t < n; t += blockDim.x) {
+    const int64_t v = y ? y[t] : 0;
+    if (v < 0 || v >= V) first = first < (unsigned long long)t ? first : (unsigned long long)t;
+    count += mask ? (mask[t] != 0) : 1;
+  }
+  for (int o = 32; o > 0; o >>= 1) {
+    unsigned long long f2 = __shfl_xor(first, o);
+    first = f2 < first ? f2 : first;
+    count += __shfl_xor(count, o);
+  }
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  if (lane == 0) { s_first[wave] = first; s_count[wave] = count; }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    for (int w = 1; w < int(blockDim.x >> 6); ++w) {
+      first = s_first[w] < first ? s_first[w] : first;
+      count += s_count[w];
+    }
+    const int32_t old_bad = ctl->bad;   // the previous call's verdict
+    ctl->seen_bad = keep_loss ? (ctl->seen_bad | old_bad) : 0;
+    ctl->bad = first != ULLONG_MAX ? 1 : 0;
+    ctl->first_bad = first != ULLONG_MAX ? int64_t(first) : LLONG_MAX;
+    ctl->count = int64_t(count);
+    ctl->pad1 = 0;
+    if (!keep_loss) {
+      ctl->loss_sum = 0.0;
+      ctl->z_sum = 0.0;
+    }
+  }
+}
+
 __global__ void guard_kernel(const int64_t *y, const uint8_t *mask, int64_t n, int64_t V,
                              Control *ctl) {
   guard_block(y, mask, n, V, ctl, blockIdx.x, gridDim.x);
@@ -892,6 +932,8 @@ struct Prep {
   float *zero;
   int64_t zero_count;
   int64_t nb_guard, nb_local, nb_zy, nb_tr, nb_zero;
+  int guard_init;           // one guard workgroup that also starts the control block
+  int keep_loss;            // (as ctl_init_kernel's argument)
   int64_t blocks() const { return nb_guard + nb_local + nb_zy + nb_tr + nb_zero; }
 };
 
@@ -899,7 +941,8 @@ template <class TR>
 __global__ void prep_kernel(Prep<TR> a) {
   int64_t b = blockIdx.x;
   if (b < a.nb_guard) {
-    guard_block(a.y, a.mask, a.n, a.v_check, a.ctl, b, a.nb_guard);
+    if (a.guard_init) guard_init_block(a.y, a.mask, a.n, a.v_check, a.ctl, a.keep_loss);
+    else guard_block(a.y, a.mask, a.n, a.v_check, a.ctl, b, a.nb_guard);
     return;
   }
   b -= a.nb_guard;
@@ -1094,9 +1137,10 @@ struct Shard {
   Acc *stats = nullptr;   // forward: {m, s, z_target} rows of n tokens
 };
 
-// The per-call preparation: ctl_init, then one prep_kernel with the guard
-// (against the head's rows), the shard-local ids (shard calls), the target
-// logits (zy), H^T (Ht) and the cleared d_hidden accumulators (zero; absent
+// The per-call preparation: one prep_kernel with the guard (against the
+// head's rows; for up to 32768 tokens one workgroup that also starts the
+// control block, else after a ctl_init launch), the shard-local ids (shard
+// calls), the target logits (zy), H^T (Ht) and a cleared buffer (zero; absent
 // when null).  Returns the target ids the later kernels use.
 template <class TR>
 static const int64_t *prepare(const CEPlan &p, const int64_t *y, const uint8_t *mask,
@@ -1105,9 +1149,15 @@ static const int64_t *prepare(const CEPlan &p, const int64_t *y, const uint8_t *
                               typename TR::Acc *zy, bool vec, typename TR::E *Ht, float *zero,
                               int64_t zero_count, hipStream_t st, lce_timers *tm, int keep_loss) {
   TimedLaunch tl(tm, LCE_K_GUARD, st);
-  hipLaunchKernelGGL(ctl_init_kernel, dim3(1), dim3(64), 0, st, ctl, keep_loss);
+  // Up to kGuardOneBlock tokens one guard workgroup also starts the control
+  // block; beyond, ctl_init runs first and the guard is spread out.
+  constexpr int64_t kGuardOneBlock = 32768;
+  const bool one = p.n <= kGuardOneBlock;
+  if (!one) hipLaunchKernelGGL(ctl_init_kernel, dim3(1), dim3(64), 0, st, ctl, keep_loss);
   const int64_t row_blocks = cdiv(p.n, 256) < 1024 ? cdiv(p.n, 256) : 1024;
   Prep<TR> a{};
+  a.guard_init = one ? 1 : 0;
+  a.keep_loss = keep_loss;
   a.y = y;
   a.mask = mask;
   a.n = p.n;
@@ -1126,7 +1176,7 @@ static const int64_t *prepare(const CEPlan &p, const int64_t *y, const uint8_t *
   a.tr_cols = cdiv(p.d_ld, 64);
   a.zero = zero;
   a.zero_count = zero_count;
-  a.nb_guard = row_blocks;
+  a.nb_guard = one ? 1 : row_blocks;
   a.nb_local = sh.total ? row_blocks : 0;
   a.nb_zy = zy ? cdiv(p.n, 4) : 0;
   a.nb_tr = Ht ? a.tr_cols * cdiv(p.D, 64) : 0;
@@ -1190,9 +1240,9 @@ static void forward_impl(const CEPlan &p, const void *H, const void *W, const in
 // 16-bit backward as a slab pipeline: launch k runs d_hidden and d_weight of
 // slab k-1 (from slab buffer (k-1) % 2) together with the logit gradient of
 // slab k (into buffer k % 2), longest products first.  Slab 0 may be shorter
-// than the rest (the plan sizes it to one round of CUs).  The d_hidden split
-// accumulators start at zero (prepare clears them) and every launch adds to
-// them.
+// than the rest (the plan sizes it to one round of CUs).  The first launch
+// with d_hidden work stores the split accumulators and every later launch adds
+// to them.
 template <class TR, bool ACC_DW>
 static void backward_pipelined(const CEPlan &p, const uint16_t *Hp, const uint16_t *Wp,
                                const int64_t *y, const uint8_t *mask, const float *lse,
