@@ -315,6 +315,41 @@ def test_refusals_leave_outputs_untouched():
     assert torch.all(dh == 3.0) and torch.all(dw == 5.0)
 
 
+@pytest.mark.parametrize("dt", ["bf16", "f64"])
+def test_many_tokens_spread_guard(dt):
+    """More than 32768 tokens: the guard runs over many workgroups after a
+    separate control-block launch (fewer tokens take one guard workgroup that
+    also starts the control block).  Parity, then a target out of range in
+    the last workgroup's share: 586 from the forward and, through the fetch,
+    from the asynchronous backward, with the outputs untouched."""
+    w = syn.TINY_F64 if dt == "f64" else syn.QWEN_BF16
+    n, D, V, chunk = 40000, 64, 300, 4096
+    _say(f"case spread guard {dt} n={n} D={D} V={V} chunk={chunk}")
+    c = Case(w, n, D, V, seed=11, mask_frac=0.05, z=1e-4)
+    fwd = c.gpu_forward(chunk)
+    ref = c.oracle_forward(chunk)
+    check_forward(c, fwd, ref)
+    dH, dW = c.gpu_backward(fwd.lse, chunk, grad_out=1.5)
+    rdH, rdW = oracle.backward(c.H64, c.W64, c.x.targets, ref["lse"], mask=c.x.mask,
+                               z_coef=c.z, grad_out=1.5)
+    check_grads(c, dH, dW, rdH, rdW)
+    dev = c.H.device
+    acc = torch.float64 if dt == "f64" else torch.float32
+    lse = torch.full((n,), 7.0, dtype=acc, device=dev)
+    ws = lce.workspace_for(n, D, V, chunk, c.H.dtype, dev)
+    bad = c.y.clone()
+    bad[n - 3] = V
+    st, _ = lce.lce_forward(c.H, c.W, bad, c.m, n, D, V, chunk, 1e-4, lse, ws)
+    assert st == 586
+    dh = torch.full_like(c.H, 3.0)
+    dw = torch.full((V, D), 5.0, dtype=acc, device=dev)
+    st = lce.lce_backward(c.H, c.W, bad, c.m, lse, n, D, V, chunk, 1e-4, 1.0, dh, dw, 0, ws)
+    assert st == 580
+    assert lce.lce_loss_fetch(ws)[0] == 586
+    torch.cuda.synchronize()
+    assert torch.all(lse == 7.0) and torch.all(dh == 3.0) and torch.all(dw == 5.0)
+
+
 # ------------------------------------------------------------ full size --
 
 def _sample(rng, hi, k):
