@@ -713,16 +713,16 @@ struct StoreEpi {
 
 // Ht[d][t] = H[t][d] for t < n, 0 for n <= t < ld (16-bit values).  64x64
 // tiles through LDS; blockDim 256; block (bt, bd) of the tile grid.
-__device__ __forceinline__ void transpose_h_block(const uint16_t *H, int64_t n, int64_t D,
-                                                  uint16_t *Ht, int64_t ld, int64_t bt,
-                                                  int64_t bd) {
-  __shared__ uint16_t tile[64][66];
+template <class E>
+__device__ __forceinline__ void transpose_h_block(const E *H, int64_t n, int64_t D, E *Ht,
+                                                  int64_t ld, int64_t bt, int64_t bd) {
+  __shared__ E tile[64][66];
   const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;
   const int64_t t0 = bt * 64, d0 = bd * 64;
 #pragma unroll
   for (int j = 0; j < 16; ++j) {
     const int64_t t = t0 + ty + 4 * j, d = d0 + tx;
-    tile[ty + 4 * j][tx] = (t < n && d < D) ? H[t * D + d] : uint16_t(0);
+    tile[ty + 4 * j][tx] = (t < n && d < D) ? H[t * D + d] : E(0);
   }
   __syncthreads();
 #pragma unroll
@@ -960,8 +960,7 @@ __global__ void prep_kernel(Prep<TR> a) {
   }
   b -= a.nb_zy;
   if (b < a.nb_tr) {
-    if constexpr (IsH16<TR>::value)
-      transpose_h_block(a.H, a.n, a.D, a.Ht, a.ld, b % a.tr_cols, b / a.tr_cols);
+    transpose_h_block(a.H, a.n, a.D, a.Ht, a.ld, b % a.tr_cols, b / a.tr_cols);
     return;
   }
   b -= a.nb_tr;
@@ -1411,6 +1410,10 @@ static void backward_impl(const CEPlan &p, const void *H, const void *W, const i
       Ht = reinterpret_cast<E *>(ws + p.off_ht);
       zyb = reinterpret_cast<Acc *>(ws + p.off_zyb);
     }
+  } else {
+    // fp64: H^T too, so that the d_weight product reads both operands
+    // K-major instead of transposing H's 8 x 8 blocks in registers
+    Ht = reinterpret_cast<E *>(ws + p.off_ht);
   }
   const int64_t *y = prepare<TR>(p, y_in, mask, sh, ctl, ws, Hp, Wp, zyb, vec, Ht, nullptr, 0,
                                  st, tm, 1);
@@ -1457,7 +1460,7 @@ static void backward_impl(const CEPlan &p, const void *H, const void *W, const i
       TimedLaunch tl(tm, LCE_K_DW_GEMM, st);
       const StoreEpi<TR, true> e_acc{dW, p.D, vs0, rows, p.D, 0};
       const StoreEpi<TR, false> e_set{dW, p.D, vs0, rows, p.D, 0};
-      if (pipe) {  // B = H^T, K-major like the slab buffer
+      if (Ht) {    // B = H^T, K-major like the slab buffer
         g.B = Ht; g.ldb = p.d_ld;
         g.N_read = p.D;
         if (accumulate) launch_any<TR, true, true>(pipe, vec, g, 1, e_acc, st);

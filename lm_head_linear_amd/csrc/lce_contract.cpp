@@ -309,7 +309,7 @@ int32_t plan_ce(int64_t n, int64_t D, int64_t V, int64_t chunk, int32_t dtype, C
     off = align256(off + size_t(sp) * size_t(n) * size_t(D) * q.acc);
   }
   q.off_ht = off;
-  if (bf) off = align256(off + size_t(D) * size_t(q.d_ld) * q.elem);
+  off = align256(off + size_t(D) * size_t(q.d_ld) * q.elem);
   q.off_zyb = off;
   if (bf) off = align256(off + size_t(n) * q.acc);
   // shard-local target ids (vocabulary-shard calls), past both regions

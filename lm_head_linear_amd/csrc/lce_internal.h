@@ -61,7 +61,7 @@ struct CEPlan {
   // workspace layout (byte offsets)
   size_t off_partials = 0, off_zy = 0, off_losstok = 0;
   size_t off_dbuf = 0, off_dhacc = 0;
-  size_t off_ht = 0;          // bf16: H^T [D][d_ld] (zero past n); 0 bytes for fp64
+  size_t off_ht = 0;          // H^T [D][d_ld] (zero past n), the d_weight product's K-major operand
   size_t off_zyb = 0;         // bf16: target logits for the backward; 0 bytes for fp64
   size_t off_yloc = 0;        // [n] int64 shard-local target ids (shard calls)
   size_t total = 0;
