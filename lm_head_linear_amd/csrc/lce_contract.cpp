@@ -160,24 +160,27 @@ int32_t plan_ce(int64_t n, int64_t D, int64_t V, int64_t chunk, int32_t dtype, C
   int64_t slab_max = budget / q.d_ld;
   const int64_t tile_n = bf ? 256 : 128;
   const int64_t out_tiles = ceil_div(n, tile_m) * ceil_div(D, tile_n);
+  // Workgroups resident at once: one 16-bit tile per compute unit, two fp64
+  // tiles (the fp64 core runs two workgroups per CU).
+  const int64_t slots = bf ? kComputeUnits : kF64PerCu * kComputeUnits;
   // Split the vocabulary reduction of d_hidden so that the grid has about one
-  // workgroup per compute unit, keeping each split at least 512 deep.
+  // workgroup per slot, keeping each split at least 512 deep.
   auto dh_splits_for = [&](int64_t slab) {
-    int64_t sp = ceil_div(kComputeUnits, out_tiles);
+    int64_t sp = ceil_div(slots, out_tiles);
     if (sp > slab / 512) sp = slab / 512;
     if (sp > 16) sp = 16;
     return sp < 1 ? int64_t(1) : sp;
   };
-  if (bf && slab_max >= tile_m) {
-    // bf16: one 256x256 tile per compute unit per round, so a launch costs
-    // about (rounds of tiles) x (depth + epilogue).  Pick the slab (a multiple
-    // of 256 rows) with the lowest modelled total over the three backward
-    // GEMMs of every slab; ties go to the larger slab.
+  if (slab_max >= tile_m) {
+    // A launch costs about (rounds of tiles over the slots) x (depth +
+    // epilogue).  Pick the slab (a multiple of the tile rows) with the lowest
+    // modelled total over the three backward GEMMs of every slab; ties go to
+    // the larger slab.
     slab_max = slab_max / tile_m * tile_m;
     if (slab_max > round_up(V, tile_m)) slab_max = round_up(V, tile_m);
     const int64_t tn = ceil_div(n, tile_m), td = ceil_div(D, tile_n);
     const int64_t kEpi = 256, kLaunch = 64;
-    auto rounds = [&](int64_t wgs) { return ceil_div(wgs, kComputeUnits); };
+    auto rounds = [&](int64_t wgs) { return ceil_div(wgs, slots); };
     auto slab_cost = [&](int64_t rows, int64_t sp) {
       const int64_t tm = ceil_div(rows, tile_m);
       return rounds(tm * tn) * (D + kEpi) + rounds(tm * td) * (n + kEpi) +
@@ -193,8 +196,7 @@ int32_t plan_ce(int64_t n, int64_t D, int64_t V, int64_t chunk, int32_t dtype, C
     q.slab = best < V ? best : V;
     q.n_slabs = ceil_div(V, q.slab);
   } else {
-    if (slab_max >= tile_m) slab_max = slab_max / tile_m * tile_m;
-    else if (slab_max >= 32) slab_max = slab_max / 32 * 32;
+    if (slab_max >= 32) slab_max = slab_max / 32 * 32;
     if (slab_max < 1) slab_max = 1;
     if (slab_max >= V) {
       q.slab = V;

@@ -29,6 +29,7 @@ constexpr int64_t kBf16TileM = 256;   // vocabulary rows per GEMM tile (bf16)
 constexpr int64_t kComputeUnits = 256; // compute units of an MI355X (gfx950): one tile each per round
 constexpr int64_t kBf16WaveM = 128;   // rows per forward partial (bf16)
 constexpr int64_t kF64TileM = 128;
+constexpr int64_t kF64PerCu = 2;      // fp64 workgroups resident per CU
 constexpr int64_t kF64WaveM = 64;
 
 // How one lce_forward / lce_backward call is laid out for a shape.
