@@ -910,10 +910,10 @@ __global__ void dlogit_rows4_kernel(float *Z, int64_t V, int64_t n, int64_t ld,
 
 // Per-call preparation in one launch.  Its parts do not read each other's
 // results, so they share a grid: blocks [0, nb_guard) run the target guard
-// and token count (ctl_init has run), then nb_local blocks the shard-local
-// target ids, nb_zy blocks the target logits, nb_tr blocks H^T (the d_weight
-// product's K-major operand) and nb_zero blocks clear the d_hidden split
-// accumulators.  A part with no blocks is absent.  blockDim 256.
+// and token count (one block that also starts the control block, or several
+// after ctl_init), then nb_local blocks the shard-local target ids, nb_zy
+// blocks the target logits and nb_tr blocks H^T (the d_weight product's
+// K-major operand).  A part with no blocks is absent.  blockDim 256.
 template <class TR>
 struct Prep {
   const int64_t *y;
@@ -929,12 +929,10 @@ struct Prep {
   int vec8;
   typename TR::E *Ht;       // [D][ld] (16-bit inputs)
   int64_t ld, tr_cols;      // tr_cols = ceil(ld / 64) tile columns
-  float *zero;
-  int64_t zero_count;
-  int64_t nb_guard, nb_local, nb_zy, nb_tr, nb_zero;
+  int64_t nb_guard, nb_local, nb_zy, nb_tr;
   int guard_init;           // one guard workgroup that also starts the control block
   int keep_loss;            // (as ctl_init_kernel's argument)
-  int64_t blocks() const { return nb_guard + nb_local + nb_zy + nb_tr + nb_zero; }
+  int64_t blocks() const { return nb_guard + nb_local + nb_zy + nb_tr; }
 };
 
 template <class TR>
@@ -959,13 +957,7 @@ __global__ void prep_kernel(Prep<TR> a) {
     return;
   }
   b -= a.nb_zy;
-  if (b < a.nb_tr) {
-    transpose_h_block(a.H, a.n, a.D, a.Ht, a.ld, b % a.tr_cols, b / a.tr_cols);
-    return;
-  }
-  b -= a.nb_tr;
-  for (int64_t i = b * blockDim.x + threadIdx.x; i < a.zero_count; i += a.nb_zero * blockDim.x)
-    a.zero[i] = 0.f;
+  transpose_h_block(a.H, a.n, a.D, a.Ht, a.ld, b % a.tr_cols, b / a.tr_cols);
 }
 
 // d_hidden = sum over splits (ascending) of the split accumulators, in the
@@ -1139,14 +1131,14 @@ struct Shard {
 // The per-call preparation: one prep_kernel with the guard (against the
 // head's rows; for up to 32768 tokens one workgroup that also starts the
 // control block, else after a ctl_init launch), the shard-local ids (shard
-// calls), the target logits (zy), H^T (Ht) and a cleared buffer (zero; absent
-// when null).  Returns the target ids the later kernels use.
+// calls), the target logits (zy; absent when null) and H^T (Ht; absent when
+// null).  Returns the target ids the later kernels use.
 template <class TR>
 static const int64_t *prepare(const CEPlan &p, const int64_t *y, const uint8_t *mask,
                               const Shard<typename TR::Acc> &sh, Control *ctl, uint8_t *ws,
                               const typename TR::E *H, const typename TR::E *W,
-                              typename TR::Acc *zy, bool vec, typename TR::E *Ht, float *zero,
-                              int64_t zero_count, hipStream_t st, lce_timers *tm, int keep_loss) {
+                              typename TR::Acc *zy, bool vec, typename TR::E *Ht,
+                              hipStream_t st, lce_timers *tm, int keep_loss) {
   TimedLaunch tl(tm, LCE_K_GUARD, st);
   // Up to kGuardOneBlock tokens one guard workgroup also starts the control
   // block; beyond, ctl_init runs first and the guard is spread out.
@@ -1173,13 +1165,10 @@ static const int64_t *prepare(const CEPlan &p, const int64_t *y, const uint8_t *
   a.Ht = Ht;
   a.ld = p.d_ld;
   a.tr_cols = cdiv(p.d_ld, 64);
-  a.zero = zero;
-  a.zero_count = zero_count;
   a.nb_guard = one ? 1 : row_blocks;
   a.nb_local = sh.total ? row_blocks : 0;
   a.nb_zy = zy ? cdiv(p.n, 4) : 0;
   a.nb_tr = Ht ? a.tr_cols * cdiv(p.D, 64) : 0;
-  a.nb_zero = zero ? (cdiv(zero_count, 256) < 4096 ? cdiv(zero_count, 256) : 4096) : 0;
   hipLaunchKernelGGL(prep_kernel<TR>, dim3(unsigned(a.blocks())), dim3(256), 0, st, a);
   return sh.total ? a.yl : y;
 }
@@ -1196,7 +1185,7 @@ static void forward_impl(const CEPlan &p, const void *H, const void *W, const in
   const typename TR::E *Hp = static_cast<const typename TR::E *>(H);
   const int64_t *y =
       prepare<TR>(p, y_in, mask, sh, ctl, ws, Hp, static_cast<const typename TR::E *>(W), zy, vec,
-                  nullptr, nullptr, 0, st, tm, 0);
+                  nullptr, st, tm, 0);
   for (int64_t tok0 = 0; tok0 < p.n; tok0 += p.tok_per_pass) {
     const int64_t ntok = p.tok_per_pass < p.n - tok0 ? p.tok_per_pass : p.n - tok0;
     GemmParams g;
@@ -1415,8 +1404,7 @@ static void backward_impl(const CEPlan &p, const void *H, const void *W, const i
     // K-major instead of transposing H's 8 x 8 blocks in registers
     Ht = reinterpret_cast<E *>(ws + p.off_ht);
   }
-  const int64_t *y = prepare<TR>(p, y_in, mask, sh, ctl, ws, Hp, Wp, zyb, vec, Ht, nullptr, 0,
-                                 st, tm, 1);
+  const int64_t *y = prepare<TR>(p, y_in, mask, sh, ctl, ws, Hp, Wp, zyb, vec, Ht, st, tm, 1);
   if constexpr (IsH16<TR>::value) {
     if (pipe) {
       if (p.pslab > 0) {
@@ -1520,7 +1508,7 @@ static void forward_backward_single(const CEPlan &p, const void *H, const void *
   const Shard<float> whole;
   // (every d_hidden split partial is written whole by its own workgroup:
   // nothing to clear)
-  prepare<TR>(p, y, mask, whole, ctl, ws, Hp, Wp, zy, vec, Ht, dhacc, 0, st, tm, 0);
+  prepare<TR>(p, y, mask, whole, ctl, ws, Hp, Wp, zy, vec, Ht, st, tm, 0);
   const int64_t tiles_t = cdiv(n, 256), tiles_d = cdiv(D, 256);
   {
     GemmParams g;
