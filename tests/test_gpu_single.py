@@ -165,3 +165,33 @@ def test_kept_logits_full_vocab():
     rdW = oracle.backward_dw_rows(c.H64, c.W64, c.x.targets, ref["lse"], vw, mask=c.x.mask,
                                   z_coef=c.z)
     check_grads(c, dH, dW, rdH, rdW, rows_h=th, rows_w=vw)
+
+
+def test_kept_logits_full_size_512x4096():
+    """512 x 4096 x 151936 bf16, chunk 512, z 1e-4, 5% masked (the single
+    call's timed shape, where the cost model keeps the logits): lse, the loss
+    and every d_hidden and d_weight element against the oracle, and lse, the
+    loss scalars and d_weight bit for bit against the two-call path."""
+    n, D, V, chunk = 512, 4096, 151936, 512
+    _say(f"case kept logits full size {n} x {D} x {V}: generating inputs")
+    c = _case("bf16", n, D, V, seed=7, mask_frac=0.05, z=1e-4)
+    assert lce.lce_forward_backward_keeps_logits(n, D, V, chunk, c.H.dtype) == 1
+    fwd, dH, dW = _single(c, chunk, grad_out=1.0)
+    torch.cuda.synchronize()
+    _say("  oracle forward (all tokens)")
+    ref = c.oracle_forward(chunk)
+    check_forward(c, fwd, ref)
+    _say("  oracle backward: every d_hidden and d_weight element")
+    rdH, rdW = oracle.backward(c.H64, c.W64, c.x.targets, ref["lse"], mask=c.x.mask, z_coef=c.z,
+                               grad_out=1.0)
+    check_grads(c, dH, dW, rdH, rdW)
+    del rdH, rdW
+    f2 = c.gpu_forward(chunk)
+    dH2, dW2 = c.gpu_backward(f2.lse, chunk, grad_out=1.0)
+    torch.cuda.synchronize()
+    assert fwd.loss == f2.loss
+    assert torch.equal(fwd.lse, f2.lse)
+    assert torch.equal(dW, dW2)
+    e = normwise(dH.double().cpu().numpy(), dH2.double().cpu().numpy())
+    _say(f"  single vs two calls: d_hidden {e:.2e}")
+    assert e <= 1e-2
