@@ -157,10 +157,11 @@ struct PipeOperand {
     }
   }
 
-  // MN-major reads issued by hand (mn_frag_addr / mn_frag_issue): the LDS
-  // address of the fragment of tile rows base..base+31 at k-substep 0 of the
-  // stage at `src`; substep kk adds kk * 16 k-rows of 512 bytes, the second
-  // half of the fragment 4 k-rows more (both fit the instruction's offset).
+  // MN-major reads issued by hand (mn_frag_addr, mn_reads, mn_substep): the
+  // LDS address of the fragment of tile rows base..base+31 at k-substep 0 of
+  // the stage at `src`; substep kk adds kk * 16 k-rows of 512 bytes, the
+  // second half of the fragment 4 k-rows more (both fit the instruction's
+  // offset).
   __device__ inline uint32_t mn_frag_addr(const char *src, int base, int lane) const {
     static_assert(!KMAJOR, "MN-major operands only");
     const int g = lane >> 4, i = lane & 15;
@@ -169,17 +170,6 @@ struct PipeOperand {
     const char *a = src + krow * 512 + (((mn >> 3) ^ mswz2(krow)) << 4) + (mn & 7) * 2;
     // generic -> LDS address space: the 32-bit LDS byte address
     return uint32_t(reinterpret_cast<uintptr_t>((const __attribute__((address_space(3))) char *)a));
-  }
-  // Two ds_read_b64_tr_b16 of substep KK at `addr`.  The caller waits
-  // (lgkmcnt) before using the result: the compiler does not track these
-  // reads, and so does not make them wait for the stage loads in flight.
-  template <int KK>
-  __device__ __forceinline__ static void mn_frag_issue(u32x4 &out, uint32_t addr) {
-    u32x2 lo, hi;
-    asm volatile("ds_read_b64_tr_b16 %0, %1 offset:%2" : "=v"(lo) : "v"(addr), "n"(KK * 8192));
-    asm volatile("ds_read_b64_tr_b16 %0, %1 offset:%2"
-                 : "=v"(hi) : "v"(addr), "n"(KK * 8192 + 2048));
-    out = u32x4{lo[0], lo[1], hi[0], hi[1]};
   }
 
   // The 32x32x16 MFMA operand of tile rows base..base+31 for k-substep kk.
@@ -228,13 +218,98 @@ __device__ __forceinline__ void static_for(F &&f) {
   }
 }
 
-// Waits for every LDS read in flight and ties the fragments to the wait, so
-// that no MFMA reading them is scheduled above it.
-template <int FM, int FN>
-__device__ __forceinline__ void wait_frags(u32x4 (&a)[FM], u32x4 (&b)[FN]) {
-  static_assert(FM == 4 && FN == 2, "8-wave 128 x 64 wave tile");
-  asm volatile("s_waitcnt lgkmcnt(0)"
-               : "+v"(a[0]), "+v"(a[1]), "+v"(a[2]), "+v"(a[3]), "+v"(b[0]), "+v"(b[1]));
+// Hand-issued MN-major fragment reads (ds_read_b64_tr_b16) for the 8-wave
+// 128 x 64 wave tile: four A fragments and two B fragments per k-substep,
+// each two 8-byte transposing reads (k-rows +0 and +4).  Every block below
+// ends with its own s_waitcnt lgkmcnt(0), so no read is in flight once the
+// asm statement is over and the compiler may use the output registers freely.
+// (The builtin form of these reads makes the compiler wait for every operand
+// DMA in flight first, which exposes a whole stage load per k-step.)
+#define LCE_MN_RD(LO, HI, AD, OL, OH)                         \
+  "ds_read_b64_tr_b16 %" #LO ", %" #AD " offset:" OL "\n\t"   \
+  "ds_read_b64_tr_b16 %" #HI ", %" #AD " offset:" OH "\n\t"
+// Operands: %0..%11 the six fragments' low / high halves (outputs), %12..%17
+// their addresses.
+#define LCE_MN_READS(OL, OH)                                                         \
+  LCE_MN_RD(0, 1, 12, OL, OH) LCE_MN_RD(2, 3, 13, OL, OH) LCE_MN_RD(4, 5, 14, OL, OH)   \
+  LCE_MN_RD(6, 7, 15, OL, OH) LCE_MN_RD(8, 9, 16, OL, OH) LCE_MN_RD(10, 11, 17, OL, OH) \
+  "s_waitcnt lgkmcnt(0)"
+// One k-substep: the eight MFMAs acc[fm][fn] += A[fm] B[fn] on the current
+// fragments, with the next substep's six fragments read between them.
+// Operands: %0..%7 acc[0][0], acc[0][1], .. acc[3][1]; %8..%19 the next
+// fragments' halves (outputs); %20..%23 A[0..3]; %24, %25 B[0..1]; %26..%31
+// the next fragments' addresses.
+#define LCE_MN_SUBSTEP(MF, OL, OH)                                           \
+  MF " %0, %20, %24, %0\n\t" LCE_MN_RD(8, 9, 26, OL, OH)                     \
+  MF " %1, %20, %25, %1\n\t" LCE_MN_RD(10, 11, 27, OL, OH)                   \
+  MF " %2, %21, %24, %2\n\t" LCE_MN_RD(12, 13, 28, OL, OH)                   \
+  MF " %3, %21, %25, %3\n\t" LCE_MN_RD(14, 15, 29, OL, OH)                   \
+  MF " %4, %22, %24, %4\n\t" LCE_MN_RD(16, 17, 30, OL, OH)                   \
+  MF " %5, %22, %25, %5\n\t" LCE_MN_RD(18, 19, 31, OL, OH)                   \
+  MF " %6, %23, %24, %6\n\t"                                                 \
+  MF " %7, %23, %25, %7\n\t"                                                 \
+  "s_waitcnt lgkmcnt(0)"
+
+__device__ __forceinline__ void mn_join(u32x4 &f, u32x2 lo, u32x2 hi) {
+  f = u32x4{lo[0], lo[1], hi[0], hi[1]};
+}
+
+// The six fragments of substep KK at the addresses ad[0..5] (A[0..3], B[0..1]).
+template <int KK>
+__device__ __forceinline__ void mn_reads(u32x4 (&fa)[4], u32x4 (&fb)[2], const uint32_t (&ad)[6]) {
+  static_assert(KK >= 0 && KK < 4, "k-substep");
+  u32x2 h[12];
+#define LCE_MN_READS_ASM(OL, OH)                                                       \
+  asm volatile(LCE_MN_READS(OL, OH)                                                      \
+               : "=&v"(h[0]), "=&v"(h[1]), "=&v"(h[2]), "=&v"(h[3]), "=&v"(h[4]),        \
+                 "=&v"(h[5]), "=&v"(h[6]), "=&v"(h[7]), "=&v"(h[8]), "=&v"(h[9]),        \
+                 "=&v"(h[10]), "=&v"(h[11])                                              \
+               : "v"(ad[0]), "v"(ad[1]), "v"(ad[2]), "v"(ad[3]), "v"(ad[4]), "v"(ad[5]))
+  if constexpr (KK == 0) LCE_MN_READS_ASM("0", "2048");
+  else if constexpr (KK == 1) LCE_MN_READS_ASM("8192", "10240");
+  else if constexpr (KK == 2) LCE_MN_READS_ASM("16384", "18432");
+  else LCE_MN_READS_ASM("24576", "26624");
+#undef LCE_MN_READS_ASM
+#pragma unroll
+  for (int i = 0; i < 4; ++i) mn_join(fa[i], h[2 * i], h[2 * i + 1]);
+#pragma unroll
+  for (int i = 0; i < 2; ++i) mn_join(fb[i], h[8 + 2 * i], h[9 + 2 * i]);
+}
+
+// One k-substep on fragments (a, b) while reading the next substep's
+// fragments (substep KK of the stage the addresses ad[] point into) into
+// (na, nb).  F16: fp16 inputs (else bf16).
+template <bool F16, int KK>
+__device__ __forceinline__ void mn_substep(f32x16 (&acc)[4][2], const u32x4 (&a)[4],
+                                           const u32x4 (&b)[2], const uint32_t (&ad)[6],
+                                           u32x4 (&na)[4], u32x4 (&nb)[2]) {
+  static_assert(KK >= 0 && KK < 4, "k-substep");
+  u32x2 h[12];
+#define LCE_MN_SUBSTEP_ASM(MF, OL, OH)                                                  \
+  asm volatile(LCE_MN_SUBSTEP(MF, OL, OH)                                                 \
+               : "+v"(acc[0][0]), "+v"(acc[0][1]), "+v"(acc[1][0]), "+v"(acc[1][1]),      \
+                 "+v"(acc[2][0]), "+v"(acc[2][1]), "+v"(acc[3][0]), "+v"(acc[3][1]),      \
+                 "=&v"(h[0]), "=&v"(h[1]), "=&v"(h[2]), "=&v"(h[3]), "=&v"(h[4]),         \
+                 "=&v"(h[5]), "=&v"(h[6]), "=&v"(h[7]), "=&v"(h[8]), "=&v"(h[9]),         \
+                 "=&v"(h[10]), "=&v"(h[11])                                               \
+               : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3]), "v"(b[0]), "v"(b[1]),        \
+                 "v"(ad[0]), "v"(ad[1]), "v"(ad[2]), "v"(ad[3]), "v"(ad[4]), "v"(ad[5]))
+#define LCE_MN_SUBSTEP_KK(MF)                                       \
+  if constexpr (KK == 0) LCE_MN_SUBSTEP_ASM(MF, "0", "2048");             \
+  else if constexpr (KK == 1) LCE_MN_SUBSTEP_ASM(MF, "8192", "10240");    \
+  else if constexpr (KK == 2) LCE_MN_SUBSTEP_ASM(MF, "16384", "18432");   \
+  else LCE_MN_SUBSTEP_ASM(MF, "24576", "26624");
+  if constexpr (F16) {
+    LCE_MN_SUBSTEP_KK("v_mfma_f32_32x32x16_f16")
+  } else {
+    LCE_MN_SUBSTEP_KK("v_mfma_f32_32x32x16_bf16")
+  }
+#undef LCE_MN_SUBSTEP_KK
+#undef LCE_MN_SUBSTEP_ASM
+#pragma unroll
+  for (int i = 0; i < 4; ++i) mn_join(na[i], h[2 * i], h[2 * i + 1]);
+#pragma unroll
+  for (int i = 0; i < 2; ++i) mn_join(nb[i], h[8 + 2 * i], h[9 + 2 * i]);
 }
 
 // s_waitcnt lgkmcnt(0) vmcnt(N) followed by a bare s_barrier: unlike
@@ -356,10 +431,8 @@ __device__ __forceinline__ void gemm2_tile(const Gemm2Params &g, const Epi &epi,
   }
   if (n_k > 0) {
     if constexpr (MNMN) {
-#pragma unroll
-      for (int f = 0; f < TR::FM; ++f) OpA::template mn_frag_issue<0>(fa[0][f], a_off[f]);
-#pragma unroll
-      for (int f = 0; f < TR::FN; ++f) OpB::template mn_frag_issue<0>(fb[0][f], b_off[f]);
+      const uint32_t ad[6] = {a_off[0], a_off[1], a_off[2], a_off[3], b_off[0], b_off[1]};
+      mn_reads<0>(fa[0], fb[0], ad);
     } else {
 #pragma unroll
       for (int f = 0; f < TR::FM; ++f) fa[0][f] = pa.frag(smem, wm * TR::WTM + f * 32, 0, lane);
@@ -370,14 +443,16 @@ __device__ __forceinline__ void gemm2_tile(const Gemm2Params &g, const Epi &epi,
   }
 
   // One k-step of an MN-major x MN-major product.  Same dataflow as `step`
-  // below, in a fixed instruction order: at each substep, wait for the
-  // fragments read during the previous one, then alternate one MFMA with one
-  // fragment (two transposing reads) of the next substep.  The compiler does
-  // not see these reads, so it does not hold them until the next stage's
-  // loads have landed (which would expose the whole load latency each step).
+  // below, in a fixed instruction order: each substep is one asm block that
+  // alternates one MFMA with one fragment (two transposing reads) of the next
+  // substep and ends waiting for those reads.  The compiler does not see
+  // these reads, so it does not hold them until the next stage's loads have
+  // landed (which would expose the whole load latency each step).
   auto mn_step = [&](const int it, auto steady_tag) {
     constexpr bool STEADY = decltype(steady_tag)::value;
-    constexpr int NFR = TR::FM + TR::FN;   // fragments read per substep
+    static_assert(TR::FM == 4 && TR::FN == 2 && CFG::KSUB == 4 && CFG::BM == 256 &&
+                      CFG::BN == 256,
+                  "the asm substeps assume 128 x 64 wave tiles, k64 stages and 512-byte k-rows");
     const uint32_t sa = uint32_t((it % CFG::STAGES) * CFG::STAGE_BYTES);
     const uint32_t sn = uint32_t(((it + 1) % CFG::STAGES) * CFG::STAGE_BYTES);
     char *sa_p = smem + sa;
@@ -386,20 +461,14 @@ __device__ __forceinline__ void gemm2_tile(const Gemm2Params &g, const Epi &epi,
       constexpr int cur = kk & 1, nxt = cur ^ 1;
       constexpr bool last = kk == CFG::KSUB - 1;
       constexpr int ks = last ? 0 : kk + 1;
+      // (the last substep of the last k-step also reads: the next stage's
+      // slot holds stale data then, read and discarded, which keeps one
+      // straight-line register schedule for every k-step)
       const uint32_t so = last ? sn : sa;
-      const bool reads = !last || STEADY || it + 1 < n_k;
-      wait_frags<TR::FM, TR::FN>(fa[cur], fb[cur]);
+      const uint32_t ad[6] = {a_off[0] + so, a_off[1] + so, a_off[2] + so,
+                              a_off[3] + so, b_off[0] + so, b_off[1] + so};
+      mn_substep<TR::F16, ks>(acc, fa[cur], fb[cur], ad, fa[nxt], fb[nxt]);
       __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-      for (int i = 0; i < TR::FM * TR::FN; ++i) {
-        const int fm = i / TR::FN, fn = i % TR::FN;
-        acc[fm][fn] = mfma32<TR>(fa[cur][fm], fb[cur][fn], acc[fm][fn]);
-        if (i < NFR && reads) {
-          if (i < TR::FM) OpA::template mn_frag_issue<ks>(fa[nxt][i], a_off[i] + so);
-          else OpB::template mn_frag_issue<ks>(fb[nxt][i - TR::FM], b_off[i - TR::FM] + so);
-        }
-        __builtin_amdgcn_sched_barrier(0);
-      }
       if constexpr (kk == CFG::KSUB - 2) {
         if (STEADY) wait_vm_barrier<LPS * (CFG::STAGES - 2)>();
         else wait_vm_barrier_stages<LPS, CFG::STAGES - 2>(n_k - 2 - it);
@@ -471,6 +540,15 @@ __device__ __forceinline__ void gemm2_tile(const Gemm2Params &g, const Epi &epi,
   if constexpr (MNMN) {
     for (; it + STAGES < n_k; ++it) mn_step(it, std::true_type{});
     for (; it < n_k; ++it) mn_step(it, std::false_type{});
+    // The accumulators were last written by MFMAs inside asm blocks, which the
+    // compiler's hazard tracking does not see: give the matrix core's result
+    // latency (at most 16 passes) before any other instruction reads them
+    // (the accumulators are operands, so no read moves above the wait).
+    asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7"
+                 : "+v"(acc[0][0]), "+v"(acc[0][1]), "+v"(acc[1][0]), "+v"(acc[1][1]),
+                   "+v"(acc[2][0]), "+v"(acc[2][1]), "+v"(acc[3][0]), "+v"(acc[3][1])
+                 :
+                 : "memory");
   } else {
     for (; it + STAGES < n_k; ++it) step(it, std::true_type{});
     for (; it < n_k; ++it) step(it, std::false_type{});
