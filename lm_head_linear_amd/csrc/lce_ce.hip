@@ -432,7 +432,7 @@ template <class T, class TR> struct Staging {
   }
 };
 
-template <class T, class TR, bool ACCUM, class Xf, class Ptr, class Patch>
+template <class T, class TR, bool ACCUM, bool NT = true, class Xf, class Ptr, class Patch>
 __device__ __forceinline__ void staged_tile(const typename TR::AccBlock (&acc)[TR::FM][TR::FN],
                                             char *region, int lane, const Xf &xf, const Ptr &ptr,
                                             const Patch &patch) {
@@ -483,7 +483,7 @@ __device__ __forceinline__ void staged_tile(const typename TR::AccBlock (&acc)[T
           // fp32 results written once (d_weight rows, kept logits, split
           // partials) stream past the caches: keeping them there evicts the
           // operands the next tiles read (the 512-token heads run 4-7% faster)
-          if constexpr (S::ES == 4)
+          if constexpr (S::ES == 4 && NT)
             __builtin_nontemporal_store(d[i], reinterpret_cast<u32x4 *>(dst[i]));
           else *reinterpret_cast<u32x4 *>(dst[i]) = d[i];
         }
@@ -653,7 +653,9 @@ struct DlogitEpi {
 };
 
 // out[split][row_off + row][col] = C (ACCUM false) or += C (ACCUM true).
-template <class TR, bool ACCUM>
+// NT: stored values stream past the caches (written once, read much later);
+// otherwise they stay cached for a reader that follows soon.
+template <class TR, bool ACCUM, bool NT = true>
 struct StoreEpi {
   typedef typename TR::Acc Acc;
   Acc *out;
@@ -708,7 +710,7 @@ struct StoreEpi {
     const int64_t cw0 = n0 + int64_t(wn) * TR::WTN;
     if (rw0 >= rows || cw0 >= cols) return;  // wave-uniform
     char *region = lds + (wm * TR::WAVES_N + wn) * Staging<float, TR>::BYTES;
-    staged_tile<float, TR, ACCUM>(
+    staged_tile<float, TR, ACCUM, NT>(
         acc, region, lane, [&](int fm, int fn, int r, int) -> float { return acc[fm][fn][r]; },
         [&](int rr, int cc) -> float * {
           const int64_t row = rw0 + rr, c = cw0 + cc;
@@ -1246,8 +1248,9 @@ static void backward_pipelined(const CEPlan &p, const uint16_t *Hp, const uint16
                                hipStream_t st, lce_timers *tm) {
   typedef typename W8Of<TR>::type TRP;
   typedef Gemm2Job<PipeMN, false, false, StoreEpi<TRP, true>> JH;
-  // the first slab's d_hidden partials are stored, not added (nothing to clear)
-  typedef Gemm2Job<PipeMN, false, false, StoreEpi<TRP, false>> JH0;
+  // the first slab's d_hidden partials are stored, not added (nothing to
+  // clear), and kept in the caches for the next launch's additions
+  typedef Gemm2Job<PipeMN, false, false, StoreEpi<TRP, false, false>> JH0;
   typedef Gemm2Job<PipeKK, true, true, StoreEpi<TRP, ACC_DW>> JW;
   typedef Gemm2Job<PipeKK, true, true, DlogitEpi<TRP>> JL;
   const int64_t n = p.n, D = p.D, V = p.V, S = p.pslab, sp = p.pdh_splits;
@@ -1353,7 +1356,7 @@ static void backward_pipelined(const CEPlan &p, const uint16_t *Hp, const uint16
     if (k == 1) {
       JH0 jh0{};
       jh0.g = jh.g;
-      jh0.e = StoreEpi<TRP, false>{jh.e.out, jh.e.ldo, jh.e.row_off, jh.e.rows, jh.e.cols,
+      jh0.e = StoreEpi<TRP, false, false>{jh.e.out, jh.e.ldo, jh.e.row_off, jh.e.rows, jh.e.cols,
                                    jh.e.split_stride};
       jh0.nb = jh.nb;
       jh0.nreal = jh.nreal;
