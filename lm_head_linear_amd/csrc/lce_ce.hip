@@ -631,24 +631,37 @@ struct DlogitEpi {
     }
     typedef Staging<uint16_t, TR> S;
     char *region = lds + (wm * TR::WAVES_N + wn) * S::BYTES;
-    staged_tile<uint16_t, TR, false>(
-        acc, region, lane,
-        [&](int fm, int fn, int r, int) -> uint16_t {
-          const float e = __builtin_amdgcn_exp2f(fmaf(acc[fm][fn][r], L2E, c2[fn]));
-          return to_elem<TR>(__uint_as_float(__float_as_uint(e) ^ sb[fn]));
-        },
-        [&](int vr, int tc) -> uint16_t * {
-          const int64_t v = vw0 + vr, t = tw0 + tc;
-          return (v < rows && t < d_ld) ? dbuf + v * d_ld + t : nullptr;
-        },
-        [&](int fm, char *blk) {
-          // overwrite the target element of each column that has it here
+    auto store = [&](auto neg_tag) {
+      // NEG: some column of this wave has a negative coefficient (its sign
+      // goes onto every value by XOR); otherwise every value is positive
+      constexpr bool NEG = decltype(neg_tag)::value;
+      staged_tile<uint16_t, TR, false>(
+          acc, region, lane,
+          [&](int fm, int fn, int r, int) -> uint16_t {
+            const float e = __builtin_amdgcn_exp2f(fmaf(acc[fm][fn][r], L2E, c2[fn]));
+            if constexpr (NEG) return to_elem<TR>(__uint_as_float(__float_as_uint(e) ^ sb[fn]));
+            else return to_elem<TR>(e);
+          },
+          [&](int vr, int tc) -> uint16_t * {
+            const int64_t v = vw0 + vr, t = tw0 + tc;
+            return (v < rows && t < d_ld) ? dbuf + v * d_ld + t : nullptr;
+          },
+          [&](int fm, char *blk) {
+            // overwrite the target element of each column that has it here
 #pragma unroll
-          for (int fn = 0; fn < TR::FN; ++fn)
-            if (lane < TR::MF && yl[fn] >= fm * TR::MF && yl[fn] < fm * TR::MF + TR::MF)
-              *reinterpret_cast<uint16_t *>(blk + S::at(yl[fn] - fm * TR::MF, fn * TR::MF + lane)) =
-                  to_elem<TR>(gy[fn]);
-        });
+            for (int fn = 0; fn < TR::FN; ++fn)
+              if (lane < TR::MF && yl[fn] >= fm * TR::MF && yl[fn] < fm * TR::MF + TR::MF)
+                *reinterpret_cast<uint16_t *>(blk + S::at(yl[fn] - fm * TR::MF, fn * TR::MF + lane)) =
+                    to_elem<TR>(gy[fn]);
+          });
+    };
+    uint32_t any_sb = 0;
+#pragma unroll
+    for (int fn = 0; fn < TR::FN; ++fn) any_sb |= sb[fn];
+    if (__builtin_amdgcn_ballot_w64(any_sb != 0) != 0)   // wave-uniform
+      store(std::true_type{});
+    else
+      store(std::false_type{});
   }
 };
 
