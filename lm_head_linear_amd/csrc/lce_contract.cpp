@@ -327,12 +327,14 @@ int32_t plan_ce(int64_t n, int64_t D, int64_t V, int64_t chunk, int32_t dtype, C
   // Whether keeping pays is decided by the same launch model as the slab
   // pipeline (times in k-rows of one 256x256 tile on one compute unit,
   // about 28 ns each): the kept path saves the recompute but writes the
-  // logits in fp32, reads them back and writes the 16-bit gradient (10
-  // bytes per kept cell, about 128 KB per unit at the chip's streaming
-  // rate) and runs d_hidden as one launch over the whole vocabulary.  The
-  // logits are kept only when the model puts that path at least 3% ahead of
-  // the two-call algorithm (measured on 512 x 151936 heads: 0.93x at
-  // d_model 1024, 1.19x at 4096; 1.15x at 256 x 1024).
+  // logits in fp32 from the forward GEMM (4 bytes per kept cell, half of it
+  // hidden behind that GEMM's matrix work), then reads them back and writes
+  // the 16-bit gradient in a streaming pass (6 bytes per cell; about 128 KB
+  // per unit at the chip's streaming rate), and runs d_hidden as one launch
+  // over the whole vocabulary.  The logits are kept when the model puts that
+  // path at least 1% ahead of the two-call algorithm (measured on
+  // 512 x 151936 heads, single call against the two calls on one box:
+  // 1.21-1.26x at d_model 4096, 1.01-1.05x at 1024; 1.14-1.16x at 256 x 1024).
   q.f_total = q.total;
   if (bf) {
     int64_t fld = round_up(n, 4);
@@ -345,14 +347,14 @@ int32_t plan_ce(int64_t n, int64_t D, int64_t V, int64_t chunk, int32_t dtype, C
       const int64_t kEpi = 256, kLaunch = 64, kBytesPerUnit = 128000;
       const int64_t tn = ceil_div(n, tile_m), td = ceil_div(D, tile_n);
       const int64_t fwd = ceil_div(ceil_div(V, tile_m) * tn * (D + 2 * kEpi), kComputeUnits);
-      const int64_t kept = V * fld * 10 / kBytesPerUnit;
+      const int64_t kept = V * fld * 6 / kBytesPerUnit + V * fld * 4 / (2 * kBytesPerUnit);
       const int64_t dh_wg = (ceil_div(V, sp) * 5) / 4 + kEpi;
       const int64_t work = out_tiles * sp * dh_wg + ceil_div(V, tile_m) * td * (n + kEpi);
       const int64_t spread = ceil_div(work, kComputeUnits);
       q.model_single = fwd + kept + (spread > dh_wg ? spread : dh_wg) + 3 * kLaunch;
     }
     // (without a slab pipeline to compare with, keeping always pays)
-    const bool pays = q.model_two == 0 || q.model_single * 103 < q.model_two * 100;
+    const bool pays = q.model_two == 0 || q.model_single * 101 < q.model_two * 100;
     if (fld <= chunk && q.tok_per_pass >= n && pays) {
       q.f_ok = true;
       q.f_ld = fld;

@@ -113,16 +113,18 @@ def test_single_call_workspace():
 
 def test_single_call_dispatch():
     """lce_forward_backward_keeps_logits: the launch-cost model keeps the
-    logits where that measured faster (512 x 4096 and 256 x 1024 heads of
-    151936 rows) and takes the two-call algorithm where it measured slower
-    (512 x 1024); the workspace follows the choice."""
+    logits where that measured faster (512 x 4096, 512 x 1024 and 256 x 1024
+    heads of 151936 rows) and takes the two-call algorithm where the model
+    puts keeping behind (768 x 512: the recompute saved is small against the
+    kept logits' traffic); the workspace follows the choice."""
     k = lce.lce_forward_backward_keeps_logits
     f = lce.lce_forward_backward_workspace_bytes
     w = lce.lce_workspace_bytes
     assert k(512, 4096, 151936, 512, lce.BF16) == 1
     assert k(256, 1024, 151936, 256, lce.BF16) == 1
-    assert k(512, 1024, 151936, 512, lce.BF16) == 0
-    assert f(512, 1024, 151936, 512, lce.BF16) == w(512, 1024, 151936, 512, lce.BF16)
+    assert k(512, 1024, 151936, 512, lce.BF16) == 1
+    assert k(768, 512, 151936, 768, lce.BF16) == 0
+    assert f(768, 512, 151936, 768, lce.BF16) == w(768, 512, 151936, 768, lce.BF16)
     assert k(512, 4096, 151936, 512, lce.F16) == 1
     assert k(512, 4096, 151936, 512, lce.F64) == 0        # fp64 never keeps
     assert k(2048, 1024, 151936, 256, lce.BF16) == 0      # the batch exceeds the chunk
