@@ -1205,9 +1205,10 @@ static void forward_impl(const CEPlan &p, const void *H, const void *W, const in
   Acc *zy = reinterpret_cast<Acc *>(ws + p.off_zy);
   double *loss_tok = reinterpret_cast<double *>(ws + p.off_losstok);
   const typename TR::E *Hp = static_cast<const typename TR::E *>(H);
-  const int64_t *y =
-      prepare<TR>(p, y_in, mask, sh, ctl, ws, Hp, static_cast<const typename TR::E *>(W), zy, vec,
-                  nullptr, st, tm, 0);
+  // (the forward needs no target ids after the preparation: the target
+  // logits come from it)
+  prepare<TR>(p, y_in, mask, sh, ctl, ws, Hp, static_cast<const typename TR::E *>(W), zy, vec,
+              nullptr, st, tm, 0);
   for (int64_t tok0 = 0; tok0 < p.n; tok0 += p.tok_per_pass) {
     const int64_t ntok = p.tok_per_pass < p.n - tok0 ? p.tok_per_pass : p.n - tok0;
     GemmParams g;
