@@ -172,9 +172,14 @@ def shard_measure(lce, torch, np, dev, w, H, W, y, m, steps: int, shards: int):
     """The same training step as vocabulary shards run one after another on
     this GPU (each shard's forward, the exchange, each shard's backward with
     its d_hidden partial added up): what one GPU's share of a vocab-parallel
-    head costs, and the exchange's overhead against the unsharded step."""
+    head costs, and the exchange's overhead against the unsharded step.  Each
+    shard call gets chunk = the unsharded chunk x shards, so that a shard
+    holds as many logit cells (chunk x its rows) as the unsharded call does
+    (chunk x vocab): the peak logit memory of one GPU of a vocab-parallel
+    head at the unsharded call's budget."""
     n, D = H.shape
     V = W.shape[0]
+    chunk = w.chunk * shards
     bounds = [V * q // shards // 256 * 256 for q in range(shards)] + [V]
     acc = torch.float64 if H.dtype == torch.float64 else torch.float32
     stats = torch.empty(shards, 3, n, dtype=acc, device=dev)
@@ -183,14 +188,14 @@ def shard_measure(lce, torch, np, dev, w, H, W, y, m, steps: int, shards: int):
     dH = torch.empty(n, D, dtype=acc, device=dev)
     dW = torch.empty(V, D, dtype=acc, device=dev)
     rows = max(bounds[q + 1] - bounds[q] for q in range(shards))
-    ws = torch.empty(lce.lce_workspace_bytes(n, D, rows, w.chunk, H.dtype), dtype=torch.uint8,
+    ws = torch.empty(lce.lce_workspace_bytes(n, D, rows, chunk, H.dtype), dtype=torch.uint8,
                      device=dev)
     mws = torch.empty(lce.lce_distill_workspace_bytes(n, 1), dtype=torch.uint8, device=dev)
 
     def step():
         for q in range(shards):
             a, b = bounds[q], bounds[q + 1]
-            st = lce.lce_shard_forward(H, W[a:b], y, n, D, b - a, a, V, w.chunk, stats[q], ws)
+            st = lce.lce_shard_forward(H, W[a:b], y, n, D, b - a, a, V, chunk, stats[q], ws)
             if st != lce.OK:
                 raise lce.LceError(st, "lce_shard_forward")
         st, out = lce.lce_shard_merge(stats, shards, m, n, lse, mws)
@@ -198,7 +203,7 @@ def shard_measure(lce, torch, np, dev, w, H, W, y, m, steps: int, shards: int):
             raise lce.LceError(st, "lce_shard_merge")
         for q in range(shards):
             a, b = bounds[q], bounds[q + 1]
-            st = lce.lce_shard_backward(H, W[a:b], y, m, lse, n, D, b - a, a, V, w.chunk,
+            st = lce.lce_shard_backward(H, W[a:b], y, m, lse, n, D, b - a, a, V, chunk,
                                         w.z_coef, 1.0, part, dW[a:b], 0, ws)
             if st != lce.OK:
                 raise lce.LceError(st, "lce_shard_backward")
@@ -216,7 +221,8 @@ def shard_measure(lce, torch, np, dev, w, H, W, y, m, steps: int, shards: int):
         out = step()
     torch.cuda.synchronize()
     ms = (time.perf_counter() - t0) / steps * 1e3
-    return {"shards": shards, "bounds": bounds, "ms_per_step": round(ms, 4),
+    return {"shards": shards, "bounds": bounds, "chunk_per_shard": chunk,
+            "ms_per_step": round(ms, 4),
             "tokens_per_s": round(n / (ms / 1e3), 1), "loss": out.loss_mean}
 
 
