@@ -313,7 +313,12 @@ int32_t lce_distill_fwd_bwd_noalloc(const lce_tensor *student, const lce_tensor 
  * for 16-bit inputs, LCE_F64 for fp64): stats[t] = m_t, the shard's largest
  * logit of token t; stats[n_tok + t] = s_t = sum over the shard's rows of
  * exp(z - m_t); stats[2*n_tok + t] = z[t][y_t] when the shard holds row y_t,
- * else 0.  It synchronizes the stream (target guard). */
+ * else 0.  It returns once its kernels are enqueued (no host wait, so the
+ * records can go straight into the exchange): a target out of range makes
+ * its kernels exit before writing the records and is reported as 586 by
+ * lce_loss_fetch(workspace), as for lce_backward; check it before trusting
+ * the records (the scalars lce_loss_fetch returns are meaningless for a
+ * shard's workspace). */
 int32_t lce_shard_forward(const lce_tensor *hidden, const lce_tensor *weight_shard,
                           const lce_tensor *targets, int64_t n_tok, int64_t d_model,
                           int64_t vocab_shard, int64_t vocab_offset, int64_t vocab_total,

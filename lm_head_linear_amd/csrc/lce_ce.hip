@@ -1718,9 +1718,9 @@ int32_t lce_shard_forward(const lce_tensor *hidden, const lce_tensor *weight_sha
                           const lce_tensor *targets, int64_t n_tok, int64_t d_model,
                           int64_t vocab_shard, int64_t vocab_offset, int64_t vocab_total,
                           int64_t chunk, lce_tensor *stats, lce_tensor *workspace, void *stream) {
-  lce_loss unused;
+  // asynchronous: a target out of range shows in lce_loss_fetch(workspace)
   return forward_call(hidden, weight_shard, targets, nullptr, n_tok, d_model, vocab_shard, chunk,
-                      0.0, nullptr, workspace, &unused, stream, nullptr, vocab_offset, vocab_total,
+                      0.0, nullptr, workspace, nullptr, stream, nullptr, vocab_offset, vocab_total,
                       stats);
 }
 

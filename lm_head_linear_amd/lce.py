@@ -346,7 +346,9 @@ def lce_ce_logits_fwd_bwd(logits, targets, loss_mask, n_tok, vocab, z_coef, grad
 
 def lce_shard_forward(hidden, weight_shard, targets, n_tok, d_model, vocab_shard, vocab_offset,
                       vocab_total, chunk, stats, workspace, stream: Optional[int] = None) -> int:
-    """Direct call of the C entry point; returns the status."""
+    """Direct call of the C entry point; returns the status.  The call does not
+    wait for the device: a target out of range shows as 586 in
+    lce_loss_fetch(workspace)."""
     ts = [_t(hidden), _t(weight_shard), _t(targets)]
     st_t, ws = _t(stats), _t(workspace)
     return lib().lce_shard_forward(*[ctypes.byref(a) for a in ts], n_tok, d_model, vocab_shard,

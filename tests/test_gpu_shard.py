@@ -176,10 +176,12 @@ def test_shard_refusals():
     assert call(stats=stats[0]) == 582
     bad = y.clone()
     bad[3] = 300                                  # outside the whole head
-    assert call(targets=bad) == 586
+    assert call(targets=bad) == 580               # enqueued; the guard's verdict is fetched
+    assert lce.lce_loss_fetch(ws)[0] == 586
     torch.cuda.synchronize()
     assert torch.all(stats == 7.0)
     assert call() == 580
+    assert lce.lce_loss_fetch(ws)[0] == 580
     lse = torch.empty(16, dtype=torch.float32, device=dev)
     mws = torch.empty(lce.lce_distill_workspace_bytes(16, 1), dtype=torch.uint8, device=dev)
     assert lce.lce_shard_merge(stats, 0, None, 16, lse, mws)[0] == 581
