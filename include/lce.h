@@ -140,8 +140,11 @@ int32_t lce_peak_cells(int64_t n_tok, int64_t vocab, int64_t chunk, lce_peak *ou
 
 /* Bytes of device workspace lce_forward and lce_backward need for this
  * shape and compute dtype (LCE_BF16, LCE_F16 or LCE_F64).  Negative = -status when
- * the shape, chunk or dtype is refused.  The logit-derived part of the
- * workspace never exceeds chunk*vocab cells. */
+ * the shape, chunk or dtype is refused.  Each logit-derived buffer of the
+ * workspace stays within chunk*vocab cells, with two floors where the budget
+ * is smaller than the unit of work: one token's forward partials
+ * (2*ceil(vocab/128) cells, 2*ceil(vocab/64) for fp64) and one vocabulary row
+ * for every token, rounded up to 64, in the backward. */
 int64_t lce_workspace_bytes(int64_t n_tok, int64_t d_model, int64_t vocab, int64_t chunk,
                             int32_t dtype);
 
@@ -177,8 +180,9 @@ int64_t lce_distill_workspace_bytes(int64_t n_tok, int64_t vocab);
  *   weight    [vocab*d_model] same dtype, row-major [vocab][d_model]
  *   targets   [n_tok] LCE_I64, each must satisfy 0 <= y < vocab (586)
  *   loss_mask [n_tok] LCE_U8 (1 = counted) or data == NULL (all counted)
- *   chunk     tokens whose logits may exist at once: the call holds at most
- *             chunk*vocab logit-derived cells (587 above 2^27)
+ *   chunk     tokens whose logits may exist at once: each logit-derived
+ *             buffer of the call holds at most chunk*vocab cells (587 above
+ *             2^27; floors as for lce_workspace_bytes)
  *   z_coef    z-loss coefficient; only validated here (z_sum is unscaled)
  *   lse_out   [n_tok] per-token log-sum-exp, LCE_F32 for 16-bit inputs,
  *             LCE_F64 for fp64 inputs; lce_backward takes it back

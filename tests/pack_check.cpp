@@ -1,5 +1,5 @@
 // Host check of the backward's tile packing (lce::pack_tiles), built with g++
-// against lce_contract.cpp by tests/test_pack_host.py.
+// against lce_contract.cpp by tests/test_host_planner.py.
 //
 // For each case it replays the walk a packed launch makes on the device --
 // slot b = 8 s + x of XCD x runs c[b][j] tiles of product j, starting after
