@@ -1,7 +1,8 @@
-"""The asynchronous forward + backward captured in a HIP graph (torch.cuda.graph
-on the caller's stream) and replayed: every replay gives, bit for bit, the
-lse, loss scalars, d_hidden and d_weight of the same calls made eagerly, and
-the eager result itself matches the fp64 oracle.
+"""The asynchronous forward + backward, and the asynchronous single call
+(lce_forward_backward, with and without kept logits), captured in a HIP graph
+(torch.cuda.graph on the caller's stream) and replayed: every replay gives,
+bit for bit, the lse, loss scalars, d_hidden and d_weight of the same calls
+made eagerly, and the eager result itself matches the fp64 oracle.
 
 The captured calls launch kernels only: no host wait, no memset node, no
 allocation (every buffer, the workspace included, exists before capture).
@@ -74,6 +75,55 @@ def test_graph_replay_matches_eager(n, D, V, chunk):
         lse.fill_(float(rep) - 7.0)
         dH.fill_(3.0)
         dW.fill_(-5.0)
+        torch.cuda.synchronize()
+        g.replay()
+        st, loss = lce.lce_loss_fetch(ws)
+        assert st == lce.OK
+        _say(f"  replay {rep}: loss_sum {loss.loss_sum!r}")
+        assert torch.equal(lse, ref[0])
+        assert torch.equal(dH, ref[1])
+        assert torch.equal(dW, ref[2])
+        assert (loss.loss_sum, loss.z_sum, loss.n_counted) == ref[3:]
+
+
+@pytest.mark.parametrize("n,D,V,chunk,keeps", [
+    (300, 192, 3000, 300, 1),       # the logits kept: FwdKeepEpi, dlogit rows, one backward launch
+    (512, 256, 12000, 128, 0),      # chunk below the batch: the two-call algorithm inside
+])
+def test_graph_replay_single_call(n, D, V, chunk, keeps):
+    """lce_forward_backward without a host result (asynchronous) captured and
+    replayed: every replay equals the eager call bit for bit."""
+    w = syn.QWEN_BF16
+    c = Case(w, n=n, D=D, V=V, seed=43)
+    dev = c.H.device
+    _say(f"case graph replay single call bf16 n={n} D={D} V={V} chunk={chunk}")
+    assert lce.lce_forward_backward_keeps_logits(n, D, V, chunk, c.H.dtype) == keeps
+    nbytes = lce.lce_forward_backward_workspace_bytes(n, D, V, chunk, c.H.dtype)
+    ws = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    lse = torch.empty(n, dtype=torch.float32, device=dev)
+    dH = torch.empty_like(c.H)
+    dW = torch.empty(V, D, dtype=torch.float32, device=dev)
+
+    def step():
+        st, _ = lce.lce_forward_backward(c.H, c.W, c.y, c.m, n, D, V, chunk, c.z, 1.0, lse, dH,
+                                         dW, 0, ws, sync=False)
+        assert st == lce.OK
+
+    step()
+    st, loss = lce.lce_loss_fetch(ws)
+    assert st == lce.OK
+    ref = (lse.clone(), dH.clone(), dW.clone(), loss.loss_sum, loss.z_sum, loss.n_counted)
+    r = oracle.fused_forward(c.H64, c.W64, c.x.targets, mask=c.x.mask, chunk=chunk, z_coef=c.z)
+    check_forward(c, SimpleNamespace(lse=ref[0], loss=loss.as_dict()), r)
+
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    for rep in range(3):
+        lse.fill_(float(rep) + 11.0)
+        dH.fill_(-2.0)
+        dW.fill_(7.0)
         torch.cuda.synchronize()
         g.replay()
         st, loss = lce.lce_loss_fetch(ws)
