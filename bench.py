@@ -171,12 +171,12 @@ def label_measure(lce, torch, np, dev, steps: int):
 def shard_measure(lce, torch, np, dev, w, H, W, y, m, steps: int, shards: int):
     """The same training step as vocabulary shards run one after another on
     this GPU (each shard's forward, the exchange, each shard's backward with
-    its d_hidden partial added up): what one GPU's share of a vocab-parallel
-    head costs, and the exchange's overhead against the unsharded step.  Each
-    shard call gets chunk = the unsharded chunk x shards, so that a shard
-    holds as many logit cells (chunk x its rows) as the unsharded call does
-    (chunk x vocab): the peak logit memory of one GPU of a vocab-parallel
-    head at the unsharded call's budget."""
+    its d_hidden partial added up, no host wait inside the step): what one
+    GPU's share of a vocab-parallel head costs, and the exchange's overhead
+    against the unsharded step.  Each shard call gets chunk = the unsharded
+    chunk x shards, so that a shard holds as many logit cells (chunk x its
+    rows) as the unsharded call does (chunk x vocab): the peak logit memory
+    of one GPU of a vocab-parallel head at the unsharded call's budget."""
     n, D = H.shape
     V = W.shape[0]
     chunk = w.chunk * shards
@@ -198,7 +198,8 @@ def shard_measure(lce, torch, np, dev, w, H, W, y, m, steps: int, shards: int):
             st = lce.lce_shard_forward(H, W[a:b], y, n, D, b - a, a, V, chunk, stats[q], ws)
             if st != lce.OK:
                 raise lce.LceError(st, "lce_shard_forward")
-        st, out = lce.lce_shard_merge(stats, shards, m, n, lse, mws)
+        # asynchronous exchange: no host wait anywhere in the step
+        st, _ = lce.lce_shard_merge(stats, shards, m, n, lse, mws, sync=False)
         if st != lce.OK:
             raise lce.LceError(st, "lce_shard_merge")
         for q in range(shards):
@@ -211,16 +212,22 @@ def shard_measure(lce, torch, np, dev, w, H, W, y, m, steps: int, shards: int):
                 dH.copy_(part)
             else:
                 dH.add_(part)
-        return out
 
     for _ in range(2):
         step()
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for _ in range(steps):
-        out = step()
+        step()
     torch.cuda.synchronize()
     ms = (time.perf_counter() - t0) / steps * 1e3
+    # the shard calls' target guards (their workspace) and the exchange's scalars
+    st, _ = lce.lce_loss_fetch(ws)
+    if st != lce.OK:
+        raise lce.LceError(st, "lce_shard_forward / lce_shard_backward")
+    st, out = lce.lce_loss_fetch(mws)
+    if st != lce.OK:
+        raise lce.LceError(st, "lce_shard_merge")
     return {"shards": shards, "bounds": bounds, "chunk_per_shard": chunk,
             "ms_per_step": round(ms, 4),
             "tokens_per_s": round(n / (ms / 1e3), 1), "loss": out.loss_mean}

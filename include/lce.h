@@ -337,7 +337,9 @@ int32_t lce_shard_forward(const lce_tensor *hidden, const lce_tensor *weight_sha
  *   loss_mask [n_tok] LCE_U8 or data == NULL
  *   lse_out   [n_tok], stats' dtype (the backward's lse)
  *   workspace LCE_U8, numel >= lce_distill_workspace_bytes(n_tok, 1)
- *   out       host loss scalars; synchronizes the stream. */
+ *   out       host loss scalars; synchronizes the stream.  NULL: the call
+ *             returns once its kernels are enqueued and
+ *             lce_loss_fetch(workspace) returns the scalars later. */
 int32_t lce_shard_merge(const lce_tensor *stats, int32_t n_shards, const lce_tensor *loss_mask,
                         int64_t n_tok, lce_tensor *lse_out, lce_tensor *workspace, lce_loss *out,
                         void *stream);

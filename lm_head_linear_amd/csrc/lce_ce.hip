@@ -1729,7 +1729,7 @@ int32_t lce_shard_merge(const lce_tensor *stats, int32_t n_shards, const lce_ten
                         void *stream) {
   if (n_tok < 1 || n_shards < 1) return LCE_EMPTY_DIMENSION;
   if (n_tok > LCE_MAX_N_TOK) return LCE_DIMENSION_TOO_LARGE;
-  if (!stats || !lse_out || !workspace || !out) return LCE_LENGTH_MISMATCH;
+  if (!stats || !lse_out || !workspace) return LCE_LENGTH_MISMATCH;
   const int32_t adt = stats->dtype;
   if (adt != LCE_F32 && adt != LCE_F64) return LCE_DTYPE_MISMATCH;
   if (lse_out->dtype != adt) return LCE_DTYPE_MISMATCH;
@@ -1767,6 +1767,7 @@ int32_t lce_shard_merge(const lce_tensor *stats, int32_t n_shards, const lce_ten
                        (const double *)loss_tok, static_cast<const double *>(lse_out->data), mask,
                        n_tok, ctl);
   }
+  if (!out) return enqueued();   // the scalars: lce_loss_fetch(workspace)
   Control hc;
   st = finish(s, ctl, &hc);
   if (st != LCE_OK) return st;

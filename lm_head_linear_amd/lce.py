@@ -358,12 +358,15 @@ def lce_shard_forward(hidden, weight_shard, targets, n_tok, d_model, vocab_shard
 
 
 def lce_shard_merge(stats, n_shards, loss_mask, n_tok, lse_out, workspace,
-                    stream: Optional[int] = None):
-    """Direct call of the C entry point.  Returns (status, Loss)."""
-    out = Loss()
+                    stream: Optional[int] = None, sync: bool = True):
+    """Direct call of the C entry point.  Returns (status, Loss or None when
+    sync is False: the call is then asynchronous and lce_loss_fetch(workspace)
+    returns the scalars)."""
+    out = Loss() if sync else None
     a, m, l, ws = _t(stats), _t(loss_mask), _t(lse_out), _t(workspace)
     st = lib().lce_shard_merge(ctypes.byref(a), int(n_shards), ctypes.byref(m), n_tok,
-                               ctypes.byref(l), ctypes.byref(ws), ctypes.byref(out),
+                               ctypes.byref(l), ctypes.byref(ws),
+                               ctypes.byref(out) if sync else None,
                                stream if stream is not None else _stream(stats.device))
     return st, out
 

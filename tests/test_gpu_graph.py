@@ -1,5 +1,7 @@
-"""The asynchronous forward + backward, and the asynchronous single call
-(lce_forward_backward, with and without kept logits), captured in a HIP graph
+"""The asynchronous forward + backward, the asynchronous single call
+(lce_forward_backward, with and without kept logits) and a whole
+vocabulary-shard step (shard forwards, asynchronous exchange, shard
+backwards), captured in a HIP graph
 (torch.cuda.graph on the caller's stream) and replayed: every replay gives,
 bit for bit, the lse, loss scalars, d_hidden and d_weight of the same calls
 made eagerly, and the eager result itself matches the fp64 oracle.
@@ -127,6 +129,75 @@ def test_graph_replay_single_call(n, D, V, chunk, keeps):
         torch.cuda.synchronize()
         g.replay()
         st, loss = lce.lce_loss_fetch(ws)
+        assert st == lce.OK
+        _say(f"  replay {rep}: loss_sum {loss.loss_sum!r}")
+        assert torch.equal(lse, ref[0])
+        assert torch.equal(dH, ref[1])
+        assert torch.equal(dW, ref[2])
+        assert (loss.loss_sum, loss.z_sum, loss.n_counted) == ref[3:]
+
+
+def test_graph_replay_shard_step():
+    """A whole vocabulary-shard step -- every shard's forward, the asynchronous
+    exchange, every shard's backward with the d_hidden partials added up --
+    captured and replayed: every replay equals the eager step bit for bit, and
+    the eager loss matches the oracle's."""
+    w = syn.QWEN_BF16
+    n, D, V, chunk = 300, 128, 3000, 64
+    bounds = [0, 1024, 1100, 3000]
+    c = Case(w, n=n, D=D, V=V, seed=47)
+    dev = c.H.device
+    _say(f"case graph replay shard step bf16 n={n} D={D} V={V} bounds={bounds}")
+    P = len(bounds) - 1
+    rows = max(bounds[q + 1] - bounds[q] for q in range(P))
+    ws = torch.empty(lce.lce_workspace_bytes(n, D, rows, chunk, c.H.dtype), dtype=torch.uint8,
+                     device=dev)
+    mws = torch.empty(lce.lce_distill_workspace_bytes(n, 1), dtype=torch.uint8, device=dev)
+    stats = torch.empty(P, 3, n, dtype=torch.float32, device=dev)
+    lse = torch.empty(n, dtype=torch.float32, device=dev)
+    part = torch.empty(n, D, dtype=torch.float32, device=dev)
+    dH = torch.empty(n, D, dtype=torch.float32, device=dev)
+    dW = torch.empty(V, D, dtype=torch.float32, device=dev)
+
+    def step():
+        for q in range(P):
+            a, b = bounds[q], bounds[q + 1]
+            st = lce.lce_shard_forward(c.H, c.W[a:b], c.y, n, D, b - a, a, V, chunk, stats[q],
+                                       ws)
+            assert st == lce.OK
+        st, _ = lce.lce_shard_merge(stats, P, c.m, n, lse, mws, sync=False)
+        assert st == lce.OK
+        for q in range(P):
+            a, b = bounds[q], bounds[q + 1]
+            st = lce.lce_shard_backward(c.H, c.W[a:b], c.y, c.m, lse, n, D, b - a, a, V, chunk,
+                                        c.z, 1.0, part, dW[a:b], 0, ws)
+            assert st == lce.OK
+            if q == 0:
+                dH.copy_(part)
+            else:
+                dH.add_(part)
+
+    step()
+    assert lce.lce_loss_fetch(ws)[0] == lce.OK       # the shard calls' target guards
+    st, loss = lce.lce_loss_fetch(mws)
+    assert st == lce.OK
+    ref = (lse.clone(), dH.clone(), dW.clone(), loss.loss_sum, loss.z_sum, loss.n_counted)
+    r = oracle.fused_forward(c.H64, c.W64, c.x.targets, mask=c.x.mask, chunk=chunk, z_coef=c.z)
+    check_forward(c, SimpleNamespace(lse=ref[0], loss=loss.as_dict()), r)
+
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    for rep in range(3):
+        stats.fill_(5.0)
+        lse.fill_(float(rep) - 1.0)
+        dH.fill_(9.0)
+        dW.fill_(-4.0)
+        torch.cuda.synchronize()
+        g.replay()
+        assert lce.lce_loss_fetch(ws)[0] == lce.OK
+        st, loss = lce.lce_loss_fetch(mws)
         assert st == lce.OK
         _say(f"  replay {rep}: loss_sum {loss.loss_sum!r}")
         assert torch.equal(lse, ref[0])

@@ -139,6 +139,34 @@ def test_f16_shards():
 
 
 @pytest.mark.parametrize("dt", ["bf16", "f64"])
+def test_async_merge_matches_the_synchronous_merge(dt):
+    """lce_shard_merge without a host result returns once enqueued; the lse it
+    writes and the scalars lce_loss_fetch then returns equal the synchronous
+    call's bit for bit."""
+    w = syn.QWEN_BF16 if dt == "bf16" else syn.TINY_F64
+    x = syn.ce_inputs(w, n_tok=200, d_model=64, vocab=3000, seed=17)
+    dev = _dev()
+    H, W = x.hidden.to(dev), x.weight.to(dev)
+    y = torch.from_numpy(x.targets).to(dev)
+    mask = syn.exact_mask(np.random.default_rng(3), 200, 0.1)
+    m = torch.from_numpy(mask).to(dev)
+    _say(f"case async shard merge {dt} n=200 V=3000 in 3 shards")
+    ref, lse, stats, _, _ = run_shards(H, W, y, m, [0, 1000, 2048, 3000], 64, 1e-3,
+                                      backward=False)
+    lse2 = torch.full_like(lse, -3.0)
+    mws = torch.empty(lce.lce_distill_workspace_bytes(200, 1), dtype=torch.uint8, device=dev)
+    st, out = lce.lce_shard_merge(stats, 3, m, 200, lse2, mws, sync=False)
+    assert st == 580 and out is None
+    st, loss = lce.lce_loss_fetch(mws)
+    assert st == 580
+    assert torch.equal(lse2, lse)
+    assert loss.as_dict() == ref
+    # refusals come back before anything is enqueued, with or without a result
+    assert lce.lce_shard_merge(stats, 0, None, 200, lse2, mws, sync=False)[0] == 581
+    assert lce.lce_shard_merge(stats, 4, None, 200, lse2, mws, sync=False)[0] == 582
+
+
+@pytest.mark.parametrize("dt", ["bf16", "f64"])
 def test_one_shard_is_the_unsharded_call(dt):
     """A single shard over the whole head runs the same kernels: lse, loss,
     d_weight and the rounded d_hidden are identical bit for bit."""
