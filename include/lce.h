@@ -26,10 +26,13 @@
  *   be ordered (same stream).
  * Streams: device work is enqueued on the caller's stream (a hipStream_t
  *   passed as void*; NULL = the null stream).  Calls that hand back device
- *   scalars (lce_forward with a non-NULL out, lce_distill_fwd_bwd, ...)
- *   synchronize that stream once before returning.  lce_backward never
- *   waits: it returns once its kernels are enqueued, and the verdict of its
- *   target guard reaches the host through lce_loss_fetch.
+ *   scalars (lce_forward, lce_forward_backward and lce_shard_merge with a
+ *   non-NULL out, lce_distill_fwd_bwd, lce_ce_logits_fwd_bwd) synchronize
+ *   that stream once before returning.  lce_backward, lce_shard_forward,
+ *   lce_shard_backward, and the three calls above with out == NULL never
+ *   wait: they return once their kernels are enqueued (no allocation, no
+ *   memset, so they can be captured in a HIP graph), and the scalars and the
+ *   verdict of the target guard reach the host through lce_loss_fetch.
  * Validation order: dimensions -> chunk -> scalars -> dtypes -> buffer
  *   lengths and workspace size -> objective id -> device-side target guard
  *   -> compute.  The target guard runs on the device; when it fails, every
@@ -161,10 +164,12 @@ int64_t lce_forward_backward_workspace_bytes(int64_t n_tok, int64_t d_model, int
  * (LCE_BF16 or LCE_F16); d_model a multiple of 64; a chunk that holds the
  * whole batch (chunk >= max(n_tok rounded up to 4, n_tok rounded up to 64
  * divided by 2)); and a launch-cost model of both algorithms that puts the
- * kept path at least 3% ahead (it saves the recompute but moves about 10
- * bytes per kept logit; measured on 512 x 151936 heads it loses at d_model
- * 1024 and wins at 4096).  The call additionally needs hidden, weight and
- * d_weight 16-byte aligned, which only the pointers can tell. */
+ * kept path at least 1% ahead (it saves the recompute but writes every kept
+ * logit in fp32 from the forward GEMM, then reads it back and writes the
+ * 16-bit gradient in a streaming pass; measured on 512 x 151936 heads the
+ * kept path runs 1.03-1.05x the two calls at d_model 1024 and 1.21-1.26x at
+ * 4096).  The call additionally needs hidden, weight and d_weight 16-byte
+ * aligned, which only the pointers can tell. */
 int32_t lce_forward_backward_keeps_logits(int64_t n_tok, int64_t d_model, int64_t vocab,
                                           int64_t chunk, int32_t dtype);
 
@@ -199,13 +204,15 @@ int32_t lce_forward(const lce_tensor *hidden, const lce_tensor *weight,
                     int64_t d_model, int64_t vocab, int64_t chunk, double z_coef,
                     lce_tensor *lse_out, lce_tensor *workspace, lce_loss *out, void *stream);
 
-/* The scalars of the last lce_forward on this workspace (lce_backward on the
- * same workspace keeps them): synchronizes `stream`, fills *out.  Returns 586
- * when that forward, or any lce_backward enqueued on this workspace since,
- * met a target out of range (the scalars are then not filled in), 582 for a
- * NULL out or a workspace shorter than its control block, 590 for a
- * workspace that is not LCE_U8.  Meaningful only after an lce_forward on
- * this workspace. */
+/* The scalars of the last lce_forward, lce_forward_backward or
+ * lce_shard_merge on this workspace (lce_backward on the same workspace
+ * keeps them): synchronizes `stream`, fills *out.  Returns 586 when that
+ * call, or any lce_backward, lce_shard_forward or lce_shard_backward
+ * enqueued on this workspace since, met a target out of range (the scalars
+ * are then not filled in), 582 for a NULL out or a workspace shorter than
+ * its control block, 590 for a workspace that is not LCE_U8.  The scalars
+ * are meaningful only after one of the three calls above on this
+ * workspace; on a shard call's workspace only the status is. */
 int32_t lce_loss_fetch(const lce_tensor *workspace, lce_loss *out, void *stream);
 
 /* Analytic backward of loss_mean + z_coef*z_mean scaled by grad_out
