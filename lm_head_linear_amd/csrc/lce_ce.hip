@@ -782,6 +782,8 @@ struct FwdKeepEpi {
 // tokens [t0, t1) land on the fp32 bytes of tokens [t0 / 2, t1 / 2), all read
 // by then).
 constexpr int kDlogitRows = 4;
+// Workgroups of dlogit_rows4_kernel (4 waves each): about six waves per SIMD.
+constexpr int64_t kDlogit4Blocks = 1536;
 template <class TR>
 __global__ void dlogit_rows_kernel(float *Z, int64_t V, int64_t n, int64_t ld,
                                    const int64_t *y, const uint8_t *mask, const float *lse,
@@ -852,8 +854,10 @@ __global__ void dlogit_rows_kernel(float *Z, int64_t V, int64_t n, int64_t ld,
 // The same values for a token count that is a multiple of 4 (16-byte rows):
 // each lane forms four consecutive tokens per 16-byte load, so a wave's
 // access to a row is one 1 KB load and one 512-byte store per 256 tokens.
-// A segment is 512 tokens (two loads per lane and row), read for every row
-// of the wave before any is written, in ascending order as above.
+// A segment is 512 tokens (two loads per lane and row).  Each wave takes
+// groups of kDlogitRows rows in a grid stride and forms a segment's
+// per-token constants once for all its groups; a group's segment is read for
+// every row before any is written, in ascending order as above.
 template <class TR>
 __global__ void dlogit_rows4_kernel(float *Z, int64_t V, int64_t n, int64_t ld,
                                     const int64_t *y, const uint8_t *mask, const float *lse,
@@ -862,8 +866,10 @@ __global__ void dlogit_rows4_kernel(float *Z, int64_t V, int64_t n, int64_t ld,
   if (ctl->bad) return;
   const float L2E = 1.4426950408889634f;
   const int lane = threadIdx.x & 63;
-  const int64_t v0 = (int64_t(blockIdx.x) * (blockDim.x >> 6) + (threadIdx.x >> 6)) * kDlogitRows;
-  if (v0 >= V) return;
+  const int64_t wave = int64_t(blockIdx.x) * (blockDim.x >> 6) + (threadIdx.x >> 6);
+  const int64_t n_waves = int64_t(gridDim.x) * (blockDim.x >> 6);
+  const int64_t groups = (V + kDlogitRows - 1) / kDlogitRows;
+  if (wave >= groups) return;
   const int64_t C = ctl->count;
   const float g = C ? float(grad_out / double(C)) : 0.f;
   const float gz = C ? float(z_coef * grad_out / double(C)) : 0.f;
@@ -872,59 +878,69 @@ __global__ void dlogit_rows4_kernel(float *Z, int64_t V, int64_t n, int64_t ld,
   for (int64_t t0 = 0; t0 < tpad; t0 += 512) {
     float c2[2][4], gy[2][4];
     uint32_t sb[2][4];
-    int64_t yt[2][4];
+    int32_t yt[2][4];
 #pragma unroll
-    for (int k = 0; k < 2; ++k)
+    for (int k = 0; k < 2; ++k) {
+      const int64_t tb = t0 + 256 * k + 4 * lane;
+      // n % 4 == 0: the four tokens of a lane are all below n or all past it
+      if (tb < n) {
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int64_t t = t0 + 256 * k + 4 * lane + e;
-        c2[k][e] = -INFINITY;   // tokens >= n: exp2(-inf) = 0
-        sb[k][e] = 0;
-        gy[k][e] = 0.f;
-        yt[k][e] = -1;
-        if (t < n) {
+        for (int e = 0; e < 4; ++e) {
+          const int64_t t = tb + e;
           const float l = lse[t];
           const bool counted = !mask || mask[t] != 0;
           const float coef = counted ? g + 2.f * gz * l : 0.f;
           c2[k][e] = __builtin_amdgcn_logf(fabsf(coef)) - l * L2E;
           sb[k][e] = __float_as_uint(coef) & 0x80000000u;
-          yt[k][e] = y[t];
+          yt[k][e] = int32_t(y[t]);
           const float ey = __uint_as_float(
               __float_as_uint(__builtin_amdgcn_exp2f(fmaf(zy[t], L2E, c2[k][e]))) ^ sb[k][e]);
           gy[k][e] = ey - (counted ? g : 0.f);
         }
-      }
-    float4 z[kDlogitRows][2];
-#pragma unroll
-    for (int r = 0; r < kDlogitRows; ++r)
-#pragma unroll
-      for (int k = 0; k < 2; ++k) {
-        const int64_t t = t0 + 256 * k + 4 * lane;
-        z[r][k] = (t < n && v0 + r < V) ? *reinterpret_cast<const float4 *>(Z + (v0 + r) * ld + t)
-                                        : float4{0.f, 0.f, 0.f, 0.f};
-      }
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // the segment of every row is read
-#pragma unroll
-    for (int r = 0; r < kDlogitRows; ++r) {
-      const int64_t v = v0 + r;
-      if (v >= V) break;
-      E *dr = reinterpret_cast<E *>(Z) + v * 2 * ld;
-#pragma unroll
-      for (int k = 0; k < 2; ++k) {
-        const int64_t t = t0 + 256 * k + 4 * lane;
-        if (t >= tpad) continue;
-        const float zz[4] = {z[r][k].x, z[r][k].y, z[r][k].z, z[r][k].w};
-        E o[4];
+      } else {
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          const float d = __uint_as_float(
-              __float_as_uint(__builtin_amdgcn_exp2f(fmaf(zz[e], L2E, c2[k][e]))) ^ sb[k][e]);
-          o[e] = to_elem<TR>(yt[k][e] == v ? gy[k][e] : d);
+          c2[k][e] = -INFINITY;   // tokens >= n: exp2(-inf) = 0
+          sb[k][e] = 0;
+          gy[k][e] = 0.f;
+          yt[k][e] = -1;
         }
-        uint2 w;
-        w.x = uint32_t(o[0]) | (uint32_t(o[1]) << 16);
-        w.y = uint32_t(o[2]) | (uint32_t(o[3]) << 16);
-        *reinterpret_cast<uint2 *>(dr + t) = w;
+      }
+    }
+    for (int64_t grp = wave; grp < groups; grp += n_waves) {
+      const int64_t v0 = grp * kDlogitRows;
+      float4 z[kDlogitRows][2];
+#pragma unroll
+      for (int r = 0; r < kDlogitRows; ++r)
+#pragma unroll
+        for (int k = 0; k < 2; ++k) {
+          const int64_t t = t0 + 256 * k + 4 * lane;
+          z[r][k] = (t < n && v0 + r < V) ? *reinterpret_cast<const float4 *>(Z + (v0 + r) * ld + t)
+                                          : float4{0.f, 0.f, 0.f, 0.f};
+        }
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // the segment of every row is read
+#pragma unroll
+      for (int r = 0; r < kDlogitRows; ++r) {
+        const int64_t v = v0 + r;
+        if (v >= V) break;
+        E *dr = reinterpret_cast<E *>(Z) + v * 2 * ld;
+#pragma unroll
+        for (int k = 0; k < 2; ++k) {
+          const int64_t t = t0 + 256 * k + 4 * lane;
+          if (t >= tpad) continue;
+          const float zz[4] = {z[r][k].x, z[r][k].y, z[r][k].z, z[r][k].w};
+          E o[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const float d = __uint_as_float(
+                __float_as_uint(__builtin_amdgcn_exp2f(fmaf(zz[e], L2E, c2[k][e]))) ^ sb[k][e]);
+            o[e] = to_elem<TR>(yt[k][e] == int32_t(v) ? gy[k][e] : d);
+          }
+          uint2 w;
+          w.x = uint32_t(o[0]) | (uint32_t(o[1]) << 16);
+          w.y = uint32_t(o[2]) | (uint32_t(o[3]) << 16);
+          *reinterpret_cast<uint2 *>(dr + t) = w;
+        }
       }
     }
   }
@@ -1566,7 +1582,8 @@ static void forward_backward_single(const CEPlan &p, const void *H, const void *
   {
     TimedLaunch tl(tm, LCE_K_DLOGIT_ROWS, st);
     if (n % 4 == 0)
-      hipLaunchKernelGGL(dlogit_rows4_kernel<TR>, dim3(unsigned(cdiv(V, 4 * kDlogitRows))),
+      hipLaunchKernelGGL(dlogit_rows4_kernel<TR>,
+                         dim3(unsigned(std::min<int64_t>(cdiv(V, 4 * kDlogitRows), kDlogit4Blocks))),
                          dim3(256), 0, st, Z, V, n, p.f_ld, y, mask, (const float *)lse_out,
                          (const float *)zy, (const Control *)ctl, grad_out, z_coef);
     else
