@@ -48,6 +48,8 @@ KEPT = [
     ("bf16", 64, 64, 5000, 64, 0.25, 1e-2),
     ("f16", 300, 192, 3000, 300, 0.05, 1e-4),
     ("f16", 130, 128, 500, 132, None, 1e-3),
+    ("bf16", 1028, 256, 5000, 1028, 0.05, 1e-4),  # three 512-token segments, the last ragged
+    ("f16", 1540, 128, 3000, 1544, None, 1e-3),   # four segments, chunk past the batch
 ]
 
 
