@@ -286,10 +286,11 @@ int32_t lce_distill_fwd_bwd(const lce_tensor *student, const lce_tensor *teacher
                             double grad_out, lce_tensor *grad_logits, lce_tensor *workspace,
                             lce_loss *out, void *stream);
 
-/* lce_distill_fwd_bwd for callers that cannot allocate device memory (code
- * under HIP graph capture, tight serving loops, harnesses that forbid
- * hipMalloc): the same computation, arguments and statuses without the
- * workspace argument.  Its scratch (control block and per-row results) is a
+/* lce_distill_fwd_bwd for callers that cannot allocate device memory (tight
+ * serving loops, harnesses that forbid hipMalloc): the same computation,
+ * arguments and statuses without the workspace argument.  Like
+ * lce_distill_fwd_bwd it synchronizes the stream once to return the scalars,
+ * so it is not meant for a stream under graph capture.  Its scratch (control block and per-row results) is a
  * static device array of this library, 256 + 16 * 65536 bytes per GPU, held
  * by every GPU the library runs on until the process ends; the call itself
  * allocates nothing.
