@@ -26,13 +26,14 @@
  *   be ordered (same stream).
  * Streams: device work is enqueued on the caller's stream (a hipStream_t
  *   passed as void*; NULL = the null stream).  Calls that hand back device
- *   scalars (lce_forward, lce_forward_backward and lce_shard_merge with a
- *   non-NULL out, lce_distill_fwd_bwd, lce_ce_logits_fwd_bwd) synchronize
- *   that stream once before returning.  lce_backward, lce_shard_forward,
- *   lce_shard_backward, and the three calls above with out == NULL never
- *   wait: they return once their kernels are enqueued (no allocation, no
- *   memset, so they can be captured in a HIP graph), and the scalars and the
- *   verdict of the target guard reach the host through lce_loss_fetch.
+ *   scalars (lce_forward, lce_forward_backward, lce_shard_merge,
+ *   lce_distill_fwd_bwd and lce_ce_logits_fwd_bwd with a non-NULL out, and
+ *   lce_distill_fwd_bwd_noalloc) synchronize that stream once before
+ *   returning.  lce_backward, lce_shard_forward, lce_shard_backward, and the
+ *   five calls above with out == NULL never wait: they return once their
+ *   kernels are enqueued (no allocation, no memset, so they can be captured
+ *   in a HIP graph), and the scalars and the verdict of the target guard
+ *   reach the host through lce_loss_fetch.
  * Validation order: dimensions -> chunk -> scalars -> dtypes -> buffer
  *   lengths and workspace size -> objective id -> device-side target guard
  *   -> compute.  The target guard runs on the device; when it fails, every
@@ -204,15 +205,16 @@ int32_t lce_forward(const lce_tensor *hidden, const lce_tensor *weight,
                     int64_t d_model, int64_t vocab, int64_t chunk, double z_coef,
                     lce_tensor *lse_out, lce_tensor *workspace, lce_loss *out, void *stream);
 
-/* The scalars of the last lce_forward, lce_forward_backward or
- * lce_shard_merge on this workspace (lce_backward on the same workspace
- * keeps them): synchronizes `stream`, fills *out.  Returns 586 when that
- * call, or any lce_backward, lce_shard_forward or lce_shard_backward
- * enqueued on this workspace since, met a target out of range (the scalars
- * are then not filled in), 582 for a NULL out or a workspace shorter than
- * its control block, 590 for a workspace that is not LCE_U8.  The scalars
- * are meaningful only after one of the three calls above on this
- * workspace; on a shard call's workspace only the status is. */
+/* The scalars of the last lce_forward, lce_forward_backward,
+ * lce_shard_merge, lce_distill_fwd_bwd or lce_ce_logits_fwd_bwd on this
+ * workspace (lce_backward on the same workspace keeps them): synchronizes
+ * `stream`, fills *out.  Returns 586 when that call, or any lce_backward,
+ * lce_shard_forward or lce_shard_backward enqueued on this workspace since,
+ * met a target out of range (the scalars are then not filled in), 582 for a
+ * NULL out or a workspace shorter than its control block, 590 for a
+ * workspace that is not LCE_U8.  The scalars are meaningful only after one
+ * of the five calls above on this workspace; on a shard call's workspace
+ * only the status is. */
 int32_t lce_loss_fetch(const lce_tensor *workspace, lce_loss *out, void *stream);
 
 /* Analytic backward of loss_mean + z_coef*z_mean scaled by grad_out
@@ -279,7 +281,10 @@ int32_t lce_forward_backward(const lce_tensor *hidden, const lce_tensor *weight,
  *                    (grad_out/C) (dL/dx + 2 z_coef lse(x) p) / T, masked rows 0
  *   workspace        LCE_U8, numel >= lce_distill_workspace_bytes(...)
  *   out              host; loss_sum/loss_mean = distillation loss,
- *                    z_sum/z_mean = unscaled z-loss, n_counted = C */
+ *                    z_sum/z_mean = unscaled z-loss, n_counted = C; the call
+ *                    synchronizes the stream to fill it.  NULL: the call
+ *                    returns once its kernels are enqueued and
+ *                    lce_loss_fetch(workspace) returns the scalars later. */
 int32_t lce_distill_fwd_bwd(const lce_tensor *student, const lce_tensor *teacher,
                             const lce_tensor *loss_mask, int64_t n_tok, int64_t vocab,
                             int32_t objective, double temperature, double z_coef,
@@ -381,9 +386,13 @@ int32_t lce_shard_backward(const lce_tensor *hidden, const lce_tensor *weight_sh
  *                logits are then read once)
  *   workspace    LCE_U8, numel >= lce_distill_workspace_bytes(n_tok, vocab)
  *   out          host; loss_sum/loss_mean = sum/mean over counted rows of
- *                lse - z[y], z_sum/z_mean = unscaled lse^2, n_counted = C
- * Statuses as lce_distill_fwd_bwd (no objective or temperature); returns
- * after the scalars reach the host. */
+ *                lse - z[y], z_sum/z_mean = unscaled lse^2, n_counted = C;
+ *                the call returns after the scalars reach the host.  NULL:
+ *                it returns once its kernels are enqueued; lce_loss_fetch
+ *                (workspace) then returns the scalars, or 586 for a target
+ *                out of range (grad_logits untouched, as in the synchronous
+ *                call).
+ * Statuses as lce_distill_fwd_bwd (no objective or temperature). */
 int32_t lce_ce_logits_fwd_bwd(const lce_tensor *logits, const lce_tensor *targets,
                               const lce_tensor *loss_mask, int64_t n_tok, int64_t vocab,
                               double z_coef, double grad_out, lce_tensor *grad_logits,

@@ -1223,7 +1223,9 @@ int32_t distill_call(const lce_tensor *student, const lce_tensor *teacher,
     return LCE_LENGTH_MISMATCH;
   }
   if (objective < 0 || objective > 2) return LCE_UNKNOWN_OBJECTIVE;
-  if (!out) return LCE_LENGTH_MISMATCH;
+  // out == NULL: asynchronous, the scalars stay in the caller's workspace for
+  // lce_loss_fetch; the static scratch has no such handle
+  if (!out && ws) return LCE_LENGTH_MISMATCH;
 
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (!ws) {
@@ -1258,6 +1260,7 @@ int32_t distill_call(const lce_tensor *student, const lce_tensor *teacher,
                          temperature, z_coef, grad_out, ctl,
                          static_cast<double *>(grad_logits->data), rows, s, timers);
   if (hipGetLastError() != hipSuccess) return LCE_DEVICE_ERROR;
+  if (!out) return LCE_OK;   // enqueued; lce_loss_fetch(workspace) reads the scalars
   Control hc;
   if (hipMemcpyAsync(&hc, ctl, sizeof(Control), hipMemcpyDeviceToHost, s) != hipSuccess)
     return LCE_DEVICE_ERROR;
@@ -1357,7 +1360,6 @@ extern "C" int32_t lce_ce_logits_fwd_bwd_timed(const lce_tensor *logits,
   if (want_grad && grad_logits->numel < cells) return LCE_LENGTH_MISMATCH;
   if (has(loss_mask) && loss_mask->numel < n_tok) return LCE_LENGTH_MISMATCH;
   if (!has(workspace) || workspace->numel < int64_t(p.total) + 256) return LCE_LENGTH_MISMATCH;
-  if (!out) return LCE_LENGTH_MISMATCH;
 
   hipStream_t s = static_cast<hipStream_t>(stream);
   uintptr_t base = (reinterpret_cast<uintptr_t>(workspace->data) + 255) & ~uintptr_t(255);
@@ -1391,6 +1393,8 @@ extern "C" int32_t lce_ce_logits_fwd_bwd_timed(const lce_tensor *logits,
                        want_grad ? static_cast<double *>(grad_logits->data) : nullptr, rows, s,
                        timers);
   if (hipGetLastError() != hipSuccess) return LCE_DEVICE_ERROR;
+  // out == NULL: enqueued; lce_loss_fetch(workspace) reads the scalars, or 586
+  if (!out) return LCE_OK;
   Control hc;
   if (hipMemcpyAsync(&hc, ctl, sizeof(Control), hipMemcpyDeviceToHost, s) != hipSuccess)
     return LCE_DEVICE_ERROR;

@@ -295,14 +295,16 @@ def lce_backward(hidden, weight, targets, loss_mask, lse, n_tok, d_model, vocab,
 
 def lce_distill_fwd_bwd(student, teacher, loss_mask, n_tok, vocab, objective, temperature,
                         z_coef, grad_out, grad_logits, workspace, stream: Optional[int] = None,
-                        timer: Optional[KernelTimer] = None):
+                        timer: Optional[KernelTimer] = None, sync: bool = True):
     """Direct call of the C entry point (the _timed variant when a timer is
-    given).  Returns (status, Loss)."""
-    out = Loss()
+    given).  Returns (status, Loss or None when sync is False: the call is then
+    asynchronous and lce_loss_fetch(workspace) returns the scalars)."""
+    out = Loss() if sync else None
     ts = [_t(student), _t(teacher), _t(loss_mask)]
     g, ws = _t(grad_logits), _t(workspace)
     call = [*[ctypes.byref(a) for a in ts], n_tok, vocab, int(objective), float(temperature),
-            float(z_coef), float(grad_out), ctypes.byref(g), ctypes.byref(ws), ctypes.byref(out),
+            float(z_coef), float(grad_out), ctypes.byref(g), ctypes.byref(ws),
+            ctypes.byref(out) if sync else None,
             stream if stream is not None else _stream(student.device)]
     if timer is None:
         st = lib().lce_distill_fwd_bwd(*call)
@@ -328,14 +330,16 @@ def lce_distill_fwd_bwd_noalloc(student, teacher, loss_mask, n_tok, vocab, objec
 
 def lce_ce_logits_fwd_bwd(logits, targets, loss_mask, n_tok, vocab, z_coef, grad_out,
                           grad_logits, workspace, stream: Optional[int] = None,
-                          timer: Optional[KernelTimer] = None):
+                          timer: Optional[KernelTimer] = None, sync: bool = True):
     """Direct call of the C entry point (the _timed variant when a timer is
-    given); grad_logits None computes the loss only.  Returns (status, Loss)."""
-    out = Loss()
+    given); grad_logits None computes the loss only.  Returns (status, Loss or
+    None when sync is False: the call is then asynchronous and
+    lce_loss_fetch(workspace) returns the scalars, or 586)."""
+    out = Loss() if sync else None
     ts = [_t(logits), _t(targets), _t(loss_mask)]
     g, ws = _t(grad_logits), _t(workspace)
     call = [*[ctypes.byref(a) for a in ts], n_tok, vocab, float(z_coef), float(grad_out),
-            ctypes.byref(g), ctypes.byref(ws), ctypes.byref(out),
+            ctypes.byref(g), ctypes.byref(ws), ctypes.byref(out) if sync else None,
             stream if stream is not None else _stream(logits.device)]
     if timer is None:
         st = lib().lce_ce_logits_fwd_bwd(*call)

@@ -121,6 +121,41 @@ def test_distill_refusals():
     assert torch.all(g == 9.0)
 
 
+@pytest.mark.parametrize("obj", [0, 1, 2])
+@pytest.mark.parametrize("n,V", [(37, 1000), (3, 155656)])
+def test_async_distill_matches_sync(obj, n, V):
+    """lce_distill_fwd_bwd without a host result returns once enqueued; the
+    gradient it writes and the scalars lce_loss_fetch then returns equal the
+    synchronous call's bit for bit.  The allocation-free call has no
+    workspace to fetch from and refuses a NULL result with 582."""
+    print(f"case async distill obj={obj} n={n} V={V}", flush=True)
+    dev = _dev()
+    d = syn.distill_inputs(syn.DISTILL_BF16, n_tok=n, vocab=V, seed=90 + obj, dtype="bf16")
+    S, U = d.student.to(dev), d.teacher.to(dev)
+    m = torch.from_numpy(d.mask).to(dev)
+    nb = lce.lce_distill_workspace_bytes(n, V)
+    ws1 = torch.empty(nb, dtype=torch.uint8, device=dev)
+    ws2 = torch.empty(nb, dtype=torch.uint8, device=dev)
+    g1 = torch.empty_like(S)
+    g2 = torch.full_like(S, 5.0)
+    args = dict(student=S, teacher=U, loss_mask=m, n_tok=n, vocab=V, objective=obj,
+                temperature=2.0, z_coef=1e-3, grad_out=1.3)
+    st, ref = lce.lce_distill_fwd_bwd(**args, grad_logits=g1, workspace=ws1)
+    assert st == 580
+    st, out = lce.lce_distill_fwd_bwd(**args, grad_logits=g2, workspace=ws2, sync=False)
+    assert st == 580 and out is None
+    st, loss = lce.lce_loss_fetch(ws2)
+    assert st == 580
+    assert loss.as_dict() == ref.as_dict()
+    assert torch.equal(g1, g2)
+    L = lce.lib()
+    ts = [lce._t(S), lce._t(U), lce._t(m), lce._t(g2)]
+    st = L.lce_distill_fwd_bwd_noalloc(*[lce.ctypes.byref(a) for a in ts[:3]], n, V, obj, 2.0,
+                                       1e-3, 1.3, lce.ctypes.byref(ts[3]), None,
+                                       lce._stream(dev))
+    assert st == 582
+
+
 def test_distill_full_size_sampled_rows():
     """4096 x 151936 bf16, T = 2, 10% masked, z 1e-4: every objective."""
     w = syn.DISTILL_BF16

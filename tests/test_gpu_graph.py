@@ -1,7 +1,8 @@
 """The asynchronous forward + backward, the asynchronous single call
-(lce_forward_backward, with and without kept logits) and a whole
+(lce_forward_backward, with and without kept logits), a whole
 vocabulary-shard step (shard forwards, asynchronous exchange, shard
-backwards), captured in a HIP graph
+backwards) and the asynchronous logits-in calls (distillation, label
+cross-entropy), captured in a HIP graph
 (torch.cuda.graph on the caller's stream) and replayed: every replay gives,
 bit for bit, the lse, loss scalars, d_hidden and d_weight of the same calls
 made eagerly, and the eager result itself matches the fp64 oracle.
@@ -204,3 +205,51 @@ def test_graph_replay_shard_step():
         assert torch.equal(dH, ref[1])
         assert torch.equal(dW, ref[2])
         assert (loss.loss_sum, loss.z_sum, loss.n_counted) == ref[3:]
+
+
+def test_graph_replay_logits_in_calls():
+    """The asynchronous distillation call (the three objectives) and label
+    cross-entropy from logits captured in one graph: every replay equals the
+    eager calls bit for bit (gradients and the scalars lce_loss_fetch reads)."""
+    dev = torch.device("cuda:0")
+    n, V = 37, 3000
+    _say(f"case graph replay logits-in calls bf16 n={n} V={V}")
+    d = syn.distill_inputs(syn.DISTILL_BF16, n_tok=n, vocab=V, seed=53, dtype="bf16")
+    S, U = d.student.to(dev), d.teacher.to(dev)
+    m = torch.from_numpy(d.mask).to(dev)
+    y = torch.from_numpy(syn.label_inputs(syn.LABEL_BF16, n_tok=n, vocab=V, seed=54).targets).to(dev)
+    nb = lce.lce_distill_workspace_bytes(n, V)
+    wss = [torch.empty(nb, dtype=torch.uint8, device=dev) for _ in range(4)]
+    gs = [torch.empty_like(S) for _ in range(4)]
+
+    def step():
+        for obj in range(3):
+            st, _ = lce.lce_distill_fwd_bwd(S, U, m, n, V, obj, 2.0, 1e-3, 1.1, gs[obj], wss[obj],
+                                            sync=False)
+            assert st == lce.OK
+        st, _ = lce.lce_ce_logits_fwd_bwd(S, y, m, n, V, 1e-3, 0.9, gs[3], wss[3], sync=False)
+        assert st == lce.OK
+
+    def fetch_all():
+        res = []
+        for ws in wss:
+            st, loss = lce.lce_loss_fetch(ws)
+            assert st == lce.OK
+            res.append((loss.loss_sum, loss.z_sum, loss.n_counted))
+        return res
+
+    step()
+    ref_g = [g.clone() for g in gs]
+    ref_l = fetch_all()
+    torch.cuda.synchronize()
+    gr = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(gr):
+        step()
+    for rep in range(3):
+        for g in gs:
+            g.fill_(float(rep) + 2.0)
+        torch.cuda.synchronize()
+        gr.replay()
+        assert fetch_all() == ref_l
+        for g, r in zip(gs, ref_g):
+            assert torch.equal(g, r)

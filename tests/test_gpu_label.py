@@ -138,6 +138,44 @@ def test_label_refusals_leave_outputs_untouched():
     assert call() == 580
 
 
+@pytest.mark.parametrize("n,V,grad", [(37, 1000, True), (3, 155656, True), (20, 1003, False)])
+def test_async_label_ce(n, V, grad):
+    """lce_ce_logits_fwd_bwd without a host result returns once enqueued: its
+    gradient and the scalars lce_loss_fetch then returns equal the
+    synchronous call's bit for bit; a target out of range shows as 586 in
+    lce_loss_fetch and leaves the gradient untouched."""
+    print(f"case async label CE n={n} V={V} grad={grad}", flush=True)
+    dev = _dev()
+    d = syn.label_inputs(syn.LABEL_BF16, n_tok=n, vocab=V, seed=31 + n)
+    Z = d.logits.to(dev)
+    y = torch.from_numpy(d.targets).to(dev)
+    m = torch.from_numpy(d.mask).to(dev) if d.mask is not None else None
+    nb = lce.lce_distill_workspace_bytes(n, V)
+    ws1 = torch.empty(nb, dtype=torch.uint8, device=dev)
+    ws2 = torch.empty(nb, dtype=torch.uint8, device=dev)
+    g1 = torch.empty_like(Z) if grad else None
+    g2 = torch.full_like(Z, 3.0) if grad else None
+    args = dict(logits=Z, targets=y, loss_mask=m, n_tok=n, vocab=V, z_coef=1e-3, grad_out=0.8)
+    st, ref = lce.lce_ce_logits_fwd_bwd(**args, grad_logits=g1, workspace=ws1)
+    assert st == 580
+    st, out = lce.lce_ce_logits_fwd_bwd(**args, grad_logits=g2, workspace=ws2, sync=False)
+    assert st == 580 and out is None
+    st, loss = lce.lce_loss_fetch(ws2)
+    assert st == 580
+    assert loss.as_dict() == ref.as_dict()
+    if grad:
+        assert torch.equal(g1, g2)
+    bad = y.clone()
+    bad[n // 2] = V
+    g3 = torch.full_like(Z, 7.0) if grad else None
+    st, _ = lce.lce_ce_logits_fwd_bwd(**{**args, "targets": bad}, grad_logits=g3, workspace=ws2,
+                                      sync=False)
+    assert st == 580                                  # enqueued; the verdict is fetched
+    assert lce.lce_loss_fetch(ws2)[0] == 586
+    if grad:
+        assert torch.all(g3 == 7.0)
+
+
 def test_label_ce_full_size_sampled_rows():
     """4096 x 151936 bf16 logits, 10% masked, z 1e-4: the loss of every row
     and the gradient of sampled rows against the oracle."""
